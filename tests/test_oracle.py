@@ -1,0 +1,300 @@
+"""Pins of the CPU oracle against facts other than itself (CPU only).
+
+Each test is chosen so that a plausible mistake in the oracle (wrong nibble
+order, arithmetic instead of logical shift, wrong group index, transposed
+scales, dropped or sign-flipped zero point, wrong rounding) fails at least
+one of them. Expected values come from the pages, from exact integer
+arithmetic, from closed forms, or from torch's own casts.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from weight_only_int4_unpack_amd import synthetic
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_problem(M, K, N, G, dtype, has_zp, seed):
+    d = synthetic.draw(M, K, N, G, dtype, has_zp, family=900 + seed)
+    b_q = O.pack_int4(d["q"])
+    qz = None if d["z"] is None else O.pack_int4(d["z"])
+    return d, b_q, qz
+
+
+# ---------------------------------------------------------------- packing
+def test_pack_printed_vectors():
+    # The stated convention: value j of a word sits in bits [4j, 4j+4).
+    w = O.pack_int4(np.array([[0, 1, 2, 3, 4, 5, 6, 7]], np.uint8))
+    assert int(w[0, 0]) == 0x76543210
+    w = O.pack_int4(np.array([[15, 14, 13, 12, 11, 10, 9, 8]], np.uint8))
+    assert int(w[0, 0]) == -1985229329          # 0x89ABCDEF as int32
+    q = O.unpack_int4(np.array([[-1985229329, 0x76543210]], np.int32))
+    assert q.tolist() == [[15, 14, 13, 12, 11, 10, 9, 8, 0, 1, 2, 3, 4, 5, 6, 7]]
+
+
+def test_unpack_sign_bit_is_logical():
+    # 0x80000000: only value 7 is set, to 8; an arithmetic shift would smear it
+    q = O.unpack_int4(np.array([[np.int32(-2147483648)]], np.int32))
+    assert q.tolist() == [[0, 0, 0, 0, 0, 0, 0, 8]]
+    q = O.unpack_int4(np.array([[-1]], np.int32))
+    assert q.tolist() == [[15] * 8]
+
+
+def test_pack_roundtrip_random():
+    rng = np.random.default_rng(1)
+    q = rng.integers(0, 16, size=(37, 96), dtype=np.uint8)
+    assert np.array_equal(O.unpack_int4(O.pack_int4(q)), q)
+    x = rng.integers(-2**31, 2**31, size=(41, 13), dtype=np.int64).astype(np.int32)
+    assert np.array_equal(O.pack_int4(O.unpack_int4(x)), x)
+
+
+def test_pack_rejects_bad_values():
+    with pytest.raises(ValueError):
+        O.pack_int4(np.full((1, 8), 16, np.int32))
+    with pytest.raises(ValueError):
+        O.pack_int4(np.zeros((1, 7), np.uint8))
+
+
+# ---------------------------------------------------------------- rounding
+def _interesting_f32(n, seed):
+    rng = np.random.default_rng(seed)
+    u = rng.integers(0, 2**32, size=n, dtype=np.uint64).astype(np.uint32)
+    x = u.view(np.float32)
+    x = x[np.isfinite(x)]
+    # exact ties and near-ties for bf16 (low 16 bits 0x8000 / 0x7FFF / 0x8001)
+    base = rng.integers(0, 2**32, size=4096, dtype=np.uint64).astype(np.uint32)
+    base &= np.uint32(0xFFFF0000)
+    ties = np.concatenate([base | np.uint32(0x8000), base | np.uint32(0x7FFF),
+                           base | np.uint32(0x8001)]).view(np.float32)
+    ties = ties[np.isfinite(ties)]
+    normal = rng.standard_normal(n).astype(np.float32)
+    small = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    return np.concatenate([x, ties, normal, small,
+                           np.array([0.0, -0.0, 1.0, -1.0, 65504.0, 65520.0,
+                                     3.4e38, -3.4e38, np.inf, -np.inf],
+                                    np.float32)])
+
+
+def test_bf16_rne_matches_torch():
+    x = _interesting_f32(1_000_000, 2)
+    got = O.rne_bits(x, O.BF16)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_f16_rne_matches_torch():
+    x = _interesting_f32(1_000_000, 3)
+    got = O.rne_bits(x, O.F16)
+    want = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("dtype", [O.F16, O.BF16])
+def test_widening_is_exact(dtype):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = O.to_f32(bits, dtype)
+    ok = ~np.isnan(x)
+    assert np.array_equal(O.rne_bits(x[ok], dtype), bits[ok])
+    tdt = torch.float16 if dtype == O.F16 else torch.bfloat16
+    want = torch.from_numpy(bits.view(np.int16)).view(tdt).float().numpy()
+    assert np.array_equal(x[ok], want[ok])
+
+
+# ---------------------------------------------------------------- dequant
+@pytest.mark.parametrize("has_zp", [False, True])
+@pytest.mark.parametrize("dtype", [O.F16, O.BF16])
+def test_dequant_closed_form_integral(dtype, has_zp):
+    K, N, G = 256, 64, 32
+    d, b_q, qz = _rand_problem(1, K, N, G, dtype, has_zp, 1)
+    W = O.dequant_fp32(b_q, d["s_bits"], qz, G, 8, dtype)
+    S = O.to_f32(d["s_bits"], dtype)
+    Z = d["z"] if has_zp else np.full(S.shape, 8)
+    Sfull = np.repeat(S, G, axis=0)
+    ratio = W / Sfull
+    # (q - z) * s / s must be the exact small integer q - z
+    assert np.array_equal(ratio, ratio.round())
+    assert np.array_equal(ratio.astype(np.int64),
+                          d["q"].astype(np.int64) - np.repeat(Z, G, axis=0))
+
+
+def test_dequant_group_rows_and_orientation():
+    # Q - Z == 1 everywhere, scales distinct per (group, column):
+    # then W[k, n] must be exactly scale row k // G, column n.
+    K, N, G = 128, 16, 32
+    ng = K // G
+    s = (np.arange(ng)[:, None] * 100 + np.arange(N)[None, :] + 1) / 4096.0
+    s_bits = O.rne_bits(s.astype(np.float32), O.F16)
+    z = np.random.default_rng(3).integers(0, 15, size=(ng, N))
+    q = np.repeat(z, G, axis=0) + 1
+    W = O.dequant_fp32(O.pack_int4(q), s_bits, O.pack_int4(z), G, 8, O.F16)
+    S = O.to_f32(s_bits, O.F16)
+    for k in (0, 31, 32, 63, 64, 127):
+        assert np.array_equal(W[k], S[k // 32])
+    assert W[1, 5] != W[1, 6] and W[0, 3] != W[40, 3]
+
+
+@pytest.mark.parametrize("dtype", [O.F16, O.BF16])
+def test_power_of_two_scales_make_tile_exact(dtype):
+    K, N, G = 64, 32, 32
+    d, b_q, qz = _rand_problem(1, K, N, G, dtype, True, 2)
+    s_bits = O.rne_bits(np.full(d["s_bits"].shape, 2.0 ** -7, np.float32), dtype)
+    W = O.dequant_fp32(b_q, s_bits, qz, G, 8, dtype)
+    T = O.to_f32(O.dequant_tile(b_q, s_bits, qz, G, 8, dtype), dtype)
+    assert np.array_equal(W, T)
+
+
+def test_sampled_columns_match_full():
+    d, b_q, qz = _rand_problem(3, 96, 80, 32, O.F16, True, 4)
+    W = O.dequant_fp32(b_q, d["s_bits"], qz, 32, 8, O.F16)
+    cols = np.array([79, 0, 8, 9, 17, 17, 64])
+    Ws = O.dequant_fp32(b_q, d["s_bits"], qz, 32, 8, O.F16, cols=cols)
+    assert np.array_equal(Ws, W[:, cols])
+
+
+# ---------------------------------------------------------------- GEMM invariants
+@pytest.mark.parametrize("dtype", [O.F16, O.BF16])
+def test_q_equals_z_gives_zero_symmetric(dtype):
+    M, K, N, G = 5, 256, 64, 128
+    a = synthetic.random_bits((M, K), dtype, 11)
+    q = np.full((K, N), 8, np.uint8)
+    s = synthetic.random_bits((K // G, N), dtype, 12, 1e-2)
+    C = O.gemm_f32(a, O.pack_int4(q), s, None, G, 8, dtype)
+    assert np.all(C == 0.0)
+
+
+def test_q_equals_z_gives_zero_asymmetric():
+    M, K, N, G = 3, 192, 48, 64
+    a = synthetic.random_bits((M, K), O.F16, 13)
+    z = np.random.default_rng(14).integers(0, 16, size=(K // G, N), dtype=np.uint8)
+    q = np.repeat(z, G, axis=0)
+    s = synthetic.random_bits((K // G, N), O.F16, 15, 1e-2)
+    C = O.gemm_f32(a, O.pack_int4(q), s, O.pack_int4(z), G, 8, O.F16)
+    assert np.all(C == 0.0)
+    # and a dropped zero point (symmetric bias used instead) is visibly wrong
+    C8 = O.gemm_f32(a, O.pack_int4(q), s, None, G, 8, O.F16)
+    assert np.any(C8 != 0.0)
+
+
+@pytest.mark.parametrize("dtype", [O.F16, O.BF16])
+def test_scale_and_activation_linearity_bitwise(dtype):
+    M, K, N, G = 6, 256, 64, 64
+    d, b_q, qz = _rand_problem(M, K, N, G, dtype, True, 5)
+    C = O.gemm_f32(d["a_bits"], b_q, d["s_bits"], qz, G, 8, dtype)
+    s2 = O.rne_bits(2.0 * O.to_f32(d["s_bits"], dtype), dtype)
+    a2 = O.rne_bits(2.0 * O.to_f32(d["a_bits"], dtype), dtype)
+    an = O.rne_bits(-O.to_f32(d["a_bits"], dtype), dtype)
+    assert np.array_equal(O.gemm_f32(d["a_bits"], b_q, s2, qz, G, 8, dtype), 2 * C)
+    assert np.array_equal(O.gemm_f32(a2, b_q, d["s_bits"], qz, G, 8, dtype), 2 * C)
+    assert np.array_equal(O.gemm_f32(an, b_q, d["s_bits"], qz, G, 8, dtype), -C)
+
+
+def test_per_channel_equals_repeated_groups():
+    M, K, N = 4, 256, 64
+    d, b_q, _ = _rand_problem(M, K, N, K, O.F16, True, 6)
+    s_row = d["s_bits"][:1]
+    z_row = d["z"][:1]
+    Cpc = O.gemm_f32(d["a_bits"], b_q, s_row, O.pack_int4(z_row), K, 8, O.F16)
+    s_rep = np.repeat(s_row, K // 32, axis=0)
+    z_rep = np.repeat(z_row, K // 32, axis=0)
+    C32 = O.gemm_f32(d["a_bits"], b_q, s_rep, O.pack_int4(z_rep), 32, 8, O.F16)
+    assert np.array_equal(Cpc, C32)
+
+
+@pytest.mark.parametrize("dtype", [O.F16, O.BF16])
+def test_one_hot_rows_select_weight_rows(dtype):
+    K, N, G = 128, 64, 32
+    d, b_q, qz = _rand_problem(1, K, N, G, dtype, True, 7)
+    ks = [0, 1, 31, 32, 77, 127]
+    a = np.zeros((len(ks), K), np.float32)
+    for i, k in enumerate(ks):
+        a[i, k] = 1.0
+    a_bits = O.rne_bits(a, dtype)
+    out = O.gemm(a_bits, b_q, d["s_bits"], qz, G, 8, dtype)
+    tile = O.dequant_tile(b_q, d["s_bits"], qz, G, 8, dtype)
+    assert np.array_equal(out, tile[ks])
+
+
+@pytest.mark.parametrize("has_zp", [False, True])
+def test_exact_integer_case(has_zp):
+    # A in {-1, 0, 1} with at most 16 nonzeros per row and S = 2^-4: every
+    # partial sum is n / 16 with |n| <= 240, so fp32 (and fp16/bf16) hold the
+    # result exactly; compare with rational arithmetic.
+    M, K, N, G = 4, 512, 32, 128
+    rng = np.random.default_rng(8)
+    a = np.zeros((M, K), np.float32)
+    for m in range(M):
+        idx = rng.choice(K, size=16, replace=False)
+        a[m, idx] = rng.choice([-1.0, 1.0], size=16)
+    q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    z = rng.integers(0, 16, size=(K // G, N), dtype=np.uint8) if has_zp else None
+    for dtype in (O.F16, O.BF16):
+        s_bits = O.rne_bits(np.full((K // G, N), 1.0 / 16, np.float32), dtype)
+        qz = None if z is None else O.pack_int4(z)
+        C = O.gemm_f32(O.rne_bits(a, dtype), O.pack_int4(q), s_bits, qz, G, 8, dtype)
+        for m in range(M):
+            for n in range(N):
+                exact = Fraction(0)
+                for k in np.nonzero(a[m])[0]:
+                    zz = 8 if z is None else int(z[k // G, n])
+                    exact += Fraction(int(a[m, k])) * (int(q[k, n]) - zz) * Fraction(1, 16)
+                assert Fraction(float(C[m, n])) == exact
+        out = O.gemm(O.rne_bits(a, dtype), O.pack_int4(q), s_bits, qz, G, 8, dtype)
+        assert np.array_equal(O.to_f32(out, dtype), C)
+
+
+@pytest.mark.parametrize("dtype,has_zp,G", [(O.F16, False, 128), (O.BF16, True, 32),
+                                            (O.F16, True, 64)])
+def test_bruteforce_fp64_tiny(dtype, has_zp, G):
+    M, K, N = 3, 128, 16
+    d, b_q, qz = _rand_problem(M, K, N, G, dtype, has_zp, 9)
+    C32 = O.gemm_f32(d["a_bits"], b_q, d["s_bits"], qz, G, 8, dtype).astype(np.float64)
+    C64 = O.bruteforce_f64(d["a_bits"], b_q, d["s_bits"], qz, G, 8, dtype)
+    # the brute force itself against a textbook fp64 product of its weights
+    A64 = O.to_f32(d["a_bits"], dtype).astype(np.float64)
+    W64 = O.dequant_fp32(b_q, d["s_bits"], qz, G, 8, dtype).astype(np.float64)
+    assert np.allclose(C64, A64 @ W64, rtol=1e-12, atol=1e-12)
+    # fp32 accumulation error bound |C32 - C64| <= K u sum|a w| (u = 2^-24)
+    bound = K * 2.0 ** -24 * (np.abs(A64) @ np.abs(W64)) + 1e-30
+    assert np.all(np.abs(C32 - C64) <= bound)
+
+
+# ---------------------------------------------------------------- pages
+def test_pages_shape_contract():
+    g = json.load(open(os.path.join(GOLDEN, "pages_shape_contract.json")))
+    M, K = g["a_shape"]
+    N = g["b_q_shape"][1] * 8
+    G = g["group_size"]
+    assert g["scales_shape"] == [K // G, N]
+    d = synthetic.draw(M, K, N, G, g["a_dtype"], False, family=0)
+    b_q = O.pack_int4(d["q"])
+    assert list(b_q.shape) == g["b_q_shape"]
+    out = O.gemm(d["a_bits"], b_q, d["s_bits"], None, G, g["zp_bias_default"], g["a_dtype"])
+    assert list(out.shape) == g["out_shape"] and out.dtype == np.uint16
+
+
+def test_check_rejections():
+    O.check(4, 256, 512, 128, O.F16, False)
+    O.check(8, 2112, 5120, 64, O.F16, True)
+    O.check(16, 4096, 4096, 4096, O.F16, True)
+    O.check(3, 2120, 64, 2120, O.BF16, False)       # per-channel with any K
+    for bad in [dict(N=516), dict(G=16), dict(G=96), dict(K=2112, G=128),
+                dict(dtype="fp32"), dict(zp=16), dict(zp=-1), dict(K=0), dict(M=-1)]:
+        args = dict(M=4, K=256, N=512, G=128, dtype=O.F16, zp=8)
+        args.update(bad)
+        with pytest.raises(ValueError):
+            O.check(args["M"], args["K"], args["N"], args["G"], args["dtype"],
+                    False, args["zp"])
+
+
+def test_tolerance_helper():
+    w = O.rne_bits(np.array([0.5, 10.0, -300.0], np.float32), O.F16)
+    g = O.rne_bits(np.array([0.519, 10.19, -305.9], np.float32), O.F16)
+    assert O.within_tolerance(g, w, O.F16).all()
+    g = O.rne_bits(np.array([0.53, 10.0, -300.0], np.float32), O.F16)
+    assert not O.within_tolerance(g, w, O.F16)[0]
