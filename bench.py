@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 GEMM on one MI355X; prints one JSON line.
+
+Default workload (the decode configuration of the headline metric): one step
+is two GEMMs, M = 1 and M = 5, K = 5120, N = 17408, bf16 activations, uint4
+weights with group size 128, symmetric. ``value`` is the effective HBM
+bandwidth of the step: algorithmic bytes (packed weights + scales + zero
+points + activations + output) over the step's wall time on the GPU. Weight
+sets are rotated over at least 512 MB of distinct copies so that the 256 MB
+Infinity Cache cannot hold them between launches; inputs are resident in HBM
+before timing starts.
+
+``--workload NAME`` times one of the other workloads instead (prefill reports
+TFLOP/s); ``--all`` prints one line per workload. The prefill GEMM (M = 2048)
+is always timed too and reported under ``extra``.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2516.6      # MI355X dense fp16/bf16 (256 CU x 4096 flop/clk x 2.4 GHz)
+ROTATE_BYTES = 512 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode",
+                    help="decode (M=1 and M=5), prefill, k2112, tiny, sweep_m<M>, sweep_pc16")
+    ap.add_argument("--all", action="store_true", help="one line per workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-prefill-extra", action="store_true")
+    ap.add_argument("--warm", action="store_true", help="no weight rotation (cache-warm)")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per launch measured with rocprofv3 counters")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+def alg_bytes(w) -> int:
+    """Packed weights + scales + packed zero points + activations + output."""
+    ng = w.K // w.group_size
+    zp = ng * (w.N // 8) * 4 if w.has_zp else 0
+    return w.K * w.N // 2 + ng * w.N * 2 + zp + w.M * w.K * 2 + w.M * w.N * 2
+
+
+def flops(w) -> int:
+    return 2 * w.M * w.N * w.K
+
+
+class Launch:
+    """Device-resident inputs of one workload with rotated weight copies."""
+
+    def __init__(self, w, torch, W, synthetic, rotate: bool):
+        d = synthetic.draw_workload(w)
+        dt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
+        dev = torch.device("cuda", 0)
+        self.w = w
+        self.a = torch.from_numpy(d["a_bits"].view("int16")).view(dt).to(dev)
+        bq = torch.from_numpy(W.pack_int4(d["q"])).to(dev)
+        s = torch.from_numpy(d["s_bits"].view("int16")).view(dt).to(dev)
+        qz = None if d["z"] is None else torch.from_numpy(W.pack_int4(d["z"])).to(dev)
+        weight_bytes = bq.numel() * 4 + s.numel() * 2 + (0 if qz is None else qz.numel() * 4)
+        copies = max(1, math.ceil(ROTATE_BYTES / weight_bytes)) if rotate else 1
+        self.sets = [(bq, s, qz)] + [(bq.clone(), s.clone(), None if qz is None else qz.clone())
+                                     for _ in range(copies - 1)]
+        self.out = torch.empty((w.M, w.N), dtype=dt, device=dev)
+        self.W = W
+        self.i = 0
+
+    def __call__(self):
+        bq, s, qz = self.sets[self.i % len(self.sets)]
+        self.i += 1
+        self.W.gemm(self.a, bq, s, qz, self.w.group_size, 8, out=self.out)
+
+
+def time_launches(launches, steps, warmup, torch):
+    """Per-launch durations from HIP events on the launch stream, and the
+    wall time of the timed steps (synchronised on both sides)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for L in launches:
+            L()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in launches] for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(steps):
+        for j, L in enumerate(launches):
+            ev[k][j][0].record(stream)
+            L()
+            ev[k][j][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per = [[ev[k][j][0].elapsed_time(ev[k][j][1]) for k in range(steps)]
+           for j in range(len(launches))]
+    return total_ms, per
+
+
+def load_traffic(path, name):
+    try:
+        with open(path) as f:
+            t = json.load(f)
+        return t.get(name)
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(workloads, budget_s=12.0):
+    """The oracle (untuned) on the host, on a bounded sample of the workload."""
+    import numpy as np
+    import oracle as O
+    from weight_only_int4_unpack_amd import synthetic
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()
+                    if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        blas = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    inputs = []
+    for w in workloads:
+        d = synthetic.draw_workload(w)
+        inputs.append((w, d["a_bits"], O.pack_int4(d["q"]), d["s_bits"],
+                       None if d["z"] is None else O.pack_int4(d["z"])))
+    done_bytes = 0
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        for w, a, bq, s, qz in inputs:
+            O.gemm(a, bq, s, qz, w.group_size, 8, w.dtype)
+            done_bytes += alg_bytes(w)
+            calls += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done_bytes / el / 1e12, "unit": "TB/s", "cores": blas, "kind": "oracle",
+            "sample": f"{calls} full oracle GEMMs ({'+'.join(w.name for w in workloads)}) in "
+                      f"{el:.1f} s: NumPy unpack/dequant on one thread, fp32 matmul on "
+                      f"{blas} OpenBLAS threads; host has {os.cpu_count()} CPUs, affinity "
+                      f"{len(os.sched_getaffinity(0))}"}
+
+
+def run_workload(names, steps, warmup, rotate, torch, W, synthetic):
+    ws = [synthetic.WORKLOADS[n] for n in names]
+    launches = [Launch(w, torch, W, synthetic, rotate) for w in ws]
+    total_ms, per = time_launches(launches, steps, warmup, torch)
+    res = []
+    for w, d in zip(ws, per):
+        d = sorted(d)
+        res.append({"name": w.name, "median_us": 1e3 * d[len(d) // 2],
+                    "mean_us": 1e3 * sum(d) / len(d), "bytes": alg_bytes(w), "flops": flops(w),
+                    "plan": W.plan(w.M, w.K, w.N, w.group_size, w.has_zp,
+                                   torch.float16 if w.dtype == "fp16" else torch.bfloat16).as_dict()})
+    return total_ms, res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: this build "
+              "runs the GEMM on a single MI355X (sharding is described, not built).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from weight_only_int4_unpack_amd import synthetic
+    from weight_only_int4_unpack_amd import w4a16 as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    rotate = not args.warm
+
+    if args.copy_probe:
+        x = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(4):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
+
+    groups = {"decode": ["decode_m1", "decode_m5"]}
+    todo = ([["decode_m1", "decode_m5"], ["prefill"], ["k2112"], ["tiny"], ["sweep_pc16"]]
+            + [[f"sweep_m{m}"] for m in (1, 2, 4, 5, 6, 16, 64, 256, 4096)]) if args.all \
+        else [groups.get(args.workload, [args.workload])]
+
+    cpu = None
+    for names in todo:
+        is_prefill = names == ["prefill"] or (len(names) == 1 and
+                                              synthetic.WORKLOADS[names[0]].M > 16)
+        steps = args.steps if not is_prefill else max(5, min(args.steps, 50))
+        total_ms, res = run_workload(names, steps, args.warmup, rotate, torch, W, synthetic)
+        step_bytes = sum(r["bytes"] for r in res)
+        step_flops = sum(r["flops"] for r in res)
+        ms_per_step = total_ms / steps
+        mean_launch_us = sum(r["mean_us"] for r in res) / len(res)
+        mean_bytes = step_bytes / len(res)
+        mean_flops = step_flops / len(res)
+        if is_prefill:
+            metric = "W4A16 GEMM TFLOP/s (prefill, MFMA path), 1 MI355X"
+            value = step_flops / (ms_per_step * 1e-3) / 1e12
+            unit = "TFLOP/s"
+            ach = mean_flops / (mean_launch_us * 1e-6) / 1e12
+            roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS, 4)}
+        else:
+            metric = "W4A16 GEMM effective HBM TB/s (decode M<=8), 1 MI355X"
+            value = step_bytes / (ms_per_step * 1e-3) / 1e12
+            unit = "TB/s"
+            ach = mean_bytes / (mean_launch_us * 1e-6) / 1e9
+            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4)}
+        tr = load_traffic(args.traffic, "+".join(names))
+        roof["traffic"] = tr
+        line = {
+            "metric": metric, "value": round(value, 4), "unit": unit, "n_gpus": 1,
+            "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": synthetic.WORKLOADS[names[0]].dtype, "data": "synthetic",
+            "config": {"workload": "+".join(names),
+                       "shapes": [{"M": synthetic.WORKLOADS[n].M, "K": synthetic.WORKLOADS[n].K,
+                                   "N": synthetic.WORKLOADS[n].N,
+                                   "group_size": synthetic.WORKLOADS[n].group_size,
+                                   "zero_points": synthetic.WORKLOADS[n].has_zp} for n in names],
+                       "weights_rotated_over_mb": 0 if not rotate else ROTATE_BYTES >> 20,
+                       "parallelism": "single GPU"},
+            "roofline": roof,
+            "launches": res,
+        }
+        if names == ["decode_m1", "decode_m5"] and not args.no_prefill_extra:
+            ptot, pres = run_workload(["prefill"], 20, 3, rotate, torch, W, synthetic)
+            pf = pres[0]
+            tf = pf["flops"] / (pf["mean_us"] * 1e-6) / 1e12
+            line["extra"] = {"prefill": {"tflops": round(tf, 1),
+                                         "frac_of_mfma_peak": round(tf / MFMA_PEAK_TFLOPS, 4),
+                                         "median_us": round(pf["median_us"], 2),
+                                         "plan": pf["plan"]}}
+        if not args.no_cpu and cpu is None and not args.all:
+            cpu = cpu_baseline([synthetic.WORKLOADS[n] for n in names])
+            if is_prefill:
+                cpu["sample"] += " (value in TB/s of algorithmic bytes)"
+        line["cpu_baseline"] = cpu
+        print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+/*
+ * w4a16.h - C ABI of the MI355X (gfx950) weight-only int4 GEMM.
+ *
+ *   C[M,N] = A[M,K] . dequant(B),   dequant(B)[k,n] = (q[k,n] - z[k/G,n]) * s[k/G,n]
+ *
+ * Where the operation is defined (pages cited by title and section):
+ *   - Operands and shapes: PR #51453 "Register the Triton W4A16 GEMM as a
+ *     custom op", implementation item 1 (contiguous inputs, M,K from the
+ *     activation, N = 8 * packed columns) and its Code section (the facade
+ *     signature a, b_q, scales, qzeros|None, group_size, zp_bias=8; the
+ *     output [M, 8*b_q.cols] in the activation's dtype; no input mutated).
+ *   - Arithmetic: PR #40977 "RDNA hybrid W4A16", Code section (reference:
+ *     zero points and scales repeated along K per group, (raw - zero)*scale
+ *     in fp32, fp32 product, one cast to the activation dtype; symmetric
+ *     weights use the constant 8).
+ *   - Rejections: PR #43731 "TritonW4A16LinearKernel as CUDA fallback",
+ *     Code section (can_implement: activation dtype, N % 8, g_idx, group
+ *     size unless equal to the full K) and its Motivation (no kernel is an
+ *     error, never a silent substitute).
+ *
+ * Layout (all row-major, contiguous, no padding):
+ *   a       [M, K]    fp16 or bf16
+ *   b_q     [K, N/8]  int32; uint4 value j of word c is column 8c+j, in
+ *                     bits [4j, 4j+4) (LSB first)
+ *   scales  [K/G, N]  same dtype as a
+ *   qzeros  [K/G, N/8] int32 packed like b_q, or NULL (symmetric: z = zp_bias)
+ *   out     [M, N]    same dtype as a
+ *
+ * Conventions:
+ *   - Every call returns a w4a16_status; nothing is thrown or aborted. The
+ *     calling thread's last message is returned by w4a16_last_error().
+ *   - All argument checks run before anything is launched.
+ *   - Device pointers must be 16-byte aligned; the caller owns every buffer.
+ *   - GPU calls are enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and never synchronise.
+ *   - G (group_size) is 32, 64, 128 or K (one group per column), and K is a
+ *     multiple of G. N is a multiple of 8. M = 0 is a no-op that succeeds.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W4A16_OK = 0,
+  W4A16_ERR_NULL = 1,       /* a required pointer is NULL */
+  W4A16_ERR_SHAPE = 2,      /* M < 0, K <= 0, N <= 0, N % 8, K % G, size overflow */
+  W4A16_ERR_GROUP = 3,      /* G not in {32, 64, 128, K} */
+  W4A16_ERR_DTYPE = 4,      /* dtype not W4A16_F16 / W4A16_BF16 */
+  W4A16_ERR_ZP = 5,         /* zp_bias outside 0..15 (symmetric calls only) */
+  W4A16_ERR_ALIGN = 6,      /* a device pointer is not 16-byte aligned */
+  W4A16_ERR_DEVICE = 7,     /* no device, or the current device is not gfx950 */
+  W4A16_ERR_HIP = 8,        /* a HIP runtime call or launch failed */
+  W4A16_ERR_VALUE = 9,      /* pack: a value outside 0..15 */
+  W4A16_ERR_PLAN = 10       /* a caller-supplied plan does not fit the problem */
+} w4a16_status;
+
+typedef enum { W4A16_F16 = 0, W4A16_BF16 = 1 } w4a16_dtype;
+
+typedef enum {
+  W4A16_ROUTE_NONE = 0,     /* M == 0: nothing to launch */
+  W4A16_ROUTE_DECODE = 1,   /* skinny split-K kernel, M <= 16 */
+  W4A16_ROUTE_PREFILL = 2   /* tiled MFMA kernel, any M */
+} w4a16_route;
+
+/* The launch the selector picked for one problem (all fields plain ints). */
+typedef struct {
+  int32_t route;            /* w4a16_route */
+  int32_t block_m;          /* rows of A per workgroup tile (decode: 16) */
+  int32_t block_n;          /* output columns per workgroup */
+  int32_t block_k;          /* K rows per pipeline step */
+  int32_t scale_in_tile;    /* decode: 1 = scale folded into each weight,
+                               0 = applied once per group to the partial sum */
+  int32_t splits;           /* decode: K splits across workgroups */
+  int32_t steps_per_wave;   /* decode: 32-row K steps per wavefront */
+  int32_t grid;             /* workgroups launched */
+  int32_t threads;          /* threads per workgroup */
+  int32_t lds_bytes;        /* LDS per workgroup */
+  int64_t workspace_bytes;  /* device scratch the launch needs (0 = none) */
+} w4a16_plan_t;
+
+/*
+ * w4a16_gemm - out = a . dequant(b_q, scales, qzeros) on the GPU.
+ * Route and tiles are chosen from the runtime M, K, N, G on every call
+ * (PR #51453 Motivation: a tile choice frozen at trace time slowed decode).
+ * Uses a per-device scratch buffer for split-K partials that the library
+ * allocates on first need and keeps; that first call is therefore not
+ * capturable into a HIP graph. Concurrent calls on one device that both
+ * need the scratch buffer must be ordered (same stream).
+ * Errors: NULL, SHAPE, GROUP, DTYPE, ZP, ALIGN, DEVICE, HIP.
+ */
+w4a16_status w4a16_gemm(const void* a, const int32_t* b_q, const void* scales,
+                        const int32_t* qzeros, int32_t group_size,
+                        int32_t zp_bias, void* out, int64_t M, int64_t K,
+                        int64_t N, int32_t dtype, void* stream);
+
+/*
+ * w4a16_gemm_planned - as w4a16_gemm, but runs the launch in `plan`
+ * (obtained from w4a16_plan or w4a16_plan_route, possibly with another
+ * route or split forced). The plan is checked against the problem first.
+ * Errors: those of w4a16_gemm, and PLAN.
+ */
+w4a16_status w4a16_gemm_planned(const void* a, const int32_t* b_q,
+                                const void* scales, const int32_t* qzeros,
+                                int32_t group_size, int32_t zp_bias, void* out,
+                                int64_t M, int64_t K, int64_t N, int32_t dtype,
+                                const w4a16_plan_t* plan, void* stream);
+
+/*
+ * w4a16_plan - the launch w4a16_gemm would make (host only, no GPU call).
+ * num_cus: compute units of the target (256 on MI355X); <= 0 means 256.
+ * Errors: SHAPE, GROUP, DTYPE, NULL (plan).
+ */
+w4a16_status w4a16_plan(int64_t M, int64_t K, int64_t N, int32_t group_size,
+                        int32_t has_zp, int32_t dtype, int32_t num_cus,
+                        w4a16_plan_t* plan);
+
+/*
+ * w4a16_plan_route - as w4a16_plan with the route forced
+ * (W4A16_ROUTE_DECODE needs 1 <= M <= 16) and, for decode, the K split
+ * and scale placement forced when `splits` > 0 / `scale_in_tile` >= 0.
+ * Errors: those of w4a16_plan, and PLAN.
+ */
+w4a16_status w4a16_plan_route(int64_t M, int64_t K, int64_t N,
+                              int32_t group_size, int32_t has_zp,
+                              int32_t dtype, int32_t num_cus, int32_t route,
+                              int32_t splits, int32_t scale_in_tile,
+                              w4a16_plan_t* plan);
+
+/*
+ * w4a16_dequant - w_out[k,n] = RNE_dtype((q - z) * s), the dequantised
+ * weight as the prefill kernel stages it, written as a dense [K, N] array
+ * (test probe; same device routine as the GEMM's weight tiles).
+ * Errors: NULL, SHAPE, GROUP, DTYPE, ZP, ALIGN, DEVICE, HIP.
+ */
+w4a16_status w4a16_dequant(const int32_t* b_q, const void* scales,
+                           const int32_t* qzeros, int32_t group_size,
+                           int32_t zp_bias, void* w_out, int64_t K, int64_t N,
+                           int32_t dtype, void* stream);
+
+/*
+ * w4a16_pack_int4 - host utility: q [rows, cols] uint8 values 0..15 ->
+ * packed [rows, cols/8] int32 in the layout above (used for b_q and
+ * qzeros). Host pointers. Errors: NULL, SHAPE (cols % 8), VALUE.
+ */
+w4a16_status w4a16_pack_int4(const uint8_t* q, int64_t rows, int64_t cols,
+                             int32_t* packed);
+
+/*
+ * w4a16_unpack_int4 - host inverse of w4a16_pack_int4 (diagnostics).
+ * Host pointers; `cols` counts unpacked columns. Errors: NULL, SHAPE.
+ */
+w4a16_status w4a16_unpack_int4(const int32_t* packed, int64_t rows,
+                               int64_t cols, uint8_t* q);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* w4a16_last_error(void);
+
+/* Library version string. */
+const char* w4a16_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,175 @@
+"""CPU tests of the C ABI: symbols, host pack utility, argument checks, selector.
+
+Nothing here launches a kernel; every call either is host-only or fails its
+argument checks before the library touches a device.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from weight_only_int4_unpack_amd import w4a16 as W
+
+HAS_GPU = torch.cuda.is_available()
+
+
+def test_library_exports_every_header_symbol():
+    L = W.lib()
+    names = W.header_functions()
+    assert {"w4a16_gemm", "w4a16_gemm_planned", "w4a16_plan", "w4a16_plan_route",
+            "w4a16_dequant", "w4a16_pack_int4", "w4a16_unpack_int4", "w4a16_last_error",
+            "w4a16_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert W.version().startswith("w4a16-gfx950")
+
+
+def test_pack_matches_oracle_bitwise():
+    rng = np.random.default_rng(5)
+    q = rng.integers(0, 16, size=(333, 1024), dtype=np.uint8)
+    assert np.array_equal(W.pack_int4(q), O.pack_int4(q))
+    assert np.array_equal(W.unpack_int4(W.pack_int4(q)), q)
+    x = rng.integers(-2**31, 2**31, size=(17, 40), dtype=np.int64).astype(np.int32)
+    assert np.array_equal(W.unpack_int4(x), O.unpack_int4(x))
+
+
+def test_pack_printed_vectors():
+    w = W.pack_int4(np.array([[0, 1, 2, 3, 4, 5, 6, 7, 15, 14, 13, 12, 11, 10, 9, 8]], np.uint8))
+    assert w.tolist() == [[0x76543210, -1985229329]]
+
+
+def test_pack_errors():
+    with pytest.raises(W.W4A16Error) as e:
+        W.pack_int4(np.full((2, 8), 16, np.uint8))
+    assert e.value.status == W.ERR_VALUE and "outside 0..15" in W.last_error()
+    with pytest.raises(W.W4A16Error) as e:
+        W.pack_int4(np.zeros((2, 12), np.uint8))
+    assert e.value.status == W.ERR_SHAPE
+    with pytest.raises(W.W4A16Error):
+        W.pack_int4(np.array([[300] * 8]))
+    L = W.lib()
+    assert L.w4a16_pack_int4(None, 2, 8, None) == W.ERR_NULL
+    assert L.w4a16_pack_int4(None, 0, 8, None) == W.OK       # empty is fine
+
+
+# ------------------------------------------------------------ argument checks
+FAKE = ctypes.c_void_p(0x10000)    # aligned, never dereferenced on the host
+
+
+def _gemm(a=FAKE, b=FAKE, s=FAKE, z=None, G=128, zp=8, out=FAKE, M=4, K=256, N=512, dt=W.F16):
+    return W.lib().w4a16_gemm(a, b, s, z, G, zp, out, M, K, N, dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=2), W.ERR_DTYPE),
+    (dict(N=516), W.ERR_SHAPE),
+    (dict(K=0), W.ERR_SHAPE),
+    (dict(M=-1), W.ERR_SHAPE),
+    (dict(G=16), W.ERR_GROUP),
+    (dict(G=96), W.ERR_GROUP),
+    (dict(G=100, K=200), W.ERR_GROUP),
+    (dict(K=2112, G=128), W.ERR_SHAPE),
+    (dict(a=None), W.ERR_NULL),
+    (dict(out=None), W.ERR_NULL),
+    (dict(s=None), W.ERR_NULL),
+    (dict(zp=16), W.ERR_ZP),
+    (dict(zp=-1), W.ERR_ZP),
+    (dict(a=ctypes.c_void_p(0x10008)), W.ERR_ALIGN),
+    (dict(z=ctypes.c_void_p(0x10004)), W.ERR_ALIGN),
+])
+def test_gemm_rejections(kw, status):
+    assert _gemm(**kw) == status
+    assert W.last_error() != ""
+
+
+def test_group_64_is_kept_not_substituted():
+    p = W.plan(8, 2112, 5120, 64, True, torch.float16)
+    assert p.route == W.ROUTE_DECODE
+    # a non-multiple K for G=64 is an error, never a fallback to another G
+    assert _gemm(M=8, K=2100, N=5120, G=64) == W.ERR_SHAPE
+
+
+def test_m_zero_is_noop_even_with_null_pointers():
+    assert _gemm(M=0, a=None, out=None) == W.OK
+
+
+def test_zero_point_bias_ignored_when_qzeros_given():
+    # zp_bias is only checked for symmetric calls; with qzeros it is unused
+    st = _gemm(z=FAKE, zp=99)
+    assert st == (W.ERR_DEVICE if not HAS_GPU else st)
+
+
+@pytest.mark.skipif(HAS_GPU, reason="checks the no-device error path")
+def test_valid_call_without_device_reports_device_error():
+    assert _gemm() == W.ERR_DEVICE
+    assert "device" in W.last_error()
+
+
+def test_python_wrapper_validates_shapes():
+    a = torch.zeros((4, 256), dtype=torch.float16)
+    b = torch.zeros((256, 64), dtype=torch.int32)
+    s = torch.zeros((2, 512), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        W.gemm(a, b, torch.zeros((2, 256), dtype=torch.float16))    # scales shape
+    with pytest.raises(ValueError):
+        W.gemm(a, b, s.to(torch.bfloat16))                           # scales dtype
+    with pytest.raises(ValueError):
+        W.gemm(a, b, s, qzeros=torch.zeros((2, 32), dtype=torch.int32))
+    with pytest.raises(ValueError):
+        W.gemm(a, b[:128], s)                                         # K mismatch
+    with pytest.raises(ValueError):
+        W.gemm(a, b, s)                                               # CPU tensors
+
+
+# ------------------------------------------------------------ selector
+def test_selector_routes_on_runtime_m():
+    for M in (1, 2, 4, 5, 6, 8, 16):
+        assert W.plan(M, 4096, 4096, 32, True, torch.float16).route == W.ROUTE_DECODE
+    for M in (17, 64, 256, 2048, 4096):
+        assert W.plan(M, 4096, 4096, 32, True, torch.float16).route == W.ROUTE_PREFILL
+    assert W.plan(0, 4096, 4096, 32, True, torch.float16).route == W.ROUTE_NONE
+
+
+def test_selector_decode_shapes():
+    p = W.plan(1, 5120, 17408, 128, False, torch.bfloat16)
+    nb = 17408 // 256
+    assert p.block_n == 256 and p.grid == nb * p.splits
+    assert p.splits * 4 * p.steps_per_wave >= 5120 // 32
+    assert (p.splits - 1) * 4 * p.steps_per_wave < 5120 // 32        # no empty split
+    assert p.scale_in_tile == 0
+    # K = 2112 is 66 steps of 32 rows
+    p = W.plan(8, 2112, 5120, 64, True, torch.float16)
+    assert p.splits * 4 * p.steps_per_wave >= 66
+    assert p.scale_in_tile == 1
+    assert p.workspace_bytes >= p.splits * 8 * 5120 * 4 or p.splits == 1
+    assert p.lds_bytes == 4 * 8 * 256 * 4
+
+
+def test_selector_prefill_tiles():
+    p = W.plan(2048, 5120, 17408, 128, False, torch.bfloat16)
+    assert (p.block_m, p.block_n, p.block_k) == (256, 256, 64)
+    assert p.grid % 8 == 0 and p.grid >= 8 * 68
+    assert W.plan(64, 4096, 4096, 32, True, torch.float16).block_m == 64
+    assert W.plan(100, 4096, 4096, 32, True, torch.float16).block_m == 128
+
+
+def test_forced_routes_and_errors():
+    p = W.plan(5, 4096, 4096, 32, True, torch.float16, route=W.ROUTE_PREFILL)
+    assert p.route == W.ROUTE_PREFILL
+    with pytest.raises(W.W4A16Error) as e:
+        W.plan(17, 4096, 4096, 32, True, torch.float16, route=W.ROUTE_DECODE)
+    assert e.value.status == W.ERR_PLAN
+    p = W.plan(4, 4096, 4096, 32, True, torch.float16, route=W.ROUTE_DECODE, splits=1)
+    assert p.splits == 1 and p.workspace_bytes == 0
+    p = W.plan(4, 4096, 4096, 32, True, torch.float16, route=W.ROUTE_DECODE, scale_in_tile=0)
+    assert p.scale_in_tile == 0
+
+
+def test_planned_call_rejects_mismatched_plan():
+    p = W.plan(4, 4096, 4096, 32, True, torch.float16)
+    p.grid += 1
+    st = W.lib().w4a16_gemm_planned(FAKE, FAKE, FAKE, FAKE, 32, 8, FAKE, 4, 4096, 4096, W.F16,
+                                    ctypes.byref(p), None)
+    assert st == W.ERR_PLAN

@@ -1,0 +1,284 @@
+"""GPU parity: the HIP library against the CPU oracle, through the C ABI.
+
+* dequantised tiles: bit-exact (``w4a16_dequant`` vs ``oracle.dequant_tile``);
+* GEMM outputs: ``|gpu - oracle| <= 2e-2 * max(1, |oracle|)`` after the cast
+  to the output dtype, element by element (full arrays at small sizes,
+  sampled rows/columns at the full workload sizes);
+* exact-arithmetic inputs (small integers times powers of two), one-hot
+  activations and q == z: bit-exact, on both routes;
+* determinism, output canaries, input immutability and edge shapes.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from weight_only_int4_unpack_amd import w4a16 as W
+from helpers import (assert_within_tolerance, bits_to_dev, dev_to_bits, make_problem,
+                     random_problem, workload_problem, TORCH_DT)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _plan(p, route, splits=0, sit=-1):
+    return W.plan(p.M, p.K, p.N, p.G, p.qz is not None, TORCH_DT[p.dtype], route=route,
+                  splits=splits, scale_in_tile=sit)
+
+
+def _routes(M):
+    """(label, plan factory) pairs that apply to a problem with M rows."""
+    out = [("auto", lambda p: None), ("prefill", lambda p: _plan(p, W.ROUTE_PREFILL))]
+    if 1 <= M <= 16:
+        out += [("decode_sit0", lambda p: _plan(p, W.ROUTE_DECODE, sit=0)),
+                ("decode_sit1", lambda p: _plan(p, W.ROUTE_DECODE, sit=1)),
+                ("decode_s1", lambda p: _plan(p, W.ROUTE_DECODE, splits=1))]
+    return out
+
+
+# ---------------------------------------------------------------- dequant probe
+@pytest.mark.parametrize("K,N,G,dtype,zp", [
+    (256, 512, 128, "fp16", False),
+    (2112, 5120, 64, "fp16", True),
+    (4096, 4096, 32, "fp16", True),
+    (4096, 4096, 4096, "fp16", True),
+    (5120, 2048, 128, "bf16", False),
+    (1024, 1024, 64, "bf16", True),
+    (129, 520, 129, "bf16", True),
+    (64, 520, 32, "fp16", False),
+])
+def test_dequant_probe_bit_exact(K, N, G, dtype, zp):
+    p = random_problem(1, K, N, G, dtype, zp, seed=K + N + G)
+    got = dev_to_bits(W.dequant(p.b_q_d, p.s, p.qz_d, G, 8))
+    want = O.dequant_tile(p.b_q, p.s_bits, p.qz, G, 8, dtype)
+    assert np.array_equal(got, want), f"{int((got != want).sum())} mismatching weights"
+
+
+def test_dequant_probe_zp_bias_values():
+    for zp in (0, 7, 15):
+        p = random_problem(1, 128, 256, 64, "fp16", False, seed=40 + zp, zp_bias=zp)
+        got = dev_to_bits(W.dequant(p.b_q_d, p.s, None, 64, zp))
+        assert np.array_equal(got, O.dequant_tile(p.b_q, p.s_bits, None, 64, zp, "fp16"))
+
+
+# ---------------------------------------------------------------- parity grid
+GRID = [(M, dtype, G, zp) for M in (1, 5, 6, 64) for dtype in ("fp16", "bf16")
+        for G in (32, 64, 128, 512) for zp in (False, True)]
+
+
+@pytest.mark.parametrize("M,dtype,G,zp", GRID)
+def test_gemm_parity_grid(M, dtype, G, zp):
+    K, N = 512, 768
+    p = random_problem(M, K, N, G, dtype, zp, seed=M * 7 + G)
+    want = p.oracle_gemm()
+    for label, mk in _routes(M):
+        got = dev_to_bits(p.gpu_gemm(plan=mk(p)))
+        assert_within_tolerance(got, want, dtype, f"M={M} {dtype} G={G} zp={zp} {label}")
+
+
+# ---------------------------------------------------------------- workloads
+def _check_workload(name, rows=None, cols=None, routes=True):
+    p = workload_problem(name)
+    labels = _routes(p.M) if routes else [("auto", lambda q: None)]
+    want = p.oracle_gemm(rows=rows, cols=cols)
+    for label, mk in labels:
+        out = dev_to_bits(p.gpu_gemm(plan=mk(p)))
+        if rows is not None:
+            out = out[np.asarray(rows)]
+        if cols is not None:
+            out = out[:, np.asarray(cols)]
+        assert_within_tolerance(out, want, p.dtype, f"{name} {label}")
+
+
+def test_workload_tiny():
+    _check_workload("tiny")
+
+
+def test_workload_k2112():
+    _check_workload("k2112")
+
+
+@pytest.mark.parametrize("name", ["decode_m1", "decode_m5"])
+def test_workload_decode_sampled(name):
+    rng = np.random.default_rng(3)
+    cols = np.unique(np.concatenate([np.arange(0, 64), np.arange(17408 - 64, 17408),
+                                     rng.choice(17408, 512, replace=False)]))
+    _check_workload(name, cols=cols)
+
+
+def test_workload_prefill_sampled():
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 2047], rng.choice(2048, 59, replace=False)]))
+    cols = np.unique(np.concatenate([np.arange(0, 32), np.arange(17408 - 32, 17408),
+                                     rng.choice(17408, 448, replace=False)]))
+    _check_workload("prefill", rows=rows, cols=cols, routes=False)
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 5, 6, 16, 64, 256])
+def test_workload_sweep(m):
+    _check_workload(f"sweep_m{m}", routes=m <= 16)
+
+
+def test_workload_sweep_m4096_sampled():
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 4095], rng.choice(4096, 126, replace=False)]))
+    _check_workload("sweep_m4096", rows=rows, routes=False)
+
+
+def test_workload_sweep_per_channel():
+    _check_workload("sweep_pc16")
+
+
+# ---------------------------------------------------------------- exact pins
+def _exact_problem(M, K, N, G, dtype, zp, seed):
+    rng = np.random.default_rng(seed)
+    a = np.zeros((M, K), np.float32)
+    for m in range(M):
+        idx = rng.choice(K, size=16, replace=False)
+        a[m, idx] = rng.choice([-1.0, 1.0], size=16)
+    d = {"a_bits": O.rne_bits(a, dtype),
+         "q": rng.integers(0, 16, size=(K, N), dtype=np.uint8),
+         "s_bits": O.rne_bits(np.full((K // G, N), 1.0 / 16, np.float32), dtype),
+         "z": rng.integers(0, 16, size=(K // G, N), dtype=np.uint8) if zp else None}
+    return make_problem(d, M, K, N, G, dtype)
+
+
+@pytest.mark.parametrize("M,K,N,G,dtype,zp", [
+    (4, 4096, 512, 128, "bf16", False),
+    (8, 2112, 640, 64, "fp16", True),
+    (16, 4096, 512, 32, "fp16", True),
+    (64, 1024, 768, 1024, "bf16", True),
+    (300, 512, 256, 32, "fp16", False),
+])
+def test_exact_arithmetic_bitwise(M, K, N, G, dtype, zp):
+    p = _exact_problem(M, K, N, G, dtype, zp, seed=M + K)
+    want = p.oracle_gemm()
+    for label, mk in _routes(M):
+        got = dev_to_bits(p.gpu_gemm(plan=mk(p)))
+        assert np.array_equal(got, want), f"{label}: {int((got != want).sum())} differ"
+
+
+@pytest.mark.parametrize("dtype,G,zp", [("fp16", 32, True), ("bf16", 128, False),
+                                        ("fp16", 64, False), ("bf16", 256, True)])
+def test_one_hot_rows_bitwise(dtype, G, zp):
+    K, N = 256, 512
+    p = random_problem(1, K, N, G, dtype, zp, seed=G)
+    ks = [0, 1, 31, 32, 100, 127, 128, 255, 7, 200, 64, 65, 96, 33]
+    a = np.zeros((len(ks), K), np.float32)
+    for i, k in enumerate(ks):
+        a[i, k] = 1.0
+    p.a_bits = O.rne_bits(a, dtype)
+    p.a = bits_to_dev(p.a_bits, dtype)
+    p.M = len(ks)
+    tile = O.dequant_tile(p.b_q, p.s_bits, p.qz, G, 8, dtype)[ks]
+    for label, mk in _routes(p.M):
+        got = dev_to_bits(p.gpu_gemm(plan=mk(p)))
+        assert np.array_equal(got, tile), f"{label}: {int((got != tile).sum())} differ"
+
+
+@pytest.mark.parametrize("dtype,zp", [("fp16", True), ("bf16", False)])
+def test_q_equals_z_gives_zero(dtype, zp):
+    M, K, N, G = 8, 512, 512, 64
+    rng = np.random.default_rng(9)
+    z = rng.integers(0, 16, size=(K // G, N), dtype=np.uint8) if zp else None
+    q = np.repeat(z, G, axis=0) if zp else np.full((K, N), 8, np.uint8)
+    d = {"a_bits": O.rne_bits(rng.standard_normal((M, K)).astype(np.float32), dtype), "q": q,
+         "s_bits": O.rne_bits(rng.uniform(1e-3, 1e-2, (K // G, N)).astype(np.float32), dtype),
+         "z": z}
+    p = make_problem(d, M, K, N, G, dtype)
+    for label, mk in _routes(M):
+        got = O.to_f32(dev_to_bits(p.gpu_gemm(plan=mk(p))), dtype)
+        assert np.all(got == 0.0), label
+
+
+@pytest.mark.parametrize("M", [5, 100])
+def test_scale_linearity_bitwise(M):
+    p = random_problem(M, 1024, 512, 64, "bf16", True, seed=77)
+    base = {label: dev_to_bits(p.gpu_gemm(plan=mk(p))) for label, mk in _routes(M)}
+    p.s = p.s * 2
+    for label, mk in _routes(M):
+        got = O.to_f32(dev_to_bits(p.gpu_gemm(plan=mk(p))), "bf16")
+        assert np.array_equal(got, 2 * O.to_f32(base[label], "bf16")), label
+
+
+# ---------------------------------------------------------------- robustness
+@pytest.mark.parametrize("M", [5, 8, 300])
+def test_deterministic_repeat(M):
+    p = random_problem(M, 4096, 4096, 32, "fp16", True, seed=5)
+    for label, mk in _routes(M):
+        r1 = dev_to_bits(p.gpu_gemm(plan=mk(p)))
+        r2 = dev_to_bits(p.gpu_gemm(plan=mk(p)))
+        assert np.array_equal(r1, r2), label
+
+
+@pytest.mark.parametrize("M", [3, 70])
+def test_canaries_and_inputs_untouched(M):
+    p = random_problem(M, 512, 520, 128, "fp16", True, seed=11)
+    snap = [t.clone() for t in (p.a, p.b_q_d, p.s, p.qz_d)]
+    guard = 4096
+    for label, mk in _routes(M):
+        buf = torch.full((guard * 2 + M * p.N,), 12345, dtype=torch.int16, device="cuda")
+        out = buf[guard:guard + M * p.N].view(torch.float16).view(M, p.N)
+        p.gpu_gemm(plan=mk(p), out=out)
+        torch.cuda.synchronize()
+        assert torch.all(buf[:guard] == 12345) and torch.all(buf[guard + M * p.N:] == 12345), label
+        assert_within_tolerance(dev_to_bits(out), p.oracle_gemm(), "fp16", label)
+    for t, s in zip((p.a, p.b_q_d, p.s, p.qz_d), snap):
+        assert torch.equal(t, s)
+
+
+@pytest.mark.parametrize("M,K,N,G,dtype,zp", [
+    (1, 2120, 520, 2120, "fp16", True),     # K % 32 != 0, N % 256 != 0
+    (7, 129, 264, 129, "bf16", False),      # K % 8 != 0 (per-channel)
+    (16, 96, 24, 32, "fp16", True),         # fewer columns than one block
+    (2, 4096, 8, 128, "bf16", True),        # N = 8
+    (17, 640, 1032, 64, "fp16", False),     # first prefill M, ragged N
+    (129, 2120, 520, 2120, "bf16", True),   # ragged M, K and N on prefill
+    (255, 64, 256, 32, "fp16", True),       # a single K tile
+])
+def test_edge_shapes(M, K, N, G, dtype, zp):
+    p = random_problem(M, K, N, G, dtype, zp, seed=M + K + N)
+    want = p.oracle_gemm()
+    for label, mk in _routes(M):
+        got = dev_to_bits(p.gpu_gemm(plan=mk(p)))
+        assert_within_tolerance(got, want, dtype, f"{label}")
+
+
+def test_decode_every_m_up_to_16():
+    p16 = random_problem(16, 1024, 1024, 128, "bf16", False, seed=21)
+    for M in range(1, 17):
+        p = make_problem({"a_bits": p16.a_bits[:M], "q": W.unpack_int4(p16.b_q),
+                          "s_bits": p16.s_bits, "z": None}, M, 1024, 1024, 128, "bf16")
+        got = dev_to_bits(p.gpu_gemm(plan=_plan(p, W.ROUTE_DECODE)))
+        assert_within_tolerance(got, p.oracle_gemm(), "bf16", f"M={M}")
+
+
+def test_m_zero_is_noop():
+    p = random_problem(1, 256, 512, 128, "fp16", False, seed=1)
+    a0 = torch.empty((0, 256), dtype=torch.float16, device="cuda")
+    out = W.gemm(a0, p.b_q_d, p.s, None, 128)
+    assert tuple(out.shape) == (0, 512)
+
+
+def test_pages_shape_contract_gpu():
+    g = json.load(open(os.path.join(GOLDEN, "pages_shape_contract.json")))
+    M, K = g["a_shape"]
+    N = g["b_q_shape"][1] * 8
+    p = random_problem(M, K, N, g["group_size"], g["a_dtype"], False, seed=2)
+    out = W.gemm(p.a, p.b_q_d, p.s, None, g["group_size"])
+    assert list(out.shape) == g["out_shape"] and out.dtype == torch.float16
+    assert out.device == p.a.device
+
+
+def test_streams_are_respected():
+    p = random_problem(5, 2048, 2048, 128, "bf16", False, seed=31)
+    want = p.oracle_gemm()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = p.gpu_gemm()
+    s.synchronize()
+    assert_within_tolerance(dev_to_bits(out), want, "bf16", "side stream")

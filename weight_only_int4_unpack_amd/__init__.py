@@ -5,12 +5,4 @@ The compute path is the HIP library ``libw4a16.so`` built from ``csrc/``;
 a missing build raises immediately: there is no fallback path.
 """
 from . import synthetic  # noqa: F401  (random inputs only; no arithmetic)
-
-
-def __getattr__(name):
-    # Load the binding lazily so that ``synthetic`` (and the CPU tests of the
-    # oracle that use it) import without a built library.
-    if name == "w4a16":
-        from . import w4a16 as mod
-        return mod
-    raise AttributeError(name)
+from . import w4a16  # noqa: F401  (binding; loads the library on first call)

@@ -1,0 +1,426 @@
+// Host side of the C ABI in include/w4a16.h: argument checks, the runtime
+// route/tile selector, launches and the host pack utility.
+//
+// Checks follow the kernel-selection rules of PR #43731
+// "TritonW4A16LinearKernel as CUDA fallback" (Code section, can_implement):
+// fp16/bf16 activations only, N % 8 == 0, and a group size from the
+// supported set or equal to the full K; no input is a silent substitute
+// (PR #40977 "RDNA hybrid W4A16", Review section: group size 64 was run with
+// the parameters of 128). The route and tiles are picked from the runtime
+// shape on every call (PR #51453 "Register the Triton W4A16 GEMM as a custom
+// op", Motivation and implementation item 1).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/w4a16.h"
+#include "w4a16_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+w4a16_status fail(w4a16_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+w4a16_status check_shape(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype) {
+  if (dtype != W4A16_F16 && dtype != W4A16_BF16)
+    return fail(W4A16_ERR_DTYPE, "dtype %d: only fp16 (0) and bf16 (1) activations are supported",
+                (int)dtype);
+  if (M < 0 || K <= 0 || N <= 0)
+    return fail(W4A16_ERR_SHAPE, "need M >= 0, K > 0, N > 0 (got M=%lld K=%lld N=%lld)",
+                (long long)M, (long long)K, (long long)N);
+  if (N % 8 != 0)
+    return fail(W4A16_ERR_SHAPE, "N=%lld must be divisible by 8 (8 int4 values per int32)",
+                (long long)N);
+  if (!(G == 32 || G == 64 || G == 128 || (int64_t)G == K))
+    return fail(W4A16_ERR_GROUP, "group size %d not supported (32, 64, 128 or K=%lld)", (int)G,
+                (long long)K);
+  if (K % G != 0)
+    return fail(W4A16_ERR_SHAPE, "K=%lld is not a multiple of group size %d", (long long)K,
+                (int)G);
+  // 32-bit index limits of the kernels (rows, columns, and per-row offsets)
+  const int64_t lim = (int64_t)1 << 31;
+  if (K >= lim || N >= lim || M >= lim || (K / G) * N >= lim || M * K >= lim * 64 ||
+      K * (N / 8) >= lim * 64)
+    return fail(W4A16_ERR_SHAPE, "problem too large for 32-bit row/column indexing");
+  return W4A16_OK;
+}
+
+w4a16_status check_ptrs(const void* a, const void* b_q, const void* scales, const void* qzeros,
+                        const void* out, int32_t zp_bias) {
+  if (!a || !b_q || !scales || !out)
+    return fail(W4A16_ERR_NULL, "a, b_q, scales and out must be non-NULL");
+  if (!qzeros && (zp_bias < 0 || zp_bias > 15))
+    return fail(W4A16_ERR_ZP, "zp_bias=%d must lie in 0..15", (int)zp_bias);
+  if (!aligned16(a) || !aligned16(b_q) || !aligned16(scales) || !aligned16(out) ||
+      (qzeros && !aligned16(qzeros)))
+    return fail(W4A16_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  return W4A16_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// selector
+// ---------------------------------------------------------------------------
+void plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype, int num_cus,
+                 int32_t splits, int32_t sit, w4a16_plan_t* pl) {
+  using namespace w4a16;
+  const int64_t KS = ceil_div(K, kStepRows);
+  const int64_t NB = ceil_div(N, kDecodeCols);
+  // Aim at about 8 wavefronts per CU (two per SIMD), each holding at least
+  // one 32-row step.
+  int64_t S = splits;
+  if (S <= 0) {
+    const int64_t target_waves = 8 * (int64_t)num_cus;
+    const int64_t per_wg = kDecodeWaves;
+    S = std::max<int64_t>(1, (target_waves + NB * per_wg - 1) / (NB * per_wg));
+  }
+  S = std::min<int64_t>(S, ceil_div(KS, kDecodeWaves));
+  S = std::max<int64_t>(S, 1);
+  int64_t L = ceil_div(KS, S * kDecodeWaves);
+  S = ceil_div(KS, L * kDecodeWaves);  // drop empty splits
+  // Scale placement: folding the scale into each weight costs a fixed amount
+  // per weight; applying it per group costs per (group, output) pair. fp16
+  // small groups favour the first, everything else the second.
+  int32_t scale_in_tile = sit;
+  if (scale_in_tile < 0) scale_in_tile = (dtype == W4A16_F16 && G <= 64 && G != K) ? 1 : 0;
+  pl->route = W4A16_ROUTE_DECODE;
+  pl->block_m = kDecodeMaxM;
+  pl->block_n = kDecodeCols;
+  pl->block_k = kStepRows;
+  pl->scale_in_tile = scale_in_tile;
+  pl->splits = (int32_t)S;
+  pl->steps_per_wave = (int32_t)L;
+  pl->grid = (int32_t)(NB * S);
+  pl->threads = kDecodeThreads;
+  pl->lds_bytes = decode_lds_bytes((int)M);
+  pl->workspace_bytes = S > 1 ? (int64_t)(S * M * N * 4 + NB * 4 + 256) : 0;
+}
+
+void plan_prefill(int64_t M, int64_t N, w4a16_plan_t* pl) {
+  using namespace w4a16;
+  int bm = 256;
+  if (M <= 64)
+    bm = 64;
+  else if (M <= 128)
+    bm = 128;
+  const int64_t tm = ceil_div(M, bm), tn = ceil_div(N, kPrefillBN);
+  const int64_t per_xcd = ceil_div(tm * tn, kXcds);
+  pl->route = W4A16_ROUTE_PREFILL;
+  pl->block_m = bm;
+  pl->block_n = kPrefillBN;
+  pl->block_k = kPrefillBK;
+  pl->scale_in_tile = 1;
+  pl->splits = 1;
+  pl->steps_per_wave = 0;
+  pl->grid = (int32_t)(per_xcd * kXcds);
+  pl->threads = kPrefillThreads;
+  pl->lds_bytes = prefill_lds_bytes(bm);
+  pl->workspace_bytes = 0;
+}
+
+w4a16_status make_plan(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype, int32_t num_cus,
+                       int32_t route, int32_t splits, int32_t sit, w4a16_plan_t* pl) {
+  if (!pl) return fail(W4A16_ERR_NULL, "plan must be non-NULL");
+  w4a16_status st = check_shape(M, K, N, G, dtype);
+  if (st != W4A16_OK) return st;
+  std::memset(pl, 0, sizeof(*pl));
+  if (num_cus <= 0) num_cus = 256;
+  if (M == 0) {
+    pl->route = W4A16_ROUTE_NONE;
+    return W4A16_OK;
+  }
+  if (route == 0) route = (M <= w4a16::kAutoDecodeMaxM) ? W4A16_ROUTE_DECODE : W4A16_ROUTE_PREFILL;
+  if (route == W4A16_ROUTE_DECODE) {
+    if (M > w4a16::kDecodeMaxM)
+      return fail(W4A16_ERR_PLAN, "decode route needs M <= %d (got %lld)", w4a16::kDecodeMaxM,
+                  (long long)M);
+    plan_decode(M, K, N, G, dtype, num_cus, splits, sit, pl);
+  } else if (route == W4A16_ROUTE_PREFILL) {
+    plan_prefill(M, N, pl);
+  } else {
+    return fail(W4A16_ERR_PLAN, "unknown route %d", (int)route);
+  }
+  return W4A16_OK;
+}
+
+// A caller-supplied plan must be one the selector could have produced.
+w4a16_status check_plan(const w4a16_plan_t* pl, int64_t M, int64_t K, int64_t N, int32_t G,
+                        int32_t dtype) {
+  w4a16_plan_t ref;
+  w4a16_status st = make_plan(M, K, N, G, dtype, 256, pl->route,
+                              pl->route == W4A16_ROUTE_DECODE ? pl->splits : 0,
+                              pl->route == W4A16_ROUTE_DECODE ? pl->scale_in_tile : -1, &ref);
+  if (st != W4A16_OK) return st;
+  if (std::memcmp(&ref, pl, sizeof(ref)) != 0)
+    return fail(W4A16_ERR_PLAN, "plan does not match the problem (route %d)", (int)pl->route);
+  return W4A16_OK;
+}
+
+// ---------------------------------------------------------------------------
+// per-device state: architecture check, CU count, split-K scratch
+// ---------------------------------------------------------------------------
+struct DeviceState {
+  bool probed = false;
+  bool ok = false;
+  int num_cus = 0;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+};
+std::mutex g_mu;
+std::vector<DeviceState> g_dev;
+
+w4a16_status device_state(DeviceState** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(W4A16_ERR_DEVICE, "no HIP device available");
+  }
+  std::lock_guard<std::mutex> lk(g_mu);
+  if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
+  DeviceState& ds = g_dev[dev];
+  if (!ds.probed) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(W4A16_ERR_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
+    }
+    ds.probed = true;
+    ds.ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    ds.num_cus = prop.multiProcessorCount;
+  }
+  if (!ds.ok) return fail(W4A16_ERR_DEVICE, "device %d is not a gfx950 (MI355X) GPU", dev);
+  *out = &ds;
+  return W4A16_OK;
+}
+
+// Grows the device's split-K scratch; new memory is zeroed once so the
+// arrival counters start at zero (the kernels leave them at zero).
+w4a16_status ensure_workspace(DeviceState* ds, size_t bytes, hipStream_t stream) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (ds->ws_bytes >= bytes) return W4A16_OK;
+  if (ds->ws) {
+    if (hipStreamSynchronize(stream) != hipSuccess || hipFree(ds->ws) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(W4A16_ERR_HIP, "freeing the old split-K scratch failed");
+    }
+    ds->ws = nullptr;
+    ds->ws_bytes = 0;
+  }
+  size_t sz = std::max<size_t>(bytes, (size_t)8 << 20);
+  if (hipMalloc(&ds->ws, sz) != hipSuccess) {
+    (void)hipGetLastError();
+    ds->ws = nullptr;
+    return fail(W4A16_ERR_HIP, "hipMalloc of %zu bytes of split-K scratch failed", sz);
+  }
+  if (hipMemset(ds->ws, 0, sz) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(W4A16_ERR_HIP, "clearing the split-K scratch failed");
+  }
+  ds->ws_bytes = sz;
+  return W4A16_OK;
+}
+
+w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, DeviceState* ds,
+                 hipStream_t stream) {
+  using namespace w4a16;
+  hipError_t e = hipSuccess;
+  if (pl.route == W4A16_ROUTE_NONE) return W4A16_OK;
+  if (pl.route == W4A16_ROUTE_DECODE) {
+    DecodeParams p{};
+    p.a = (const uint16_t*)g.a;
+    p.bq = (const uint32_t*)g.b_q;
+    p.sc = (const uint16_t*)g.scales;
+    p.qz = (const uint32_t*)g.qzeros;
+    p.out = (uint16_t*)g.out;
+    p.M = (int32_t)g.M;
+    p.K = (int32_t)g.K;
+    p.N = (int32_t)g.N;
+    p.G = g.G;
+    p.zp_bias = g.zp_bias;
+    p.KS = (int32_t)ceil_div(g.K, kStepRows);
+    p.SG = ((int64_t)g.G == g.K) ? p.KS : g.G / kStepRows;
+    p.L = pl.steps_per_wave;
+    p.S = pl.splits;
+    p.NB = (int32_t)ceil_div(g.N, kDecodeCols);
+    if (pl.splits > 1) {
+      w4a16_status st = ensure_workspace(ds, (size_t)pl.workspace_bytes, stream);
+      if (st != W4A16_OK) return st;
+      const size_t part = (size_t)pl.splits * g.M * g.N * 4;
+      p.ws = (float*)ds->ws;
+      p.counters = (int32_t*)((char*)ds->ws + ((part + 255) & ~(size_t)255));
+    }
+    e = launch_decode(p, g.dtype, g.qzeros != nullptr, pl.scale_in_tile != 0, pl.grid,
+                      pl.lds_bytes, stream);
+  } else {
+    PrefillParams p{};
+    p.a = (const uint16_t*)g.a;
+    p.bq = (const uint32_t*)g.b_q;
+    p.sc = (const uint16_t*)g.scales;
+    p.qz = (const uint32_t*)g.qzeros;
+    p.out = (uint16_t*)g.out;
+    p.M = (int32_t)g.M;
+    p.K = (int32_t)g.K;
+    p.N = (int32_t)g.N;
+    p.G = g.G;
+    p.zp_bias = g.zp_bias;
+    p.tiles_m = (int32_t)ceil_div(g.M, pl.block_m);
+    p.tiles_n = (int32_t)ceil_div(g.N, kPrefillBN);
+    p.per_xcd = pl.grid / kXcds;
+    e = launch_prefill(p, g.dtype, g.qzeros != nullptr, pl.block_m, pl.grid, stream);
+  }
+  if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return W4A16_OK;
+}
+
+w4a16_status gemm_common(const void* a, const int32_t* b_q, const void* scales,
+                         const int32_t* qzeros, int32_t G, int32_t zp_bias, void* out, int64_t M,
+                         int64_t K, int64_t N, int32_t dtype, const w4a16_plan_t* forced,
+                         void* stream) {
+  w4a16_status st = check_shape(M, K, N, G, dtype);
+  if (st != W4A16_OK) return st;
+  if (M == 0) return W4A16_OK;
+  st = check_ptrs(a, b_q, scales, qzeros, out, zp_bias);
+  if (st != W4A16_OK) return st;
+  if (forced) {
+    st = check_plan(forced, M, K, N, G, dtype);
+    if (st != W4A16_OK) return st;
+  }
+  DeviceState* ds = nullptr;
+  st = device_state(&ds);
+  if (st != W4A16_OK) return st;
+  w4a16_plan_t pl;
+  if (forced) {
+    pl = *forced;
+  } else {
+    st = make_plan(M, K, N, G, dtype, ds->num_cus, 0, 0, -1, &pl);
+    if (st != W4A16_OK) return st;
+  }
+  if (const char* lg = std::getenv("W4A16_LOG")) {
+    if (lg[0] == '1')
+      std::fprintf(stderr,
+                   "[w4a16] M=%lld K=%lld N=%lld G=%d route=%d bm=%d splits=%d L=%d sit=%d grid=%d\n",
+                   (long long)M, (long long)K, (long long)N, (int)G, pl.route, pl.block_m, pl.splits,
+                   pl.steps_per_wave, pl.scale_in_tile, pl.grid);
+  }
+  w4a16::GemmArgs g{a, b_q, scales, qzeros, out, M, K, N, G, zp_bias, dtype};
+  return run(g, pl, ds, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+w4a16_status w4a16_gemm(const void* a, const int32_t* b_q, const void* scales,
+                        const int32_t* qzeros, int32_t group_size, int32_t zp_bias, void* out,
+                        int64_t M, int64_t K, int64_t N, int32_t dtype, void* stream) {
+  return gemm_common(a, b_q, scales, qzeros, group_size, zp_bias, out, M, K, N, dtype, nullptr,
+                     stream);
+}
+
+w4a16_status w4a16_gemm_planned(const void* a, const int32_t* b_q, const void* scales,
+                                const int32_t* qzeros, int32_t group_size, int32_t zp_bias,
+                                void* out, int64_t M, int64_t K, int64_t N, int32_t dtype,
+                                const w4a16_plan_t* plan, void* stream) {
+  if (!plan) return fail(W4A16_ERR_NULL, "plan must be non-NULL");
+  return gemm_common(a, b_q, scales, qzeros, group_size, zp_bias, out, M, K, N, dtype, plan,
+                     stream);
+}
+
+w4a16_status w4a16_plan(int64_t M, int64_t K, int64_t N, int32_t group_size, int32_t has_zp,
+                        int32_t dtype, int32_t num_cus, w4a16_plan_t* plan) {
+  (void)has_zp;
+  return make_plan(M, K, N, group_size, dtype, num_cus, 0, 0, -1, plan);
+}
+
+w4a16_status w4a16_plan_route(int64_t M, int64_t K, int64_t N, int32_t group_size, int32_t has_zp,
+                              int32_t dtype, int32_t num_cus, int32_t route, int32_t splits,
+                              int32_t scale_in_tile, w4a16_plan_t* plan) {
+  (void)has_zp;
+  if (route != W4A16_ROUTE_DECODE && route != W4A16_ROUTE_PREFILL)
+    return fail(W4A16_ERR_PLAN, "route must be decode (1) or prefill (2), got %d", (int)route);
+  return make_plan(M, K, N, group_size, dtype, num_cus, route, splits, scale_in_tile, plan);
+}
+
+w4a16_status w4a16_dequant(const int32_t* b_q, const void* scales, const int32_t* qzeros,
+                           int32_t group_size, int32_t zp_bias, void* w_out, int64_t K, int64_t N,
+                           int32_t dtype, void* stream) {
+  w4a16_status st = check_shape(1, K, N, group_size, dtype);
+  if (st != W4A16_OK) return st;
+  if (!b_q || !scales || !w_out) return fail(W4A16_ERR_NULL, "b_q, scales and w_out must be non-NULL");
+  if (!qzeros && (zp_bias < 0 || zp_bias > 15))
+    return fail(W4A16_ERR_ZP, "zp_bias=%d must lie in 0..15", (int)zp_bias);
+  if (!aligned16(b_q) || !aligned16(scales) || !aligned16(w_out) || (qzeros && !aligned16(qzeros)))
+    return fail(W4A16_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  DeviceState* ds = nullptr;
+  st = device_state(&ds);
+  if (st != W4A16_OK) return st;
+  w4a16::DequantParams p{(const uint32_t*)b_q, (const uint16_t*)scales, (const uint32_t*)qzeros,
+                         (uint16_t*)w_out,     (int32_t)K,              (int32_t)N,
+                         group_size,           zp_bias};
+  hipError_t e = w4a16::launch_dequant(p, dtype, qzeros != nullptr, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_pack_int4(const uint8_t* q, int64_t rows, int64_t cols, int32_t* packed) {
+  if (rows < 0 || cols < 0 || cols % 8 != 0)
+    return fail(W4A16_ERR_SHAPE, "need rows >= 0 and cols a non-negative multiple of 8");
+  if (rows * cols == 0) return W4A16_OK;
+  if (!q || !packed) return fail(W4A16_ERR_NULL, "q and packed must be non-NULL");
+  const int64_t words = cols / 8;
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint8_t* src = q + r * cols;
+    int32_t* dst = packed + r * words;
+    for (int64_t w = 0; w < words; ++w) {
+      uint32_t v = 0;
+      for (int j = 0; j < 8; ++j) {
+        const uint8_t x = src[8 * w + j];
+        if (x > 15)
+          return fail(W4A16_ERR_VALUE, "value %u at (%lld, %lld) is outside 0..15", (unsigned)x,
+                      (long long)r, (long long)(8 * w + j));
+        v |= (uint32_t)x << (4 * j);
+      }
+      dst[w] = (int32_t)v;
+    }
+  }
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_unpack_int4(const int32_t* packed, int64_t rows, int64_t cols, uint8_t* q) {
+  if (rows < 0 || cols < 0 || cols % 8 != 0)
+    return fail(W4A16_ERR_SHAPE, "need rows >= 0 and cols a non-negative multiple of 8");
+  if (rows * cols == 0) return W4A16_OK;
+  if (!q || !packed) return fail(W4A16_ERR_NULL, "q and packed must be non-NULL");
+  const int64_t words = cols / 8;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t w = 0; w < words; ++w) {
+      const uint32_t v = (uint32_t)packed[r * words + w];
+      for (int j = 0; j < 8; ++j) q[r * cols + 8 * w + j] = (uint8_t)((v >> (4 * j)) & 0xFu);
+    }
+  return W4A16_OK;
+}
+
+const char* w4a16_last_error(void) { return g_last_error.c_str(); }
+
+const char* w4a16_version(void) { return "w4a16-gfx950 0.1.0"; }
+
+}  // extern "C"

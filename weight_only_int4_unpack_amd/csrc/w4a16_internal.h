@@ -1,0 +1,90 @@
+// Internal interface between the host side (validation, selector, launches)
+// and the gfx950 kernels. Every tile constant lives here once, so the host's
+// LDS accounting and the kernels' arrays cannot drift apart (PR #40977,
+// Review section: a hard-coded LDS size disagreed with the host-side check).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/w4a16.h"
+
+namespace w4a16 {
+
+// ---- decode route (skinny split-K, MFMA 16x16x32 with M padded to 16)
+constexpr int kDecodeMaxM = 16;        // rows of one MFMA tile
+constexpr int kDecodeCols = 256;       // output columns per workgroup
+constexpr int kDecodeWaves = 4;        // wavefronts per workgroup
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
+constexpr int kStepRows = 32;          // K rows per MFMA step
+constexpr int kDecodeChunk = 4;        // steps whose loads are issued together
+constexpr int kAutoDecodeMaxM = 16;    // selector: decode for 1 <= M <= this
+
+// ---- prefill route (tiled MFMA)
+constexpr int kPrefillBN = 256;        // output columns per workgroup (4 waves x 64)
+constexpr int kPrefillBK = 64;         // K rows per pipeline stage
+constexpr int kPrefillThreads = 256;
+constexpr int kPrefillLdsRowHalves = kPrefillBK + 8;  // padded A-tile row
+
+constexpr int kXcds = 8;               // MI355X: workgroups round-robin over 8 XCDs
+
+inline int decode_lds_bytes(int M) {
+  return kDecodeWaves * M * kDecodeCols * (int)sizeof(float);
+}
+inline int prefill_lds_bytes(int BM) {
+  return 2 * BM * kPrefillLdsRowHalves * 2;
+}
+
+struct GemmArgs {
+  const void* a;
+  const int32_t* b_q;
+  const void* scales;
+  const int32_t* qzeros;  // nullable
+  void* out;
+  int64_t M, K, N;
+  int32_t G, zp_bias, dtype;
+};
+
+struct DecodeParams {
+  const uint16_t* a;
+  const uint32_t* bq;
+  const uint16_t* sc;
+  const uint32_t* qz;
+  uint16_t* out;
+  float* ws;          // [S, M, N] fp32 partials (S > 1)
+  int32_t* counters;  // [NB] arrival counters, zero between launches
+  int32_t M, K, N, G, zp_bias;
+  int32_t KS;         // K steps of 32 rows
+  int32_t SG;         // steps per group
+  int32_t L;          // steps per wavefront
+  int32_t S;          // splits across workgroups
+  int32_t NB;         // column blocks
+};
+
+struct PrefillParams {
+  const uint16_t* a;
+  const uint32_t* bq;
+  const uint16_t* sc;
+  const uint32_t* qz;
+  uint16_t* out;
+  int32_t M, K, N, G, zp_bias;
+  int32_t tiles_m, tiles_n, per_xcd;
+};
+
+struct DequantParams {
+  const uint32_t* bq;
+  const uint16_t* sc;
+  const uint32_t* qz;
+  uint16_t* w;
+  int32_t K, N, G, zp_bias;
+};
+
+hipError_t launch_decode(const DecodeParams& p, int dtype, bool has_zp,
+                         bool scale_in_tile, int grid, int lds_bytes,
+                         hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, int dtype, bool has_zp,
+                          int block_m, int grid, hipStream_t stream);
+hipError_t launch_dequant(const DequantParams& p, int dtype, bool has_zp,
+                          hipStream_t stream);
+
+}  // namespace w4a16

@@ -1,0 +1,665 @@
+// gfx950 kernels of the weight-only int4 GEMM  C[M,N] = A[M,K] . dequant(B).
+//
+// Arithmetic follows PR #40977 "RDNA hybrid W4A16", Code section (the test's
+// reference: w = (q - z) * s with fp32 accumulation and one final cast); the
+// packed operand layout follows PR #51453 "Register the Triton W4A16 GEMM as
+// a custom op", implementation item 1 (b_q is [K, N/8], N = 8 * columns).
+//
+// Layout facts used everywhere below:
+//   * b_q word (k, c) holds columns 8c..8c+7 of row k, value j in bits
+//     [4j, 4j+4).
+//   * The MFMA v_mfma_f32_16x16x32_{f16,bf16} contracts 32 k per
+//     instruction; lane l supplies row/column (l & 15) of its operand and 8
+//     k-values chosen by lane group (l >> 4). The k-to-slot mapping is the
+//     same function for both operands, so any consistent assignment of
+//     logical k to (lane group, slot) is valid; here slot s of lane group g
+//     is logical row 8g + s of the 32-row step.
+//   * The accumulator of lane l holds rows 4(l >> 4) + v (v = 0..3) of
+//     column (l & 15).
+//
+// Dequantisation ("magic number"): OR-ing a uint4 into the low mantissa bits
+// of a float with unit ulp gives base + q exactly: fp16 0x6400 is 1024
+// (ulp 1), bf16 0x4300 is 128 (ulp 1). With two rows of four values in one
+// 32-bit word (row r in bits 0..15, row r+1 in bits 16..31) one AND-OR makes
+// a packed pair {base + q[r], base + q[r+1]} of one column. For fp16 the
+// value in bits 4..7 can be taken in place as 1024 + 16 q.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "w4a16_internal.h"
+
+namespace w4a16 {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct F16 {
+  static constexpr uint32_t kMagic = 0x64006400u;
+  static constexpr float kBase = 1024.0f;
+  static constexpr uint32_t kOnePair = 0x3C003C00u;
+};
+struct BF16 {
+  static constexpr uint32_t kMagic = 0x43004300u;
+  static constexpr float kBase = 128.0f;
+  static constexpr uint32_t kOnePair = 0x3F803F80u;
+};
+
+template <typename T>
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c);
+template <>
+__device__ __forceinline__ f32x4 mfma<F16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma<BF16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float widen(F16, uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+__device__ __forceinline__ float widen(BF16, uint32_t h) {
+  return __builtin_bit_cast(float, h << 16);
+}
+__device__ __forceinline__ uint16_t narrow(F16, float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+__device__ __forceinline__ uint16_t narrow(BF16, float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Pair {row r, row r+1} of column e (0..3) of Y as base + q (fp16, e odd:
+// base + 16 q).
+template <typename T, int E>
+__device__ __forceinline__ uint32_t magic_pair(uint32_t y) {
+  if constexpr (sizeof(T) && T::kBase == 1024.0f) {
+    constexpr uint32_t mask = (E & 1) ? 0x00F000F0u : 0x000F000Fu;
+    const uint32_t src = (E >= 2) ? (y >> 8) : y;
+    return (src & mask) | T::kMagic;
+  } else {
+    return ((y >> (4 * E)) & 0x000F000Fu) | T::kMagic;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Exact dequantisation of one pair to RNE_dtype((q - z) * s).
+//   fp16: (base + q) - (base + z) is the exact integer q - z (for e odd,
+//         (1024 + 16q)/16 - (64 + z)); one packed multiply rounds it once.
+//   bf16: (128 + q) * s and (128 + z) * s are exact in fp32, so one fp32 FMA
+//         gives (q - z) * s exactly; the bf16 conversion rounds once.
+// ---------------------------------------------------------------------------
+struct ColF16 {
+  f16x2 bias;   // {b, b}, b = 1024 + z (e even) or 64 + z (e odd)
+  f16x2 scale;  // {s, s}
+};
+struct ColBF16 {
+  float scale;  // s
+  float c;      // -(128 + z) * s, exact
+};
+template <typename T>
+struct Col;
+template <>
+struct Col<F16> { using type = ColF16; };
+template <>
+struct Col<BF16> { using type = ColBF16; };
+
+template <int E>
+__device__ __forceinline__ ColF16 make_col(F16, uint32_t s_bits, uint32_t z) {
+  ColF16 c;
+  const _Float16 b = (_Float16)(float)((E & 1) ? 64u + z : 1024u + z);
+  const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)s_bits);
+  c.bias = f16x2{b, b};
+  c.scale = f16x2{s, s};
+  return c;
+}
+template <int E>
+__device__ __forceinline__ ColBF16 make_col(BF16, uint32_t s_bits, uint32_t z) {
+  ColBF16 c;
+  c.scale = __builtin_bit_cast(float, s_bits << 16);
+  c.c = -(128.0f + (float)z) * c.scale;
+  return c;
+}
+
+template <int E>
+__device__ __forceinline__ uint32_t exact_pair(F16, uint32_t y, const ColF16& c) {
+  f16x2 h = __builtin_bit_cast(f16x2, magic_pair<F16, E>(y));
+  if constexpr (E & 1) {
+    const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    h = __builtin_elementwise_fma(h, sixteenth, -c.bias);
+  } else {
+    h = h - c.bias;
+  }
+  h = h * c.scale;
+  return __builtin_bit_cast(uint32_t, h);
+}
+template <int E>
+__device__ __forceinline__ uint32_t exact_pair(BF16, uint32_t y, const ColBF16& c) {
+  const uint32_t p = magic_pair<BF16, E>(y);
+  const float lo = __builtin_fmaf(__builtin_bit_cast(float, p << 16), c.scale, c.c);
+  const float hi = __builtin_fmaf(__builtin_bit_cast(float, p & 0xFFFF0000u), c.scale, c.c);
+  return (uint32_t)narrow(BF16{}, lo) | ((uint32_t)narrow(BF16{}, hi) << 16);
+}
+
+__device__ __forceinline__ uint32_t nib(uint32_t w, int j) { return (w >> (4 * j)) & 0xFu; }
+
+// Two rows' half-words h (0: columns 0..3, 1: columns 4..7) of words w0, w1
+// joined into one Y word (row of w0 in the low half).
+__device__ __forceinline__ uint32_t join_rows(uint32_t w0, uint32_t w1, int h) {
+  return __builtin_amdgcn_perm(w1, w0, h ? 0x07060302u : 0x05040100u);
+}
+
+// ---------------------------------------------------------------------------
+// Decode: M <= 16. A workgroup owns 256 output columns and a contiguous range
+// of 32-row K steps; its 4 wavefronts split the range. Lane (g, c) loads,
+// per step, rows 8g..8g+7 of words 2c, 2c+1 of the block (16 columns) and
+// feeds 16 MFMAs (one per column offset t = 0..15: column 16c + t).
+// Partials of the 4 wavefronts meet in LDS; partials of the S workgroups of
+// one column block meet in the fp32 workspace, and the last workgroup to
+// arrive (arrival counter) adds them in split order and writes the output.
+//
+// SCALE_IN_TILE: the MFMA operand is the exact dequantised weight.
+// Otherwise the operand is base + q, the product is taken per group, and the
+// group's scale and zero point are applied once per output element:
+//   sum_k a (q - z) s = s * (sum_k a (base + q) - (base + z) sum_k a),
+// with sum_k a from one extra MFMA against a ones operand.
+// ---------------------------------------------------------------------------
+template <typename T, bool HAS_ZP, bool SCALE_IN_TILE, bool ALIGNED>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) {
+  extern __shared__ float red[];
+  __shared__ int last_flag;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  const int b = blockIdx.x % p.NB;
+  const int s = blockIdx.x / p.NB;
+  const int N8 = p.N >> 3;
+  const int word0 = b * (kDecodeCols / 8) + 2 * c;
+  const int col0 = word0 * 8;
+  const bool full = (word0 + 1) < N8;  // both words of this lane exist
+
+  const int step_beg = (s * kDecodeWaves + wave) * p.L;
+  const int step_end = min(step_beg + p.L, p.KS);
+
+  f32x4 acc[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 R[16];
+  f32x4 Rs = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (!SCALE_IN_TILE) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) R[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const u32x4 ones = u32x4{T::kOnePair, T::kOnePair, T::kOnePair, T::kOnePair};
+  const bool a_vec = (p.K & 7) == 0;
+
+  for (int cs = step_beg; cs < step_end; cs += kDecodeChunk) {
+    u32x2 W[kDecodeChunk][8];
+    u32x4 Aop[kDecodeChunk];
+    u32x4 Sv[kDecodeChunk][2];
+    u32x2 Zv[kDecodeChunk];
+    // ---- issue every load of the chunk
+#pragma unroll
+    for (int j = 0; j < kDecodeChunk; ++j) {
+      const int st = cs + j;
+      const bool live = st < step_end;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int row = st * kStepRows + 8 * g + r;
+        u32x2 w = u32x2{0u, 0u};
+        if (live && row < p.K) {
+          const uint32_t* src = p.bq + (int64_t)row * N8 + word0;
+          if (ALIGNED && full) {
+            w = *(const u32x2*)src;
+          } else {
+            if (word0 < N8) w.x = src[0];
+            if (word0 + 1 < N8) w.y = src[1];
+          }
+        }
+        W[j][r] = w;
+      }
+      // activation operand: row c, k = 8g..8g+7 of the step
+      u32x4 av = u32x4{0u, 0u, 0u, 0u};
+      const int k = st * kStepRows + 8 * g;
+      if (live && c < p.M) {
+        const uint16_t* src = p.a + (int64_t)c * p.K + k;
+        if (a_vec && k + 8 <= p.K) {
+          av = *(const u32x4*)src;
+        } else {
+          uint32_t h[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) h[e] = (k + e < p.K) ? (uint32_t)src[e] : 0u;
+          av = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                     h[6] | (h[7] << 16)};
+        }
+      }
+      Aop[j] = av;
+      // this step's group: 16 scales, 2 zero-point words
+      const int grp = min(st, p.KS - 1) / p.SG;
+      const uint16_t* sp = p.sc + (int64_t)grp * p.N + col0;
+      if (ALIGNED && full) {
+        Sv[j][0] = *(const u32x4*)sp;
+        Sv[j][1] = *(const u32x4*)(sp + 8);
+      } else {
+        uint32_t h[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) h[e] = (col0 + e < p.N) ? (uint32_t)sp[e] : 0u;
+        Sv[j][0] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                         h[6] | (h[7] << 16)};
+        Sv[j][1] = u32x4{h[8] | (h[9] << 16), h[10] | (h[11] << 16), h[12] | (h[13] << 16),
+                         h[14] | (h[15] << 16)};
+      }
+      if constexpr (HAS_ZP) {
+        const uint32_t* zp = p.qz + (int64_t)grp * N8 + word0;
+        if (ALIGNED && full) {
+          Zv[j] = *(const u32x2*)zp;
+        } else {
+          Zv[j] = u32x2{word0 < N8 ? zp[0] : 0u, word0 + 1 < N8 ? zp[1] : 0u};
+        }
+      } else {
+        const uint32_t zb = (uint32_t)p.zp_bias * 0x11111111u;
+        Zv[j] = u32x2{zb, zb};
+      }
+    }
+    // ---- compute the chunk
+#pragma unroll
+    for (int j = 0; j < kDecodeChunk; ++j) {
+      const int st = cs + j;
+      if (st >= step_end) break;
+      uint32_t Y[2][2][4];  // [word][half][row pair]
+#pragma unroll
+      for (int w = 0; w < 2; ++w)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            Y[w][h][i] = join_rows(W[j][2 * i][w], W[j][2 * i + 1][w], h);
+      const uint32_t* sv = (const uint32_t*)&Sv[j][0];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int w = t >> 3, h = (t >> 2) & 1;
+        constexpr int dummy = 0;
+        (void)dummy;
+        u32x4 bop;
+        if constexpr (SCALE_IN_TILE) {
+          const uint32_t s_bits = (t & 1) ? (sv[t >> 1] >> 16) : (sv[t >> 1] & 0xFFFFu);
+          const uint32_t z = nib(Zv[j][w], t & 7);
+          switch (t & 3) {
+            case 0: { auto cc = make_col<0>(T{}, s_bits, z);
+              bop = u32x4{exact_pair<0>(T{}, Y[w][h][0], cc), exact_pair<0>(T{}, Y[w][h][1], cc),
+                          exact_pair<0>(T{}, Y[w][h][2], cc), exact_pair<0>(T{}, Y[w][h][3], cc)};
+            } break;
+            case 1: { auto cc = make_col<1>(T{}, s_bits, z);
+              bop = u32x4{exact_pair<1>(T{}, Y[w][h][0], cc), exact_pair<1>(T{}, Y[w][h][1], cc),
+                          exact_pair<1>(T{}, Y[w][h][2], cc), exact_pair<1>(T{}, Y[w][h][3], cc)};
+            } break;
+            case 2: { auto cc = make_col<2>(T{}, s_bits, z);
+              bop = u32x4{exact_pair<2>(T{}, Y[w][h][0], cc), exact_pair<2>(T{}, Y[w][h][1], cc),
+                          exact_pair<2>(T{}, Y[w][h][2], cc), exact_pair<2>(T{}, Y[w][h][3], cc)};
+            } break;
+            default: { auto cc = make_col<3>(T{}, s_bits, z);
+              bop = u32x4{exact_pair<3>(T{}, Y[w][h][0], cc), exact_pair<3>(T{}, Y[w][h][1], cc),
+                          exact_pair<3>(T{}, Y[w][h][2], cc), exact_pair<3>(T{}, Y[w][h][3], cc)};
+            } break;
+          }
+          acc[t] = mfma<T>(Aop[j], bop, acc[t]);
+        } else {
+          switch (t & 3) {
+            case 0: bop = u32x4{magic_pair<T, 0>(Y[w][h][0]), magic_pair<T, 0>(Y[w][h][1]),
+                                magic_pair<T, 0>(Y[w][h][2]), magic_pair<T, 0>(Y[w][h][3])}; break;
+            case 1: bop = u32x4{magic_pair<T, 1>(Y[w][h][0]), magic_pair<T, 1>(Y[w][h][1]),
+                                magic_pair<T, 1>(Y[w][h][2]), magic_pair<T, 1>(Y[w][h][3])}; break;
+            case 2: bop = u32x4{magic_pair<T, 2>(Y[w][h][0]), magic_pair<T, 2>(Y[w][h][1]),
+                                magic_pair<T, 2>(Y[w][h][2]), magic_pair<T, 2>(Y[w][h][3])}; break;
+            default: bop = u32x4{magic_pair<T, 3>(Y[w][h][0]), magic_pair<T, 3>(Y[w][h][1]),
+                                 magic_pair<T, 3>(Y[w][h][2]), magic_pair<T, 3>(Y[w][h][3])}; break;
+          }
+          R[t] = mfma<T>(Aop[j], bop, R[t]);
+        }
+      }
+      if constexpr (!SCALE_IN_TILE) {
+        Rs = mfma<T>(Aop[j], ones, Rs);
+        const bool group_end = ((st + 1) % p.SG == 0) || (st + 1 == step_end);
+        if (group_end) {
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            const int w = t >> 3;
+            const bool odd16 = (T::kBase == 1024.0f) && (t & 1);
+            const uint32_t s_bits = (t & 1) ? (sv[t >> 1] >> 16) : (sv[t >> 1] & 0xFFFFu);
+            const float z = (float)nib(Zv[j][w], t & 7);
+            const float sc = widen(T{}, s_bits) * (odd16 ? 0.0625f : 1.0f);
+            const float bias = T::kBase + z * (odd16 ? 16.0f : 1.0f);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              acc[t][v] = __builtin_fmaf(sc, __builtin_fmaf(-bias, Rs[v], R[t][v]), acc[t][v]);
+            }
+            R[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+          Rs = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+  }
+
+  // ---- the 4 wavefronts' partials meet in LDS: red[wave][m][256]
+  const int M = p.M;
+#pragma unroll
+  for (int t = 0; t < 16; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 4 * g + v;
+      if (m < M) red[(wave * M + m) * kDecodeCols + 16 * c + t] = acc[t][v];
+    }
+  __syncthreads();
+
+  const int col = b * kDecodeCols + tid;
+  const bool col_ok = col < p.N;
+  if (p.S == 1) {
+    if (col_ok) {
+      for (int m = 0; m < M; ++m) {
+        float v = red[m * kDecodeCols + tid];
+#pragma unroll
+        for (int w = 1; w < kDecodeWaves; ++w) v += red[(w * M + m) * kDecodeCols + tid];
+        p.out[(int64_t)m * p.N + col] = narrow(T{}, v);
+      }
+    }
+    return;
+  }
+  if (col_ok) {
+    for (int m = 0; m < M; ++m) {
+      float v = red[m * kDecodeCols + tid];
+#pragma unroll
+      for (int w = 1; w < kDecodeWaves; ++w) v += red[(w * M + m) * kDecodeCols + tid];
+      p.ws[((int64_t)s * M + m) * p.N + col] = v;
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = atomicAdd(&p.counters[b], 1);
+    last_flag = (prev == p.S - 1);
+  }
+  __syncthreads();
+  if (!last_flag) return;
+  __threadfence();
+  if (col_ok) {
+    for (int m = 0; m < M; ++m) {
+      float v = 0.f;
+      for (int q = 0; q < p.S; ++q) {
+        v += __builtin_nontemporal_load(&p.ws[((int64_t)q * M + m) * p.N + col]);
+      }
+      p.out[(int64_t)m * p.N + col] = narrow(T{}, v);
+    }
+  }
+  if (tid == 0) atomicExch(&p.counters[b], 0);
+}
+
+// ---------------------------------------------------------------------------
+// Prefill: workgroup tile BM x 256, K staged 64 rows at a time. The A tile
+// goes through LDS (double-buffered) and is read by all 4 wavefronts; each
+// wavefront owns 64 output columns and dequantises exactly the weights it
+// multiplies, straight into MFMA operands: lane (g, c) reads, per 32-row
+// step, rows 8g..8g+7 of columns 4c..4c+3 of its 64 (one 16-bit piece of a
+// packed word per row) and forms four operands (column 4c + t, t = 0..3).
+// Workgroup ids are spread so that the tiles of one XCD share A rows.
+// ---------------------------------------------------------------------------
+template <typename T, bool HAS_ZP, int BM>
+__global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams p) {
+  constexpr int RH = kPrefillLdsRowHalves;
+  constexpr int MB = BM / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * RH];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int c = lane & 15;
+
+  const int xcd = blockIdx.x % kXcds;
+  const int tile = xcd * p.per_xcd + blockIdx.x / kXcds;
+  if (tile >= p.tiles_m * p.tiles_n) return;
+  const int tm = tile / p.tiles_n;
+  const int tn = tile % p.tiles_n;
+  const int m0 = tm * BM;
+  const int ncol = tn * kPrefillBN + wave * 64 + 4 * c;  // this lane's 4 columns
+  const bool ncol_ok = ncol < p.N;
+  const int N4 = p.N >> 2;  // 16-bit pieces per weight row
+  const uint16_t* bq16 = (const uint16_t*)p.bq;
+  const uint16_t* qz16 = (const uint16_t*)p.qz;
+  const int KT = (p.K + kPrefillBK - 1) / kPrefillBK;
+  const bool a_vec = (p.K & 7) == 0;
+
+  f32x4 acc[MB][4];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- loaders
+  auto load_a = [&](int kt, u32x4 (&ar)[BM / 32]) {
+#pragma unroll
+    for (int j = 0; j < BM / 32; ++j) {
+      const int row = j * 32 + (tid >> 3);
+      const int k = kt * kPrefillBK + (tid & 7) * 8;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (m0 + row < p.M) {
+        const uint16_t* src = p.a + (int64_t)(m0 + row) * p.K + k;
+        if (a_vec && k + 8 <= p.K) {
+          v = *(const u32x4*)src;
+        } else {
+          uint32_t h[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) h[e] = (k + e < p.K) ? (uint32_t)src[e] : 0u;
+          v = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                    h[6] | (h[7] << 16)};
+        }
+      }
+      ar[j] = v;
+    }
+  };
+  auto store_a = [&](int buf, const u32x4 (&ar)[BM / 32]) {
+#pragma unroll
+    for (int j = 0; j < BM / 32; ++j) {
+      const int row = j * 32 + (tid >> 3);
+      *(u32x4*)&As[buf][row * RH + (tid & 7) * 8] = ar[j];
+    }
+  };
+  // weights of one 32-row step: 8 rows x 16 bits, plus 4 scales and 4 zeros
+  struct BStep {
+    uint32_t q[8];
+    u32x2 s;
+    uint32_t z;
+  };
+  auto load_b = [&](int k0, BStep& bs) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int row = k0 + 8 * g + r;
+      bs.q[r] = (row < p.K && ncol_ok) ? (uint32_t)bq16[(int64_t)row * N4 + (ncol >> 2)] : 0u;
+    }
+    const int grp = min(k0, p.K - 1) / p.G;
+    bs.s = ncol_ok ? *(const u32x2*)(p.sc + (int64_t)grp * p.N + ncol) : u32x2{0u, 0u};
+    if constexpr (HAS_ZP) {
+      bs.z = ncol_ok ? (uint32_t)qz16[(int64_t)grp * N4 + (ncol >> 2)] : 0u;
+    } else {
+      bs.z = (uint32_t)p.zp_bias * 0x1111u;
+    }
+  };
+
+  u32x4 a_next[BM / 32];
+  BStep b_cur[2], b_next[2];
+  load_a(0, a_next);
+  load_b(0, b_cur[0]);
+  load_b(32, b_cur[1]);
+  store_a(0, a_next);
+  __syncthreads();
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    const bool more = kt + 1 < KT;
+    if (more) {
+      load_a(kt + 1, a_next);
+      load_b((kt + 1) * kPrefillBK, b_next[0]);
+      load_b((kt + 1) * kPrefillBK + 32, b_next[1]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const BStep& bs = b_cur[ks];
+      uint32_t Y[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Y[i] = bs.q[2 * i] | (bs.q[2 * i + 1] << 16);
+      u32x4 bop[4];
+      {
+        auto c0 = make_col<0>(T{}, bs.s.x & 0xFFFFu, nib(bs.z, 0));
+        auto c1 = make_col<1>(T{}, bs.s.x >> 16, nib(bs.z, 1));
+        auto c2 = make_col<2>(T{}, bs.s.y & 0xFFFFu, nib(bs.z, 2));
+        auto c3 = make_col<3>(T{}, bs.s.y >> 16, nib(bs.z, 3));
+        bop[0] = u32x4{exact_pair<0>(T{}, Y[0], c0), exact_pair<0>(T{}, Y[1], c0),
+                       exact_pair<0>(T{}, Y[2], c0), exact_pair<0>(T{}, Y[3], c0)};
+        bop[1] = u32x4{exact_pair<1>(T{}, Y[0], c1), exact_pair<1>(T{}, Y[1], c1),
+                       exact_pair<1>(T{}, Y[2], c1), exact_pair<1>(T{}, Y[3], c1)};
+        bop[2] = u32x4{exact_pair<2>(T{}, Y[0], c2), exact_pair<2>(T{}, Y[1], c2),
+                       exact_pair<2>(T{}, Y[2], c2), exact_pair<2>(T{}, Y[3], c2)};
+        bop[3] = u32x4{exact_pair<3>(T{}, Y[0], c3), exact_pair<3>(T{}, Y[1], c3),
+                       exact_pair<3>(T{}, Y[2], c3), exact_pair<3>(T{}, Y[3], c3)};
+      }
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const u32x4 aop = *(const u32x4*)&As[buf][(i * 16 + c) * RH + ks * 32 + 8 * g];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[i][t] = mfma<T>(aop, bop[t], acc[i][t]);
+      }
+    }
+    if (more) {
+      store_a(buf ^ 1, a_next);
+      b_cur[0] = b_next[0];
+      b_cur[1] = b_next[1];
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds rows i*16 + 4g + v, columns ncol + t
+  if (!ncol_ok) return;
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = m0 + i * 16 + 4 * g + v;
+      if (row < p.M) {
+        const uint32_t lo = (uint32_t)narrow(T{}, acc[i][0][v]) |
+                            ((uint32_t)narrow(T{}, acc[i][1][v]) << 16);
+        const uint32_t hi = (uint32_t)narrow(T{}, acc[i][2][v]) |
+                            ((uint32_t)narrow(T{}, acc[i][3][v]) << 16);
+        *(u32x2*)(p.out + (int64_t)row * p.N + ncol) = u32x2{lo, hi};
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dequant probe: w[k, n] = RNE((q - z) * s), written densely. Thread owns
+// rows 2i, 2i+1 of one packed word (8 columns) and uses the same pair
+// routine as the prefill operands.
+// ---------------------------------------------------------------------------
+template <typename T, bool HAS_ZP>
+__global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
+  const int N8 = p.N >> 3;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t pairs = ((int64_t)p.K + 1) / 2;
+  if (idx >= pairs * N8) return;
+  const int wc = (int)(idx % N8);
+  const int r0 = (int)(idx / N8) * 2;
+  const bool has1 = r0 + 1 < p.K;
+  const uint32_t w0 = p.bq[(int64_t)r0 * N8 + wc];
+  const uint32_t w1 = has1 ? p.bq[(int64_t)(r0 + 1) * N8 + wc] : 0u;
+  const int grp = r0 / p.G;  // rows r0, r0 + 1 share a group: G is even or G == K
+  const uint32_t zw = HAS_ZP ? p.qz[(int64_t)grp * N8 + wc] : (uint32_t)p.zp_bias * 0x11111111u;
+  const uint16_t* sp = p.sc + (int64_t)grp * p.N + wc * 8;
+  uint16_t* o0 = p.w + (int64_t)r0 * p.N + wc * 8;
+  uint16_t* o1 = o0 + p.N;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t y = join_rows(w0, w1, h);
+    uint32_t pr[4];
+    pr[0] = exact_pair<0>(T{}, y, make_col<0>(T{}, sp[4 * h + 0], nib(zw, 4 * h + 0)));
+    pr[1] = exact_pair<1>(T{}, y, make_col<1>(T{}, sp[4 * h + 1], nib(zw, 4 * h + 1)));
+    pr[2] = exact_pair<2>(T{}, y, make_col<2>(T{}, sp[4 * h + 2], nib(zw, 4 * h + 2)));
+    pr[3] = exact_pair<3>(T{}, y, make_col<3>(T{}, sp[4 * h + 3], nib(zw, 4 * h + 3)));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o0[4 * h + e] = (uint16_t)(pr[e] & 0xFFFFu);
+      if (has1) o1[4 * h + e] = (uint16_t)(pr[e] >> 16);
+    }
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <typename T, bool Z, bool SIT, bool AL>
+static hipError_t decode_go(const DecodeParams& p, int grid, int lds, hipStream_t st) {
+  hipLaunchKernelGGL((decode_kernel<T, Z, SIT, AL>), dim3(grid), dim3(kDecodeThreads),
+                     lds, st, p);
+  return hipGetLastError();
+}
+template <typename T, bool Z, bool SIT>
+static hipError_t decode_al(const DecodeParams& p, int grid, int lds, hipStream_t st) {
+  if ((p.N & 15) == 0) return decode_go<T, Z, SIT, true>(p, grid, lds, st);
+  return decode_go<T, Z, SIT, false>(p, grid, lds, st);
+}
+template <typename T, bool Z>
+static hipError_t decode_sit(const DecodeParams& p, bool sit, int grid, int lds, hipStream_t st) {
+  return sit ? decode_al<T, Z, true>(p, grid, lds, st) : decode_al<T, Z, false>(p, grid, lds, st);
+}
+hipError_t launch_decode(const DecodeParams& p, int dtype, bool has_zp, bool sit, int grid,
+                         int lds, hipStream_t st) {
+  if (dtype == W4A16_F16)
+    return has_zp ? decode_sit<F16, true>(p, sit, grid, lds, st)
+                  : decode_sit<F16, false>(p, sit, grid, lds, st);
+  return has_zp ? decode_sit<BF16, true>(p, sit, grid, lds, st)
+                : decode_sit<BF16, false>(p, sit, grid, lds, st);
+}
+
+template <typename T, bool Z, int BM>
+static hipError_t prefill_go(const PrefillParams& p, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((prefill_kernel<T, Z, BM>), dim3(grid), dim3(kPrefillThreads), 0, st, p);
+  return hipGetLastError();
+}
+template <typename T, bool Z>
+static hipError_t prefill_bm(const PrefillParams& p, int bm, int grid, hipStream_t st) {
+  switch (bm) {
+    case 256: return prefill_go<T, Z, 256>(p, grid, st);
+    case 128: return prefill_go<T, Z, 128>(p, grid, st);
+    case 64: return prefill_go<T, Z, 64>(p, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+hipError_t launch_prefill(const PrefillParams& p, int dtype, bool has_zp, int bm, int grid,
+                          hipStream_t st) {
+  if (dtype == W4A16_F16)
+    return has_zp ? prefill_bm<F16, true>(p, bm, grid, st) : prefill_bm<F16, false>(p, bm, grid, st);
+  return has_zp ? prefill_bm<BF16, true>(p, bm, grid, st) : prefill_bm<BF16, false>(p, bm, grid, st);
+}
+
+template <typename T, bool Z>
+static hipError_t dequant_go(const DequantParams& p, hipStream_t st) {
+  const int64_t work = (((int64_t)p.K + 1) / 2) * (p.N >> 3);
+  const int64_t grid = (work + 255) / 256;
+  hipLaunchKernelGGL((dequant_kernel<T, Z>), dim3((unsigned)grid), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+hipError_t launch_dequant(const DequantParams& p, int dtype, bool has_zp, hipStream_t st) {
+  if (dtype == W4A16_F16) return has_zp ? dequant_go<F16, true>(p, st) : dequant_go<F16, false>(p, st);
+  return has_zp ? dequant_go<BF16, true>(p, st) : dequant_go<BF16, false>(p, st);
+}
+
+}  // namespace w4a16

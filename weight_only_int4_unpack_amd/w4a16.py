@@ -1,0 +1,221 @@
+"""ctypes binding of ``libw4a16.so`` (include/w4a16.h).
+
+Argument marshalling only: shapes are read off the tensors, checked against
+each other, and passed with raw pointers and the current HIP stream. Every
+step of the computation runs in the library's kernels. There is no fallback:
+if the library is missing or the device is not gfx950, calls raise.
+
+The Python signature mirrors the facade of PR #51453 "Register the Triton
+W4A16 GEMM as a custom op" (Code section): ``gemm(a, b_q, scales, qzeros,
+group_size, zp_bias=8)`` returning ``[M, 8 * b_q.shape[1]]`` in ``a``'s dtype.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libw4a16.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "w4a16.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_GROUP, ERR_DTYPE, ERR_ZP, ERR_ALIGN, ERR_DEVICE, \
+    ERR_HIP, ERR_VALUE, ERR_PLAN = range(11)
+STATUS_NAMES = ["OK", "NULL", "SHAPE", "GROUP", "DTYPE", "ZP", "ALIGN", "DEVICE",
+                "HIP", "VALUE", "PLAN"]
+F16, BF16 = 0, 1
+ROUTE_NONE, ROUTE_DECODE, ROUTE_PREFILL = 0, 1, 2
+
+_DTYPE_CODE = {torch.float16: F16, torch.bfloat16: BF16}
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("route", ctypes.c_int32), ("block_m", ctypes.c_int32),
+                ("block_n", ctypes.c_int32), ("block_k", ctypes.c_int32),
+                ("scale_in_tile", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("steps_per_wave", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__(f"w4a16 error {name}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m weight_only_int4_unpack_amd.build` (there is no fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.w4a16_gemm.argtypes = [vp, vp, vp, vp, i32, i32, vp, i64, i64, i64, i32, vp]
+    L.w4a16_gemm_planned.argtypes = [vp, vp, vp, vp, i32, i32, vp, i64, i64, i64, i32,
+                                     ctypes.POINTER(Plan), vp]
+    L.w4a16_plan.argtypes = [i64, i64, i64, i32, i32, i32, i32, ctypes.POINTER(Plan)]
+    L.w4a16_plan_route.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, i32, i32,
+                                   ctypes.POINTER(Plan)]
+    L.w4a16_dequant.argtypes = [vp, vp, vp, i32, i32, vp, i64, i64, i32, vp]
+    L.w4a16_pack_int4.argtypes = [vp, i64, i64, vp]
+    L.w4a16_unpack_int4.argtypes = [vp, i64, i64, vp]
+    for f in ("w4a16_gemm", "w4a16_gemm_planned", "w4a16_plan", "w4a16_plan_route",
+              "w4a16_dequant", "w4a16_pack_int4", "w4a16_unpack_int4"):
+        getattr(L, f).restype = ctypes.c_int
+    L.w4a16_last_error.restype = ctypes.c_char_p
+    L.w4a16_last_error.argtypes = []
+    L.w4a16_version.restype = ctypes.c_char_p
+    L.w4a16_version.argtypes = []
+    _lib = L
+    return L
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/w4a16.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:w4a16_status|const char\*)\s+(w4a16_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def last_error() -> str:
+    return lib().w4a16_last_error().decode()
+
+
+def _check(status: int):
+    if status != OK:
+        raise W4A16Error(status, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _shapes(a, b_q, scales, qzeros, group_size):
+    if a.dim() != 2 or b_q.dim() != 2 or scales.dim() != 2:
+        raise ValueError("a, b_q and scales must be 2-D")
+    if a.dtype not in _DTYPE_CODE:
+        raise ValueError("only float16/bfloat16 activations are supported")
+    if scales.dtype != a.dtype:
+        raise ValueError("scales must have the activations' dtype")
+    if b_q.dtype != torch.int32 or (qzeros is not None and qzeros.dtype != torch.int32):
+        raise ValueError("b_q and qzeros must be int32")
+    M, K = a.shape
+    N = b_q.shape[1] * 8
+    if b_q.shape[0] != K:
+        raise ValueError(f"b_q has {b_q.shape[0]} rows, a has K={K} columns")
+    if group_size <= 0 or K % group_size != 0:
+        raise ValueError(f"K={K} is not a multiple of group size {group_size}")
+    if tuple(scales.shape) != (K // group_size, N):
+        raise ValueError(f"scales must be [{K // group_size}, {N}], got {list(scales.shape)}")
+    if qzeros is not None and tuple(qzeros.shape) != (K // group_size, N // 8):
+        raise ValueError(f"qzeros must be [{K // group_size}, {N // 8}], got {list(qzeros.shape)}")
+    for t in (a, b_q, scales, qzeros):
+        if t is not None:
+            if not t.is_cuda or t.device != a.device:
+                raise ValueError("all tensors must be on the same GPU")
+            if not t.is_contiguous():
+                raise ValueError("all tensors must be contiguous")
+    return M, K, N
+
+
+def gemm(a: torch.Tensor, b_q: torch.Tensor, scales: torch.Tensor,
+         qzeros: torch.Tensor | None = None, group_size: int = 128, zp_bias: int = 8,
+         out: torch.Tensor | None = None, plan: Plan | None = None) -> torch.Tensor:
+    """``a @ dequant(b_q, scales, qzeros)`` on the GPU, in ``a``'s dtype."""
+    M, K, N = _shapes(a, b_q, scales, qzeros, group_size)
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    elif (tuple(out.shape) != (M, N) or out.dtype != a.dtype or out.device != a.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous [M, N] tensor like a")
+    L = lib()
+    with torch.cuda.device(a.device):
+        args = (_ptr(a), _ptr(b_q), _ptr(scales), _ptr(qzeros), group_size, zp_bias,
+                _ptr(out), M, K, N, _DTYPE_CODE[a.dtype])
+        if plan is None:
+            _check(L.w4a16_gemm(*args, _stream(a.device)))
+        else:
+            _check(L.w4a16_gemm_planned(*args, ctypes.byref(plan), _stream(a.device)))
+    return out
+
+
+def dequant(b_q: torch.Tensor, scales: torch.Tensor, qzeros: torch.Tensor | None = None,
+            group_size: int = 128, zp_bias: int = 8,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """Dense ``[K, N]`` RNE((q - z) * s) in ``scales``' dtype (test probe)."""
+    K, N = b_q.shape[0], b_q.shape[1] * 8
+    dummy = torch.empty((0, K), dtype=scales.dtype, device=scales.device)
+    _shapes(dummy, b_q, scales, qzeros, group_size)
+    if out is None:
+        out = torch.empty((K, N), dtype=scales.dtype, device=scales.device)
+    L = lib()
+    with torch.cuda.device(scales.device):
+        _check(L.w4a16_dequant(_ptr(b_q), _ptr(scales), _ptr(qzeros), group_size, zp_bias,
+                               _ptr(out), K, N, _DTYPE_CODE[scales.dtype],
+                               _stream(scales.device)))
+    return out
+
+
+def plan(M: int, K: int, N: int, group_size: int, has_zp: bool, dtype, num_cus: int = 256,
+         route: int | None = None, splits: int = 0, scale_in_tile: int = -1) -> Plan:
+    """The launch the selector picks (or the forced route), host only."""
+    code = _DTYPE_CODE.get(dtype, dtype)
+    p = Plan()
+    L = lib()
+    if route is None and splits == 0 and scale_in_tile < 0:
+        _check(L.w4a16_plan(M, K, N, group_size, int(has_zp), code, num_cus, ctypes.byref(p)))
+    else:
+        r = route if route is not None else (ROUTE_DECODE if M <= 16 else ROUTE_PREFILL)
+        _check(L.w4a16_plan_route(M, K, N, group_size, int(has_zp), code, num_cus, r,
+                                  splits, scale_in_tile, ctypes.byref(p)))
+    return p
+
+
+def pack_int4(q) -> np.ndarray:
+    """Host pack: uint8 ``[R, C]`` values 0..15 -> int32 ``[R, C/8]``."""
+    if isinstance(q, torch.Tensor):
+        q = q.cpu().numpy()
+    q = np.asarray(q)
+    if q.dtype != np.uint8 and q.size and (q.min() < 0 or q.max() > 255):
+        raise W4A16Error(ERR_VALUE, "uint4 values must lie in 0..15")
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    if q.ndim != 2:
+        raise ValueError("q must be 2-D")
+    out = np.empty((q.shape[0], q.shape[1] // 8), dtype=np.int32)
+    _check(lib().w4a16_pack_int4(q.ctypes.data_as(ctypes.c_void_p), q.shape[0], q.shape[1],
+                                 out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def unpack_int4(packed) -> np.ndarray:
+    """Host unpack: int32 ``[R, W]`` -> uint8 ``[R, 8W]``."""
+    if isinstance(packed, torch.Tensor):
+        packed = packed.cpu().numpy()
+    packed = np.ascontiguousarray(packed, dtype=np.int32)
+    out = np.empty((packed.shape[0], packed.shape[1] * 8), dtype=np.uint8)
+    _check(lib().w4a16_unpack_int4(packed.ctypes.data_as(ctypes.c_void_p), packed.shape[0],
+                                   packed.shape[1] * 8, out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def version() -> str:
+    return lib().w4a16_version().decode()
