@@ -74,10 +74,12 @@ typedef struct {
   int32_t block_m;          /* rows of A per workgroup tile (decode: 16) */
   int32_t block_n;          /* output columns per workgroup */
   int32_t block_k;          /* K rows per pipeline step */
-  int32_t scale_in_tile;    /* decode: 1 = scale folded into each weight,
-                               0 = applied once per group to the partial sum */
+  int32_t decode_mode;      /* decode: 0 = scale folded into each weight;
+                               1 = scale applied once per group, one group per
+                               wavefront; 2 = as 1, several groups per
+                               wavefront */
   int32_t splits;           /* decode: K splits across workgroups */
-  int32_t steps_per_wave;   /* decode: 32-row K steps per wavefront */
+  int32_t steps_per_wave;   /* decode: 32-row K steps per wavefront (1, 2, 4) */
   int32_t grid;             /* workgroups launched */
   int32_t threads;          /* threads per workgroup */
   int32_t lds_bytes;        /* LDS per workgroup */
@@ -122,14 +124,16 @@ w4a16_status w4a16_plan(int64_t M, int64_t K, int64_t N, int32_t group_size,
 
 /*
  * w4a16_plan_route - as w4a16_plan with the route forced
- * (W4A16_ROUTE_DECODE needs 1 <= M <= 16) and, for decode, the K split
- * and scale placement forced when `splits` > 0 / `scale_in_tile` >= 0.
+ * (W4A16_ROUTE_DECODE needs 1 <= M <= 16) and, for decode, the steps per
+ * wavefront (1, 2 or 4; 0 = selector's choice) and the decode mode
+ * (0, 1, 2; -1 = selector's choice; mode 1 needs every wavefront's steps
+ * inside one group) forced.
  * Errors: those of w4a16_plan, and PLAN.
  */
 w4a16_status w4a16_plan_route(int64_t M, int64_t K, int64_t N,
                               int32_t group_size, int32_t has_zp,
                               int32_t dtype, int32_t num_cus, int32_t route,
-                              int32_t splits, int32_t scale_in_tile,
+                              int32_t steps_per_wave, int32_t decode_mode,
                               w4a16_plan_t* plan);
 
 /*

@@ -136,15 +136,22 @@ def test_selector_decode_shapes():
     p = W.plan(1, 5120, 17408, 128, False, torch.bfloat16)
     nb = 17408 // 256
     assert p.block_n == 256 and p.grid == nb * p.splits
+    assert p.steps_per_wave in (1, 2, 4)
     assert p.splits * 4 * p.steps_per_wave >= 5120 // 32
     assert (p.splits - 1) * 4 * p.steps_per_wave < 5120 // 32        # no empty split
-    assert p.scale_in_tile == 0
-    # K = 2112 is 66 steps of 32 rows
+    assert p.decode_mode == 1                        # one group of 4 steps per wavefront
+    assert (128 // 32) % p.steps_per_wave == 0
+    # K = 2112 is 66 steps of 32 rows; fp16 with groups of 64 folds the scale
     p = W.plan(8, 2112, 5120, 64, True, torch.float16)
     assert p.splits * 4 * p.steps_per_wave >= 66
-    assert p.scale_in_tile == 1
+    assert p.decode_mode == 0
     assert p.workspace_bytes >= p.splits * 8 * 5120 * 4 or p.splits == 1
     assert p.lds_bytes == 4 * 8 * 256 * 4
+    # bf16 with groups of 32 cannot keep 2 or 4 steps in one group
+    p = W.plan(4, 4096, 4096, 32, True, torch.bfloat16, route=W.ROUTE_DECODE, steps_per_wave=4)
+    assert p.decode_mode == 2
+    # per-channel: one group spans every step
+    assert W.plan(16, 4096, 4096, 4096, True, torch.float16).decode_mode == 1
 
 
 def test_selector_prefill_tiles():
@@ -161,10 +168,19 @@ def test_forced_routes_and_errors():
     with pytest.raises(W.W4A16Error) as e:
         W.plan(17, 4096, 4096, 32, True, torch.float16, route=W.ROUTE_DECODE)
     assert e.value.status == W.ERR_PLAN
-    p = W.plan(4, 4096, 4096, 32, True, torch.float16, route=W.ROUTE_DECODE, splits=1)
-    assert p.splits == 1 and p.workspace_bytes == 0
-    p = W.plan(4, 4096, 4096, 32, True, torch.float16, route=W.ROUTE_DECODE, scale_in_tile=0)
-    assert p.scale_in_tile == 0
+    p = W.plan(4, 4096, 4096, 32, True, torch.float16, route=W.ROUTE_DECODE, steps_per_wave=1)
+    assert p.steps_per_wave == 1 and p.splits == 4096 // 32 // 4
+    p = W.plan(4, 4096, 4096, 32, True, torch.float16, route=W.ROUTE_DECODE, decode_mode=2)
+    assert p.decode_mode == 2
+    for bad in (dict(steps_per_wave=3), dict(decode_mode=3),
+                dict(steps_per_wave=4, decode_mode=1)):       # 4 steps straddle groups of 1
+        with pytest.raises(W.W4A16Error) as e:
+            W.plan(4, 4096, 4096, 32, True, torch.float16, route=W.ROUTE_DECODE, **bad)
+        assert e.value.status == W.ERR_PLAN
+    # shapes off the fast layout run one step per wavefront
+    assert W.plan(4, 2120, 520, 2120, True, torch.float16).steps_per_wave == 1
+    with pytest.raises(W.W4A16Error):
+        W.plan(4, 2120, 520, 2120, True, torch.float16, route=W.ROUTE_DECODE, steps_per_wave=2)
 
 
 def test_planned_call_rejects_mismatched_plan():

@@ -25,18 +25,22 @@ pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def _plan(p, route, splits=0, sit=-1):
+def _plan(p, route, L=0, mode=-1):
     return W.plan(p.M, p.K, p.N, p.G, p.qz is not None, TORCH_DT[p.dtype], route=route,
-                  splits=splits, scale_in_tile=sit)
+                  steps_per_wave=L, decode_mode=mode)
 
 
 def _routes(M):
-    """(label, plan factory) pairs that apply to a problem with M rows."""
+    """(label, plan factory) pairs that apply to a problem with M rows: the
+    selector's choice, the prefill kernel, and every decode mode."""
     out = [("auto", lambda p: None), ("prefill", lambda p: _plan(p, W.ROUTE_PREFILL))]
     if 1 <= M <= 16:
-        out += [("decode_sit0", lambda p: _plan(p, W.ROUTE_DECODE, sit=0)),
-                ("decode_sit1", lambda p: _plan(p, W.ROUTE_DECODE, sit=1)),
-                ("decode_s1", lambda p: _plan(p, W.ROUTE_DECODE, splits=1))]
+        def big(p):   # the fast layout takes 1, 2 or 4 steps per wavefront
+            return 4 if (p.N % 16 == 0 and p.K % 8 == 0) else 1
+        out += [("decode_sit", lambda p: _plan(p, W.ROUTE_DECODE, L=big(p), mode=0)),
+                ("decode_multi", lambda p: _plan(p, W.ROUTE_DECODE, L=big(p), mode=2)),
+                ("decode_onegroup", lambda p: _plan(p, W.ROUTE_DECODE, L=1, mode=1)),
+                ("decode_L2", lambda p: _plan(p, W.ROUTE_DECODE, L=min(2, big(p))))]
     return out
 
 
@@ -191,8 +195,15 @@ def test_q_equals_z_gives_zero(dtype, zp):
          "z": z}
     p = make_problem(d, M, K, N, G, dtype)
     for label, mk in _routes(M):
-        got = O.to_f32(dev_to_bits(p.gpu_gemm(plan=mk(p))), dtype)
-        assert np.all(got == 0.0), label
+        pl = mk(p)
+        got = O.to_f32(dev_to_bits(p.gpu_gemm(plan=pl)), dtype)
+        eff = pl if pl is not None else W.plan(M, K, N, G, zp, TORCH_DT[dtype])
+        if eff.route == W.ROUTE_DECODE and eff.decode_mode != 0:
+            # s * (sum a (base + q) - (base + z) sum a): the two fp32 sums
+            # cancel up to their rounding, not to an exact zero
+            assert np.all(np.abs(got) <= 2.0 ** -12), label
+        else:
+            assert np.all(got == 0.0), label
 
 
 @pytest.mark.parametrize("M", [5, 100])

@@ -80,39 +80,63 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ---------------------------------------------------------------------------
 // selector
 // ---------------------------------------------------------------------------
-void plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype, int num_cus,
-                 int32_t splits, int32_t sit, w4a16_plan_t* pl) {
+// Decode launch: 256 columns per workgroup, 4 wavefronts of L steps each.
+// L is the largest of 4, 2, 1 that still gives at least two workgroups per
+// CU (more bytes in flight per wavefront when the grid is large enough,
+// more wavefronts when it is not). Mode: fp16 with groups of 32 or 64 folds
+// the scale into each weight (cheap packed fp16 ops); otherwise the scale is
+// applied per group to the fp32 partial, with one group per wavefront when
+// the wavefront's steps cannot straddle a group boundary.
+w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype, int num_cus,
+                         int32_t L_forced, int32_t mode_forced, w4a16_plan_t* pl) {
   using namespace w4a16;
   const int64_t KS = ceil_div(K, kStepRows);
   const int64_t NB = ceil_div(N, kDecodeCols);
-  // Aim at about 8 wavefronts per CU (two per SIMD), each holding at least
-  // one 32-row step.
-  int64_t S = splits;
-  if (S <= 0) {
-    const int64_t target_waves = 8 * (int64_t)num_cus;
-    const int64_t per_wg = kDecodeWaves;
-    S = std::max<int64_t>(1, (target_waves + NB * per_wg - 1) / (NB * per_wg));
+  const int64_t SG = ((int64_t)G == K) ? KS : G / kStepRows;
+  const bool one_group = ((int64_t)G == K);
+  // shapes off the fast layout (N % 16 or K % 8 nonzero) use one step per
+  // wavefront
+  const bool aligned = (N % 16 == 0) && (K % 8 == 0);
+  int64_t L = L_forced;
+  if (!aligned && L > 1)
+    return fail(W4A16_ERR_PLAN, "N %% 16 or K %% 8 nonzero: decode runs one step per wavefront");
+  if (L == 0 && !aligned) L = 1;
+  if (L == 0) {
+    L = 1;
+    for (int64_t cand : {4, 2}) {
+      if (NB * ceil_div(KS, kDecodeWaves * cand) >= 2 * (int64_t)num_cus) {
+        L = cand;
+        break;
+      }
+    }
   }
-  S = std::min<int64_t>(S, ceil_div(KS, kDecodeWaves));
-  S = std::max<int64_t>(S, 1);
-  int64_t L = ceil_div(KS, S * kDecodeWaves);
-  S = ceil_div(KS, L * kDecodeWaves);  // drop empty splits
-  // Scale placement: folding the scale into each weight costs a fixed amount
-  // per weight; applying it per group costs per (group, output) pair. fp16
-  // small groups favour the first, everything else the second.
-  int32_t scale_in_tile = sit;
-  if (scale_in_tile < 0) scale_in_tile = (dtype == W4A16_F16 && G <= 64 && G != K) ? 1 : 0;
+  if (L != 1 && L != 2 && L != 4)
+    return fail(W4A16_ERR_PLAN, "steps per wavefront must be 1, 2 or 4 (got %lld)", (long long)L);
+  int32_t mode = mode_forced;
+  const bool fits_one = one_group || SG % L == 0;
+  if (mode < 0) {
+    if (dtype == W4A16_F16 && G <= 64 && !one_group)
+      mode = 0;
+    else
+      mode = fits_one ? 1 : 2;
+  }
+  if (mode < 0 || mode > 2) return fail(W4A16_ERR_PLAN, "decode mode must be 0, 1 or 2");
+  if (mode == 1 && !fits_one)
+    return fail(W4A16_ERR_PLAN, "decode mode 1 needs the %lld steps of a wavefront inside one group",
+                (long long)L);
+  const int64_t S = ceil_div(KS, kDecodeWaves * L);
   pl->route = W4A16_ROUTE_DECODE;
   pl->block_m = kDecodeMaxM;
   pl->block_n = kDecodeCols;
   pl->block_k = kStepRows;
-  pl->scale_in_tile = scale_in_tile;
+  pl->decode_mode = mode;
   pl->splits = (int32_t)S;
   pl->steps_per_wave = (int32_t)L;
   pl->grid = (int32_t)(NB * S);
   pl->threads = kDecodeThreads;
   pl->lds_bytes = decode_lds_bytes((int)M);
-  pl->workspace_bytes = S > 1 ? (int64_t)(S * M * N * 4 + NB * 4 + 256) : 0;
+  pl->workspace_bytes = S > 1 ? (int64_t)(S * M * N * 4 + NB * 4) : 0;
+  return W4A16_OK;
 }
 
 void plan_prefill(int64_t M, int64_t N, w4a16_plan_t* pl) {
@@ -128,7 +152,7 @@ void plan_prefill(int64_t M, int64_t N, w4a16_plan_t* pl) {
   pl->block_m = bm;
   pl->block_n = kPrefillBN;
   pl->block_k = kPrefillBK;
-  pl->scale_in_tile = 1;
+  pl->decode_mode = 0;
   pl->splits = 1;
   pl->steps_per_wave = 0;
   pl->grid = (int32_t)(per_xcd * kXcds);
@@ -138,7 +162,7 @@ void plan_prefill(int64_t M, int64_t N, w4a16_plan_t* pl) {
 }
 
 w4a16_status make_plan(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype, int32_t num_cus,
-                       int32_t route, int32_t splits, int32_t sit, w4a16_plan_t* pl) {
+                       int32_t route, int32_t L, int32_t mode, w4a16_plan_t* pl) {
   if (!pl) return fail(W4A16_ERR_NULL, "plan must be non-NULL");
   w4a16_status st = check_shape(M, K, N, G, dtype);
   if (st != W4A16_OK) return st;
@@ -153,7 +177,8 @@ w4a16_status make_plan(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype
     if (M > w4a16::kDecodeMaxM)
       return fail(W4A16_ERR_PLAN, "decode route needs M <= %d (got %lld)", w4a16::kDecodeMaxM,
                   (long long)M);
-    plan_decode(M, K, N, G, dtype, num_cus, splits, sit, pl);
+    st = plan_decode(M, K, N, G, dtype, num_cus, L, mode, pl);
+    if (st != W4A16_OK) return st;
   } else if (route == W4A16_ROUTE_PREFILL) {
     plan_prefill(M, N, pl);
   } else {
@@ -167,8 +192,8 @@ w4a16_status check_plan(const w4a16_plan_t* pl, int64_t M, int64_t K, int64_t N,
                         int32_t dtype) {
   w4a16_plan_t ref;
   w4a16_status st = make_plan(M, K, N, G, dtype, 256, pl->route,
-                              pl->route == W4A16_ROUTE_DECODE ? pl->splits : 0,
-                              pl->route == W4A16_ROUTE_DECODE ? pl->scale_in_tile : -1, &ref);
+                              pl->route == W4A16_ROUTE_DECODE ? pl->steps_per_wave : 0,
+                              pl->route == W4A16_ROUTE_DECODE ? pl->decode_mode : -1, &ref);
   if (st != W4A16_OK) return st;
   if (std::memcmp(&ref, pl, sizeof(ref)) != 0)
     return fail(W4A16_ERR_PLAN, "plan does not match the problem (route %d)", (int)pl->route);
@@ -182,8 +207,10 @@ struct DeviceState {
   bool probed = false;
   bool ok = false;
   int num_cus = 0;
-  void* ws = nullptr;
-  size_t ws_bytes = 0;
+  float* partials = nullptr;      // split-K fp32 partials, [S, M, N]
+  size_t partial_bytes = 0;
+  int32_t* counters = nullptr;    // arrival counters, one per column block
+  size_t counter_n = 0;
 };
 std::mutex g_mu;
 std::vector<DeviceState> g_dev;
@@ -212,30 +239,54 @@ w4a16_status device_state(DeviceState** out) {
   return W4A16_OK;
 }
 
-// Grows the device's split-K scratch; new memory is zeroed once so the
-// arrival counters start at zero (the kernels leave them at zero).
-w4a16_status ensure_workspace(DeviceState* ds, size_t bytes, hipStream_t stream) {
+// Grows the device's split-K scratch. The partials need no initial value;
+// the arrival counters live in a buffer of their own that is zeroed when it
+// is allocated and that every launch leaves at zero (the last workgroup of
+// each column block resets its counter), so shapes of different size never
+// see each other's data in a counter slot.
+w4a16_status ensure_workspace(DeviceState* ds, size_t partial_bytes, size_t counter_n) {
   std::lock_guard<std::mutex> lk(g_mu);
-  if (ds->ws_bytes >= bytes) return W4A16_OK;
-  if (ds->ws) {
-    if (hipStreamSynchronize(stream) != hipSuccess || hipFree(ds->ws) != hipSuccess) {
+  if (ds->partial_bytes >= partial_bytes && ds->counter_n >= counter_n) return W4A16_OK;
+  // other streams may still use the old buffers
+  if (hipDeviceSynchronize() != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(W4A16_ERR_HIP, "device synchronisation before growing the scratch failed");
+  }
+  if (ds->partial_bytes < partial_bytes) {
+    if (ds->partials && hipFree(ds->partials) != hipSuccess) {
       (void)hipGetLastError();
-      return fail(W4A16_ERR_HIP, "freeing the old split-K scratch failed");
+      return fail(W4A16_ERR_HIP, "freeing the old split-K partials failed");
     }
-    ds->ws = nullptr;
-    ds->ws_bytes = 0;
+    ds->partials = nullptr;
+    ds->partial_bytes = 0;
+    const size_t sz = std::max<size_t>(partial_bytes, (size_t)8 << 20);
+    if (hipMalloc((void**)&ds->partials, sz) != hipSuccess) {
+      (void)hipGetLastError();
+      ds->partials = nullptr;
+      return fail(W4A16_ERR_HIP, "hipMalloc of %zu bytes of split-K partials failed", sz);
+    }
+    ds->partial_bytes = sz;
   }
-  size_t sz = std::max<size_t>(bytes, (size_t)8 << 20);
-  if (hipMalloc(&ds->ws, sz) != hipSuccess) {
-    (void)hipGetLastError();
-    ds->ws = nullptr;
-    return fail(W4A16_ERR_HIP, "hipMalloc of %zu bytes of split-K scratch failed", sz);
+  if (ds->counter_n < counter_n) {
+    if (ds->counters && hipFree(ds->counters) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(W4A16_ERR_HIP, "freeing the old arrival counters failed");
+    }
+    ds->counters = nullptr;
+    ds->counter_n = 0;
+    const size_t n = std::max<size_t>(counter_n, 4096);
+    if (hipMalloc((void**)&ds->counters, n * sizeof(int32_t)) != hipSuccess) {
+      (void)hipGetLastError();
+      ds->counters = nullptr;
+      return fail(W4A16_ERR_HIP, "hipMalloc of the arrival counters failed");
+    }
+    if (hipMemset(ds->counters, 0, n * sizeof(int32_t)) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(W4A16_ERR_HIP, "clearing the arrival counters failed");
+    }
+    ds->counter_n = n;
   }
-  if (hipMemset(ds->ws, 0, sz) != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(W4A16_ERR_HIP, "clearing the split-K scratch failed");
-  }
-  ds->ws_bytes = sz;
   return W4A16_OK;
 }
 
@@ -258,18 +309,19 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, DeviceState* 
     p.zp_bias = g.zp_bias;
     p.KS = (int32_t)ceil_div(g.K, kStepRows);
     p.SG = ((int64_t)g.G == g.K) ? p.KS : g.G / kStepRows;
+    p.sg_shift = ((int64_t)g.G == g.K) ? -1 : (g.G == 32 ? 0 : g.G == 64 ? 1 : 2);
     p.L = pl.steps_per_wave;
     p.S = pl.splits;
     p.NB = (int32_t)ceil_div(g.N, kDecodeCols);
     if (pl.splits > 1) {
-      w4a16_status st = ensure_workspace(ds, (size_t)pl.workspace_bytes, stream);
+      const size_t part = (size_t)pl.splits * g.M * g.N * sizeof(float);
+      w4a16_status st = ensure_workspace(ds, part, (size_t)p.NB);
       if (st != W4A16_OK) return st;
-      const size_t part = (size_t)pl.splits * g.M * g.N * 4;
-      p.ws = (float*)ds->ws;
-      p.counters = (int32_t*)((char*)ds->ws + ((part + 255) & ~(size_t)255));
+      p.ws = ds->partials;
+      p.counters = ds->counters;
     }
-    e = launch_decode(p, g.dtype, g.qzeros != nullptr, pl.scale_in_tile != 0, pl.grid,
-                      pl.lds_bytes, stream);
+    e = launch_decode(p, g.dtype, g.qzeros != nullptr, pl.decode_mode, pl.grid, pl.lds_bytes,
+                      stream);
   } else {
     PrefillParams p{};
     p.a = (const uint16_t*)g.a;
@@ -317,9 +369,9 @@ w4a16_status gemm_common(const void* a, const int32_t* b_q, const void* scales,
   if (const char* lg = std::getenv("W4A16_LOG")) {
     if (lg[0] == '1')
       std::fprintf(stderr,
-                   "[w4a16] M=%lld K=%lld N=%lld G=%d route=%d bm=%d splits=%d L=%d sit=%d grid=%d\n",
+                   "[w4a16] M=%lld K=%lld N=%lld G=%d route=%d bm=%d splits=%d L=%d mode=%d grid=%d\n",
                    (long long)M, (long long)K, (long long)N, (int)G, pl.route, pl.block_m, pl.splits,
-                   pl.steps_per_wave, pl.scale_in_tile, pl.grid);
+                   pl.steps_per_wave, pl.decode_mode, pl.grid);
   }
   w4a16::GemmArgs g{a, b_q, scales, qzeros, out, M, K, N, G, zp_bias, dtype};
   return run(g, pl, ds, (hipStream_t)stream);
@@ -352,12 +404,12 @@ w4a16_status w4a16_plan(int64_t M, int64_t K, int64_t N, int32_t group_size, int
 }
 
 w4a16_status w4a16_plan_route(int64_t M, int64_t K, int64_t N, int32_t group_size, int32_t has_zp,
-                              int32_t dtype, int32_t num_cus, int32_t route, int32_t splits,
-                              int32_t scale_in_tile, w4a16_plan_t* plan) {
+                              int32_t dtype, int32_t num_cus, int32_t route, int32_t steps_per_wave,
+                              int32_t decode_mode, w4a16_plan_t* plan) {
   (void)has_zp;
   if (route != W4A16_ROUTE_DECODE && route != W4A16_ROUTE_PREFILL)
     return fail(W4A16_ERR_PLAN, "route must be decode (1) or prefill (2), got %d", (int)route);
-  return make_plan(M, K, N, group_size, dtype, num_cus, route, splits, scale_in_tile, plan);
+  return make_plan(M, K, N, group_size, dtype, num_cus, route, steps_per_wave, decode_mode, plan);
 }
 
 w4a16_status w4a16_dequant(const int32_t* b_q, const void* scales, const int32_t* qzeros,

@@ -17,7 +17,7 @@ constexpr int kDecodeCols = 256;       // output columns per workgroup
 constexpr int kDecodeWaves = 4;        // wavefronts per workgroup
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr int kStepRows = 32;          // K rows per MFMA step
-constexpr int kDecodeChunk = 4;        // steps whose loads are issued together
+constexpr int kDecodeMaxSteps = 4;     // most 32-row steps one wavefront loads at once
 constexpr int kAutoDecodeMaxM = 16;    // selector: decode for 1 <= M <= this
 
 // ---- prefill route (tiled MFMA)
@@ -56,6 +56,7 @@ struct DecodeParams {
   int32_t M, K, N, G, zp_bias;
   int32_t KS;         // K steps of 32 rows
   int32_t SG;         // steps per group
+  int32_t sg_shift;   // log2(SG); -1 when one group spans every step
   int32_t L;          // steps per wavefront
   int32_t S;          // splits across workgroups
   int32_t NB;         // column blocks
@@ -79,9 +80,8 @@ struct DequantParams {
   int32_t K, N, G, zp_bias;
 };
 
-hipError_t launch_decode(const DecodeParams& p, int dtype, bool has_zp,
-                         bool scale_in_tile, int grid, int lds_bytes,
-                         hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int dtype, bool has_zp, int mode,
+                         int grid, int lds_bytes, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int dtype, bool has_zp,
                           int block_m, int grid, hipStream_t stream);
 hipError_t launch_dequant(const DequantParams& p, int dtype, bool has_zp,

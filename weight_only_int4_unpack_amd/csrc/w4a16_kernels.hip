@@ -149,6 +149,10 @@ __device__ __forceinline__ uint32_t exact_pair(BF16, uint32_t y, const ColBF16& 
 
 __device__ __forceinline__ uint32_t nib(uint32_t w, int j) { return (w >> (4 * j)) & 0xFu; }
 
+// 16 bytes of zeros: the load source of activation operands that lie past M
+// or K, so that no loaded register has to be cleared afterwards.
+__device__ __attribute__((aligned(16))) const uint32_t kZeroBlock[4] = {0u, 0u, 0u, 0u};
+
 // Two rows' half-words h (0: columns 0..3, 1: columns 4..7) of words w0, w1
 // joined into one Y word (row of w0 in the low half).
 __device__ __forceinline__ uint32_t join_rows(uint32_t w0, uint32_t w1, int h) {
@@ -157,21 +161,50 @@ __device__ __forceinline__ uint32_t join_rows(uint32_t w0, uint32_t w1, int h) {
 
 // ---------------------------------------------------------------------------
 // Decode: M <= 16. A workgroup owns 256 output columns and a contiguous range
-// of 32-row K steps; its 4 wavefronts split the range. Lane (g, c) loads,
-// per step, rows 8g..8g+7 of words 2c, 2c+1 of the block (16 columns) and
-// feeds 16 MFMAs (one per column offset t = 0..15: column 16c + t).
-// Partials of the 4 wavefronts meet in LDS; partials of the S workgroups of
-// one column block meet in the fp32 workspace, and the last workgroup to
-// arrive (arrival counter) adds them in split order and writes the output.
+// of 32-row K steps; its 4 wavefronts split the range, L steps each, and a
+// wavefront issues the loads of all its steps before it computes any. Lane
+// (g, c) loads, per step, rows 8g..8g+7 of words 2c, 2c+1 of the block (16
+// columns) and feeds 16 MFMAs (column offset t = 0..15: column 16c + t).
+// Loads never branch: row and column indices are clamped into the arrays;
+// rows past K meet a zero activation and columns past N are never stored.
 //
-// SCALE_IN_TILE: the MFMA operand is the exact dequantised weight.
-// Otherwise the operand is base + q, the product is taken per group, and the
-// group's scale and zero point are applied once per output element:
-//   sum_k a (q - z) s = s * (sum_k a (base + q) - (base + z) sum_k a),
-// with sum_k a from one extra MFMA against a ones operand.
+// MODE selects where scale and zero point enter:
+//   kSit:    the MFMA operand is the exact dequantised weight RNE((q-z)s).
+//   kOneGrp: the operand is base + q (exact); all L steps of a wavefront lie
+//            in one group, whose scale and zero point are applied once:
+//              sum_k a (q - z) s = s (sum_k a (base + q) - (base + z) sum_k a),
+//            with sum_k a from one extra MFMA against a ones operand.
+//   kMulti:  as kOneGrp, but a wavefront may span groups: each group's
+//            partial is folded into a second accumulator at its last step.
+// Partials of the 4 wavefronts meet in LDS; partials of the S workgroups of
+// one column block meet in an fp32 scratch buffer through write-through
+// (agent-scope) stores, and the last workgroup to arrive (arrival counter)
+// adds them in split order and writes the output, so the result does not
+// depend on arrival order. No cache-wide flush is needed: the partials never
+// sit dirty in a per-XCD L2, and they are read back with agent-scope loads.
 // ---------------------------------------------------------------------------
-template <typename T, bool HAS_ZP, bool SCALE_IN_TILE, bool ALIGNED>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) {
+enum { kSit = 0, kOneGrp = 1, kMulti = 2 };
+
+template <typename T, int E>
+__device__ __forceinline__ u32x4 magic_op(const uint32_t* y) {
+  return u32x4{magic_pair<T, E>(y[0]), magic_pair<T, E>(y[1]), magic_pair<T, E>(y[2]),
+               magic_pair<T, E>(y[3])};
+}
+template <typename T, int E>
+__device__ __forceinline__ u32x4 exact_op(const uint32_t* y, uint32_t s_bits, uint32_t z) {
+  const auto cc = make_col<E>(T{}, s_bits, z);
+  return u32x4{exact_pair<E>(T{}, y[0], cc), exact_pair<E>(T{}, y[1], cc),
+               exact_pair<E>(T{}, y[2], cc), exact_pair<E>(T{}, y[3], cc)};
+}
+
+__device__ __forceinline__ uint32_t half_of(const u32x4 (&sv)[2], int t) {
+  const uint32_t w = sv[t >> 3][(t >> 1) & 3];
+  return (t & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+// MT: M rounded up to 4, 8 or 16 (compile-time row count of the reductions).
+template <typename T, bool HAS_ZP, int MODE, bool ALIGNED, int L, int MT>
+__global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams p) {
   extern __shared__ float red[];
   __shared__ int last_flag;
 
@@ -185,167 +218,158 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
   const int N8 = p.N >> 3;
   const int word0 = b * (kDecodeCols / 8) + 2 * c;
   const int col0 = word0 * 8;
-  const bool full = (word0 + 1) < N8;  // both words of this lane exist
+  // clamped indices: every load below is in bounds without a branch
+  const int wc0 = min(word0, N8 - 1);
+  const int wc1 = min(word0 + 1, N8 - 1);
+  const int wcv = ALIGNED ? min(word0, N8 - 2) : 0;  // 8-byte aligned pair
+  const int colv = ALIGNED ? min(col0, p.N - 16) : 0;
+  const int mrow = min(c, p.M - 1);
+  const bool a_live = c < p.M;
 
-  const int step_beg = (s * kDecodeWaves + wave) * p.L;
-  const int step_end = min(step_beg + p.L, p.KS);
+  const int step_beg = (s * kDecodeWaves + wave) * L;
+  const int nsteps = max(0, min(L, p.KS - step_beg));
 
   f32x4 acc[16];
-#pragma unroll
-  for (int t = 0; t < 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 R[16];
   f32x4 Rs = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (!SCALE_IN_TILE) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) R[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < 16; ++t) {
+    acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    R[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const u32x4 ones = u32x4{T::kOnePair, T::kOnePair, T::kOnePair, T::kOnePair};
-  const bool a_vec = (p.K & 7) == 0;
 
-  for (int cs = step_beg; cs < step_end; cs += kDecodeChunk) {
-    u32x2 W[kDecodeChunk][8];
-    u32x4 Aop[kDecodeChunk];
-    u32x4 Sv[kDecodeChunk][2];
-    u32x2 Zv[kDecodeChunk];
-    // ---- issue every load of the chunk
+  // ---- issue the loads of all L steps. No load is predicated and no
+  // loaded register is overwritten before use (either would make the
+  // compiler wait for the load): steps past the range read clamped
+  // addresses and are skipped at compute time; activation rows past M or K
+  // read from a block of zeros instead.
+  u32x2 W[L][8];
+  u32x4 Aop[L];
+  u32x4 Sv[MODE == kOneGrp ? 1 : L][2];
+  u32x2 Zv[MODE == kOneGrp ? 1 : L];
+  const uint16_t* arow = p.a + (int64_t)mrow * p.K;
 #pragma unroll
-    for (int j = 0; j < kDecodeChunk; ++j) {
-      const int st = cs + j;
-      const bool live = st < step_end;
+  for (int j = 0; j < L; ++j) {
+    const int st = min(step_beg + j, p.KS - 1);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int row = st * kStepRows + 8 * g + r;
-        u32x2 w = u32x2{0u, 0u};
-        if (live && row < p.K) {
-          const uint32_t* src = p.bq + (int64_t)row * N8 + word0;
-          if (ALIGNED && full) {
-            w = *(const u32x2*)src;
-          } else {
-            if (word0 < N8) w.x = src[0];
-            if (word0 + 1 < N8) w.y = src[1];
-          }
-        }
-        W[j][r] = w;
+    for (int r = 0; r < 8; ++r) {
+      const int row = min(st * kStepRows + 8 * g + r, p.K - 1);
+      const uint32_t* src = p.bq + (int64_t)row * N8;
+      if constexpr (ALIGNED) {
+        W[j][r] = *(const u32x2*)(src + wcv);
+      } else {
+        W[j][r] = u32x2{src[wc0], src[wc1]};
       }
-      // activation operand: row c, k = 8g..8g+7 of the step
-      u32x4 av = u32x4{0u, 0u, 0u, 0u};
-      const int k = st * kStepRows + 8 * g;
-      if (live && c < p.M) {
-        const uint16_t* src = p.a + (int64_t)c * p.K + k;
-        if (a_vec && k + 8 <= p.K) {
-          av = *(const u32x4*)src;
-        } else {
-          uint32_t h[8];
+    }
+    const int k = st * kStepRows + 8 * g;
+    if constexpr (ALIGNED) {  // K % 8 == 0: a whole 8-element piece or none
+      const bool live = a_live && k < p.K;
+      Aop[j] = *(const u32x4*)(live ? (const void*)(arow + k) : (const void*)kZeroBlock);
+    } else {
+      uint32_t h[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) h[e] = (k + e < p.K) ? (uint32_t)src[e] : 0u;
-          av = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+      for (int e = 0; e < 8; ++e) {
+        const bool live = a_live && k + e < p.K;
+        h[e] = *(live ? arow + k + e : (const uint16_t*)kZeroBlock);
+      }
+      Aop[j] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
                      h[6] | (h[7] << 16)};
-        }
-      }
-      Aop[j] = av;
-      // this step's group: 16 scales, 2 zero-point words
-      const int grp = min(st, p.KS - 1) / p.SG;
-      const uint16_t* sp = p.sc + (int64_t)grp * p.N + col0;
-      if (ALIGNED && full) {
-        Sv[j][0] = *(const u32x4*)sp;
-        Sv[j][1] = *(const u32x4*)(sp + 8);
+    }
+    if (MODE != kOneGrp || j == 0) {
+      const int jj = MODE == kOneGrp ? 0 : j;
+      const int grp = p.sg_shift < 0 ? 0 : (st >> p.sg_shift);
+      const uint16_t* sp = p.sc + (int64_t)grp * p.N;
+      if constexpr (ALIGNED) {
+        Sv[jj][0] = *(const u32x4*)(sp + colv);
+        Sv[jj][1] = *(const u32x4*)(sp + colv + 8);
       } else {
         uint32_t h[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) h[e] = (col0 + e < p.N) ? (uint32_t)sp[e] : 0u;
-        Sv[j][0] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                         h[6] | (h[7] << 16)};
-        Sv[j][1] = u32x4{h[8] | (h[9] << 16), h[10] | (h[11] << 16), h[12] | (h[13] << 16),
-                         h[14] | (h[15] << 16)};
+        for (int e = 0; e < 16; ++e) h[e] = sp[min(col0 + e, p.N - 1)];
+        Sv[jj][0] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                          h[6] | (h[7] << 16)};
+        Sv[jj][1] = u32x4{h[8] | (h[9] << 16), h[10] | (h[11] << 16), h[12] | (h[13] << 16),
+                          h[14] | (h[15] << 16)};
       }
       if constexpr (HAS_ZP) {
-        const uint32_t* zp = p.qz + (int64_t)grp * N8 + word0;
-        if (ALIGNED && full) {
-          Zv[j] = *(const u32x2*)zp;
+        const uint32_t* zp = p.qz + (int64_t)grp * N8;
+        if constexpr (ALIGNED) {
+          Zv[jj] = *(const u32x2*)(zp + wcv);
         } else {
-          Zv[j] = u32x2{word0 < N8 ? zp[0] : 0u, word0 + 1 < N8 ? zp[1] : 0u};
+          Zv[jj] = u32x2{zp[wc0], zp[wc1]};
         }
       } else {
         const uint32_t zb = (uint32_t)p.zp_bias * 0x11111111u;
-        Zv[j] = u32x2{zb, zb};
+        Zv[jj] = u32x2{zb, zb};
       }
     }
-    // ---- compute the chunk
+  }
+
+  // keep every load above this point: the whole range is in flight before
+  // the first wait
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- compute
 #pragma unroll
-    for (int j = 0; j < kDecodeChunk; ++j) {
-      const int st = cs + j;
-      if (st >= step_end) break;
-      uint32_t Y[2][2][4];  // [word][half][row pair]
+  for (int j = 0; j < L; ++j) {
+    if (j >= nsteps) break;
+    const int st = step_beg + j;
+    uint32_t Y[2][2][4];  // [word][half][row pair]
 #pragma unroll
-      for (int w = 0; w < 2; ++w)
+    for (int w = 0; w < 2; ++w)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            Y[w][h][i] = join_rows(W[j][2 * i][w], W[j][2 * i + 1][w], h);
-      const uint32_t* sv = (const uint32_t*)&Sv[j][0];
+        for (int i = 0; i < 4; ++i) Y[w][h][i] = join_rows(W[j][2 * i][w], W[j][2 * i + 1][w], h);
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int w = t >> 3, h = (t >> 2) & 1;
-        constexpr int dummy = 0;
-        (void)dummy;
+    for (int t = 0; t < 16; ++t) {
+      const uint32_t* y = Y[t >> 3][(t >> 2) & 1];
+      if constexpr (MODE == kSit) {
+        const uint32_t sb = half_of(Sv[j], t);
+        const uint32_t z = nib(Zv[j][t >> 3], t & 7);
         u32x4 bop;
-        if constexpr (SCALE_IN_TILE) {
-          const uint32_t s_bits = (t & 1) ? (sv[t >> 1] >> 16) : (sv[t >> 1] & 0xFFFFu);
-          const uint32_t z = nib(Zv[j][w], t & 7);
-          switch (t & 3) {
-            case 0: { auto cc = make_col<0>(T{}, s_bits, z);
-              bop = u32x4{exact_pair<0>(T{}, Y[w][h][0], cc), exact_pair<0>(T{}, Y[w][h][1], cc),
-                          exact_pair<0>(T{}, Y[w][h][2], cc), exact_pair<0>(T{}, Y[w][h][3], cc)};
-            } break;
-            case 1: { auto cc = make_col<1>(T{}, s_bits, z);
-              bop = u32x4{exact_pair<1>(T{}, Y[w][h][0], cc), exact_pair<1>(T{}, Y[w][h][1], cc),
-                          exact_pair<1>(T{}, Y[w][h][2], cc), exact_pair<1>(T{}, Y[w][h][3], cc)};
-            } break;
-            case 2: { auto cc = make_col<2>(T{}, s_bits, z);
-              bop = u32x4{exact_pair<2>(T{}, Y[w][h][0], cc), exact_pair<2>(T{}, Y[w][h][1], cc),
-                          exact_pair<2>(T{}, Y[w][h][2], cc), exact_pair<2>(T{}, Y[w][h][3], cc)};
-            } break;
-            default: { auto cc = make_col<3>(T{}, s_bits, z);
-              bop = u32x4{exact_pair<3>(T{}, Y[w][h][0], cc), exact_pair<3>(T{}, Y[w][h][1], cc),
-                          exact_pair<3>(T{}, Y[w][h][2], cc), exact_pair<3>(T{}, Y[w][h][3], cc)};
-            } break;
-          }
-          acc[t] = mfma<T>(Aop[j], bop, acc[t]);
-        } else {
-          switch (t & 3) {
-            case 0: bop = u32x4{magic_pair<T, 0>(Y[w][h][0]), magic_pair<T, 0>(Y[w][h][1]),
-                                magic_pair<T, 0>(Y[w][h][2]), magic_pair<T, 0>(Y[w][h][3])}; break;
-            case 1: bop = u32x4{magic_pair<T, 1>(Y[w][h][0]), magic_pair<T, 1>(Y[w][h][1]),
-                                magic_pair<T, 1>(Y[w][h][2]), magic_pair<T, 1>(Y[w][h][3])}; break;
-            case 2: bop = u32x4{magic_pair<T, 2>(Y[w][h][0]), magic_pair<T, 2>(Y[w][h][1]),
-                                magic_pair<T, 2>(Y[w][h][2]), magic_pair<T, 2>(Y[w][h][3])}; break;
-            default: bop = u32x4{magic_pair<T, 3>(Y[w][h][0]), magic_pair<T, 3>(Y[w][h][1]),
-                                 magic_pair<T, 3>(Y[w][h][2]), magic_pair<T, 3>(Y[w][h][3])}; break;
-          }
-          R[t] = mfma<T>(Aop[j], bop, R[t]);
+        switch (t & 3) {
+          case 0: bop = exact_op<T, 0>(y, sb, z); break;
+          case 1: bop = exact_op<T, 1>(y, sb, z); break;
+          case 2: bop = exact_op<T, 2>(y, sb, z); break;
+          default: bop = exact_op<T, 3>(y, sb, z); break;
         }
+        acc[t] = mfma<T>(Aop[j], bop, acc[t]);
+      } else {
+        u32x4 bop;
+        switch (t & 3) {
+          case 0: bop = magic_op<T, 0>(y); break;
+          case 1: bop = magic_op<T, 1>(y); break;
+          case 2: bop = magic_op<T, 2>(y); break;
+          default: bop = magic_op<T, 3>(y); break;
+        }
+        R[t] = mfma<T>(Aop[j], bop, R[t]);
       }
-      if constexpr (!SCALE_IN_TILE) {
-        Rs = mfma<T>(Aop[j], ones, Rs);
-        const bool group_end = ((st + 1) % p.SG == 0) || (st + 1 == step_end);
-        if (group_end) {
+    }
+    if constexpr (MODE != kSit) {
+      Rs = mfma<T>(Aop[j], ones, Rs);
+      const bool group_last = p.sg_shift >= 0 && (((st + 1) & ((1 << p.sg_shift) - 1)) == 0);
+      const bool fold = (MODE == kMulti) ? (group_last || (j + 1 == nsteps)) : (j + 1 == nsteps);
+      if (fold) {
+        const int jj = MODE == kOneGrp ? 0 : j;
 #pragma unroll
-          for (int t = 0; t < 16; ++t) {
-            const int w = t >> 3;
-            const bool odd16 = (T::kBase == 1024.0f) && (t & 1);
-            const uint32_t s_bits = (t & 1) ? (sv[t >> 1] >> 16) : (sv[t >> 1] & 0xFFFFu);
-            const float z = (float)nib(Zv[j][w], t & 7);
-            const float sc = widen(T{}, s_bits) * (odd16 ? 0.0625f : 1.0f);
-            const float bias = T::kBase + z * (odd16 ? 16.0f : 1.0f);
+        for (int t = 0; t < 16; ++t) {
+          const bool odd16 = (T::kBase == 1024.0f) && (t & 1);
+          const float sc = widen(T{}, half_of(Sv[jj], t)) * (odd16 ? 0.0625f : 1.0f);
+          const float bias = T::kBase + (float)nib(Zv[jj][t >> 3], t & 7) * (odd16 ? 16.0f : 1.0f);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              acc[t][v] = __builtin_fmaf(sc, __builtin_fmaf(-bias, Rs[v], R[t][v]), acc[t][v]);
+          for (int v = 0; v < 4; ++v) {
+            const float part = __builtin_fmaf(-bias, Rs[v], R[t][v]);
+            if constexpr (MODE == kMulti) {
+              acc[t][v] = __builtin_fmaf(sc, part, acc[t][v]);
+            } else {
+              acc[t][v] = sc * part;
             }
-            R[t] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
-          Rs = f32x4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (MODE == kMulti) R[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        if constexpr (MODE == kMulti) Rs = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
   }
@@ -353,54 +377,90 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
   // ---- the 4 wavefronts' partials meet in LDS: red[wave][m][256]
   const int M = p.M;
 #pragma unroll
-  for (int t = 0; t < 16; ++t)
+  for (int v = 0; v < 4; ++v) {
+    const int m = 4 * g + v;
+    if (m < M) {
+      float* dst = red + (wave * M + m) * kDecodeCols + 16 * c;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = 4 * g + v;
-      if (m < M) red[(wave * M + m) * kDecodeCols + 16 * c + t] = acc[t][v];
+      for (int t4 = 0; t4 < 4; ++t4)
+        *(f32x4*)(dst + 4 * t4) = f32x4{acc[4 * t4][v], acc[4 * t4 + 1][v], acc[4 * t4 + 2][v],
+                                        acc[4 * t4 + 3][v]};
     }
+  }
   __syncthreads();
 
+  // thread tid owns column b*256 + tid of every row
   const int col = b * kDecodeCols + tid;
   const bool col_ok = col < p.N;
+  const int colc = min(col, p.N - 1);
+  float part[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (m < M) {
+      float v = red[m * kDecodeCols + tid];
+#pragma unroll
+      for (int w = 1; w < kDecodeWaves; ++w) v += red[(w * M + m) * kDecodeCols + tid];
+      part[m] = v;
+    }
+  }
   if (p.S == 1) {
     if (col_ok) {
-      for (int m = 0; m < M; ++m) {
-        float v = red[m * kDecodeCols + tid];
 #pragma unroll
-        for (int w = 1; w < kDecodeWaves; ++w) v += red[(w * M + m) * kDecodeCols + tid];
-        p.out[(int64_t)m * p.N + col] = narrow(T{}, v);
-      }
+      for (int m = 0; m < MT; ++m)
+        if (m < M) p.out[(int64_t)m * p.N + col] = narrow(T{}, part[m]);
     }
     return;
   }
   if (col_ok) {
-    for (int m = 0; m < M; ++m) {
-      float v = red[m * kDecodeCols + tid];
 #pragma unroll
-      for (int w = 1; w < kDecodeWaves; ++w) v += red[(w * M + m) * kDecodeCols + tid];
-      p.ws[((int64_t)s * M + m) * p.N + col] = v;
-    }
+    for (int m = 0; m < MT; ++m)
+      if (m < M)
+        __hip_atomic_store(&p.ws[((int64_t)s * M + m) * p.N + col], part[m], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
   }
-  __threadfence();
+  // every write-through store of this thread has completed before the
+  // barrier, so the counter cannot run ahead of the partials
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   if (tid == 0) {
-    const int prev = atomicAdd(&p.counters[b], 1);
+    const int prev = __hip_atomic_fetch_add(&p.counters[b], 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
     last_flag = (prev == p.S - 1);
   }
   __syncthreads();
   if (!last_flag) return;
-  __threadfence();
-  if (col_ok) {
-    for (int m = 0; m < M; ++m) {
-      float v = 0.f;
-      for (int q = 0; q < p.S; ++q) {
-        v += __builtin_nontemporal_load(&p.ws[((int64_t)q * M + m) * p.N + col]);
-      }
-      p.out[(int64_t)m * p.N + col] = narrow(T{}, v);
+  // last arrival: add the S partials of every row in split order; QB splits'
+  // loads of all rows are in flight at once
+  constexpr int QB = (32 / MT) > 1 ? (32 / MT) : 1;
+  float sum[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) sum[m] = 0.f;
+  for (int q0 = 0; q0 < p.S; q0 += QB) {
+    float tq[QB][MT];
+#pragma unroll
+    for (int u = 0; u < QB; ++u) {
+      const int q = min(q0 + u, p.S - 1);
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        if (m < M)
+          tq[u][m] = __hip_atomic_load(&p.ws[((int64_t)q * M + m) * p.N + colc], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
     }
+#pragma unroll
+    for (int u = 0; u < QB; ++u)
+      if (q0 + u < p.S) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          if (m < M) sum[m] += tq[u][m];
+      }
   }
-  if (tid == 0) atomicExch(&p.counters[b], 0);
+  if (col_ok) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      if (m < M) p.out[(int64_t)m * p.N + col] = narrow(T{}, sum[m]);
+  }
+  if (tid == 0)
+    __hip_atomic_store(&p.counters[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -412,7 +472,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
 // packed word per row) and forms four operands (column 4c + t, t = 0..3).
 // Workgroup ids are spread so that the tiles of one XCD share A rows.
 // ---------------------------------------------------------------------------
-template <typename T, bool HAS_ZP, int BM>
+// PC (one group spanning all of K): the operand is the exact integer q - z
+// and each output column is multiplied by its scale once, in fp32, at the
+// end; no weight is rounded before the product.
+template <typename T, bool HAS_ZP, bool PC, int BM>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams p) {
   constexpr int RH = kPrefillLdsRowHalves;
   constexpr int MB = BM / 16;
@@ -485,8 +548,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
       const int row = k0 + 8 * g + r;
       bs.q[r] = (row < p.K && ncol_ok) ? (uint32_t)bq16[(int64_t)row * N4 + (ncol >> 2)] : 0u;
     }
-    const int grp = min(k0, p.K - 1) / p.G;
-    bs.s = ncol_ok ? *(const u32x2*)(p.sc + (int64_t)grp * p.N + ncol) : u32x2{0u, 0u};
+    const int grp = PC ? 0 : min(k0, p.K - 1) / p.G;
+    if constexpr (PC) {
+      bs.s = u32x2{T::kOnePair, T::kOnePair};
+    } else {
+      bs.s = ncol_ok ? *(const u32x2*)(p.sc + (int64_t)grp * p.N + ncol) : u32x2{0u, 0u};
+    }
     if constexpr (HAS_ZP) {
       bs.z = ncol_ok ? (uint32_t)qz16[(int64_t)grp * N4 + (ncol >> 2)] : 0u;
     } else {
@@ -548,6 +615,15 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
 
   // ---- epilogue: lane holds rows i*16 + 4g + v, columns ncol + t
   if (!ncol_ok) return;
+  if constexpr (PC) {
+    const u32x2 sv = *(const u32x2*)(p.sc + ncol);
+    const float sc[4] = {widen(T{}, sv.x & 0xFFFFu), widen(T{}, sv.x >> 16),
+                         widen(T{}, sv.y & 0xFFFFu), widen(T{}, sv.y >> 16)};
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[i][t] *= sc[t];
+  }
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -605,49 +681,81 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <typename T, bool Z, bool SIT, bool AL>
+template <typename T, bool Z, int MODE, bool AL, int L, int MT>
 static hipError_t decode_go(const DecodeParams& p, int grid, int lds, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<T, Z, SIT, AL>), dim3(grid), dim3(kDecodeThreads),
+  hipLaunchKernelGGL((decode_kernel<T, Z, MODE, AL, L, MT>), dim3(grid), dim3(kDecodeThreads),
                      lds, st, p);
   return hipGetLastError();
 }
-template <typename T, bool Z, bool SIT>
+template <typename T, bool Z, int MODE, bool AL, int L>
+static hipError_t decode_mt(const DecodeParams& p, int grid, int lds, hipStream_t st) {
+  if (p.M <= 4) return decode_go<T, Z, MODE, AL, L, 4>(p, grid, lds, st);
+  if (p.M <= 8) return decode_go<T, Z, MODE, AL, L, 8>(p, grid, lds, st);
+  return decode_go<T, Z, MODE, AL, L, 16>(p, grid, lds, st);
+}
+template <typename T, bool Z, int MODE, bool AL>
+static hipError_t decode_l(const DecodeParams& p, int grid, int lds, hipStream_t st) {
+  if constexpr (!AL) {
+    // shapes off the fast layout run one step per wavefront, 16-row reductions
+    if (p.L != 1) return hipErrorInvalidValue;
+    return decode_go<T, Z, MODE, AL, 1, 16>(p, grid, lds, st);
+  } else {
+    switch (p.L) {
+      case 1: return decode_mt<T, Z, MODE, AL, 1>(p, grid, lds, st);
+      case 2: return decode_mt<T, Z, MODE, AL, 2>(p, grid, lds, st);
+      case 4: return decode_mt<T, Z, MODE, AL, 4>(p, grid, lds, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+}
+template <typename T, bool Z, int MODE>
 static hipError_t decode_al(const DecodeParams& p, int grid, int lds, hipStream_t st) {
-  if ((p.N & 15) == 0) return decode_go<T, Z, SIT, true>(p, grid, lds, st);
-  return decode_go<T, Z, SIT, false>(p, grid, lds, st);
+  if ((p.N & 15) == 0 && (p.K & 7) == 0) return decode_l<T, Z, MODE, true>(p, grid, lds, st);
+  return decode_l<T, Z, MODE, false>(p, grid, lds, st);
 }
 template <typename T, bool Z>
-static hipError_t decode_sit(const DecodeParams& p, bool sit, int grid, int lds, hipStream_t st) {
-  return sit ? decode_al<T, Z, true>(p, grid, lds, st) : decode_al<T, Z, false>(p, grid, lds, st);
-}
-hipError_t launch_decode(const DecodeParams& p, int dtype, bool has_zp, bool sit, int grid,
-                         int lds, hipStream_t st) {
-  if (dtype == W4A16_F16)
-    return has_zp ? decode_sit<F16, true>(p, sit, grid, lds, st)
-                  : decode_sit<F16, false>(p, sit, grid, lds, st);
-  return has_zp ? decode_sit<BF16, true>(p, sit, grid, lds, st)
-                : decode_sit<BF16, false>(p, sit, grid, lds, st);
-}
-
-template <typename T, bool Z, int BM>
-static hipError_t prefill_go(const PrefillParams& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_kernel<T, Z, BM>), dim3(grid), dim3(kPrefillThreads), 0, st, p);
-  return hipGetLastError();
-}
-template <typename T, bool Z>
-static hipError_t prefill_bm(const PrefillParams& p, int bm, int grid, hipStream_t st) {
-  switch (bm) {
-    case 256: return prefill_go<T, Z, 256>(p, grid, st);
-    case 128: return prefill_go<T, Z, 128>(p, grid, st);
-    case 64: return prefill_go<T, Z, 64>(p, grid, st);
+static hipError_t decode_mode(const DecodeParams& p, int mode, int grid, int lds, hipStream_t st) {
+  switch (mode) {
+    case kSit: return decode_al<T, Z, kSit>(p, grid, lds, st);
+    case kOneGrp: return decode_al<T, Z, kOneGrp>(p, grid, lds, st);
+    case kMulti: return decode_al<T, Z, kMulti>(p, grid, lds, st);
     default: return hipErrorInvalidValue;
   }
+}
+hipError_t launch_decode(const DecodeParams& p, int dtype, bool has_zp, int mode, int grid,
+                         int lds, hipStream_t st) {
+  if (dtype == W4A16_F16)
+    return has_zp ? decode_mode<F16, true>(p, mode, grid, lds, st)
+                  : decode_mode<F16, false>(p, mode, grid, lds, st);
+  return has_zp ? decode_mode<BF16, true>(p, mode, grid, lds, st)
+                : decode_mode<BF16, false>(p, mode, grid, lds, st);
+}
+
+template <typename T, bool Z, bool PC, int BM>
+static hipError_t prefill_go(const PrefillParams& p, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((prefill_kernel<T, Z, PC, BM>), dim3(grid), dim3(kPrefillThreads), 0, st,
+                     p);
+  return hipGetLastError();
+}
+template <typename T, bool Z, bool PC>
+static hipError_t prefill_bm(const PrefillParams& p, int bm, int grid, hipStream_t st) {
+  switch (bm) {
+    case 256: return prefill_go<T, Z, PC, 256>(p, grid, st);
+    case 128: return prefill_go<T, Z, PC, 128>(p, grid, st);
+    case 64: return prefill_go<T, Z, PC, 64>(p, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+template <typename T, bool Z>
+static hipError_t prefill_pc(const PrefillParams& p, int bm, int grid, hipStream_t st) {
+  return (p.G == p.K) ? prefill_bm<T, Z, true>(p, bm, grid, st)
+                      : prefill_bm<T, Z, false>(p, bm, grid, st);
 }
 hipError_t launch_prefill(const PrefillParams& p, int dtype, bool has_zp, int bm, int grid,
                           hipStream_t st) {
   if (dtype == W4A16_F16)
-    return has_zp ? prefill_bm<F16, true>(p, bm, grid, st) : prefill_bm<F16, false>(p, bm, grid, st);
-  return has_zp ? prefill_bm<BF16, true>(p, bm, grid, st) : prefill_bm<BF16, false>(p, bm, grid, st);
+    return has_zp ? prefill_pc<F16, true>(p, bm, grid, st) : prefill_pc<F16, false>(p, bm, grid, st);
+  return has_zp ? prefill_pc<BF16, true>(p, bm, grid, st) : prefill_pc<BF16, false>(p, bm, grid, st);
 }
 
 template <typename T, bool Z>

@@ -35,7 +35,7 @@ _DTYPE_CODE = {torch.float16: F16, torch.bfloat16: BF16}
 class Plan(ctypes.Structure):
     _fields_ = [("route", ctypes.c_int32), ("block_m", ctypes.c_int32),
                 ("block_n", ctypes.c_int32), ("block_k", ctypes.c_int32),
-                ("scale_in_tile", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("decode_mode", ctypes.c_int32), ("splits", ctypes.c_int32),
                 ("steps_per_wave", ctypes.c_int32), ("grid", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_int64)]
@@ -176,17 +176,18 @@ def dequant(b_q: torch.Tensor, scales: torch.Tensor, qzeros: torch.Tensor | None
 
 
 def plan(M: int, K: int, N: int, group_size: int, has_zp: bool, dtype, num_cus: int = 256,
-         route: int | None = None, splits: int = 0, scale_in_tile: int = -1) -> Plan:
-    """The launch the selector picks (or the forced route), host only."""
+         route: int | None = None, steps_per_wave: int = 0, decode_mode: int = -1) -> Plan:
+    """The launch the selector picks, or one with the route / decode steps per
+    wavefront / decode mode forced (host only)."""
     code = _DTYPE_CODE.get(dtype, dtype)
     p = Plan()
     L = lib()
-    if route is None and splits == 0 and scale_in_tile < 0:
+    if route is None and steps_per_wave == 0 and decode_mode < 0:
         _check(L.w4a16_plan(M, K, N, group_size, int(has_zp), code, num_cus, ctypes.byref(p)))
     else:
         r = route if route is not None else (ROUTE_DECODE if M <= 16 else ROUTE_PREFILL)
         _check(L.w4a16_plan_route(M, K, N, group_size, int(has_zp), code, num_cus, r,
-                                  splits, scale_in_tile, ctypes.byref(p)))
+                                  steps_per_wave, decode_mode, ctypes.byref(p)))
     return p
 
 
