@@ -79,7 +79,7 @@ typedef struct {
                                wavefront; 2 = as 1, several groups per
                                wavefront */
   int32_t splits;           /* decode: K splits across workgroups */
-  int32_t steps_per_wave;   /* decode: 32-row K steps per wavefront (1, 2, 4) */
+  int32_t steps_per_wave;   /* decode: 32-row K steps per wavefront (1, 2, 4, 8) */
   int32_t grid;             /* workgroups launched */
   int32_t threads;          /* threads per workgroup */
   int32_t lds_bytes;        /* LDS per workgroup */
@@ -125,7 +125,7 @@ w4a16_status w4a16_plan(int64_t M, int64_t K, int64_t N, int32_t group_size,
 /*
  * w4a16_plan_route - as w4a16_plan with the route forced
  * (W4A16_ROUTE_DECODE needs 1 <= M <= 16) and, for decode, the steps per
- * wavefront (1, 2 or 4; 0 = selector's choice) and the decode mode
+ * wavefront (1, 2, 4 or 8; 0 = selector's choice) and the decode mode
  * (0, 1, 2; -1 = selector's choice; mode 1 needs every wavefront's steps
  * inside one group) forced.
  * Errors: those of w4a16_plan, and PLAN.

@@ -136,17 +136,21 @@ def test_selector_decode_shapes():
     p = W.plan(1, 5120, 17408, 128, False, torch.bfloat16)
     nb = 17408 // 256
     assert p.block_n == 256 and p.grid == nb * p.splits
-    assert p.steps_per_wave in (1, 2, 4)
+    assert p.steps_per_wave in (1, 2, 4, 8)
     assert p.splits * 4 * p.steps_per_wave >= 5120 // 32
     assert (p.splits - 1) * 4 * p.steps_per_wave < 5120 // 32        # no empty split
-    assert p.decode_mode == 1                        # one group of 4 steps per wavefront
-    assert (128 // 32) % p.steps_per_wave == 0
+    # 8 steps per wavefront span two groups of 4 steps: scale applied per group
+    assert p.steps_per_wave == 8 and p.decode_mode == 2
+    assert W.plan(1, 5120, 17408, 128, False, torch.bfloat16, route=W.ROUTE_DECODE,
+                  steps_per_wave=4).decode_mode == 1
     # K = 2112 is 66 steps of 32 rows; fp16 with groups of 64 folds the scale
     p = W.plan(8, 2112, 5120, 64, True, torch.float16)
     assert p.splits * 4 * p.steps_per_wave >= 66
     assert p.decode_mode == 0
     assert p.workspace_bytes >= p.splits * 8 * 5120 * 4 or p.splits == 1
-    assert p.lds_bytes == 4 * 8 * 256 * 4
+    # partials of 4 wavefronts, then scales and packed zeros of the staged groups
+    ng = 4 * p.steps_per_wave // 2 + 1
+    assert p.lds_bytes == 4 * 8 * 256 * 4 + ng * 256 * 2 + ng * 32 * 4
     # bf16 with groups of 32 cannot keep 2 or 4 steps in one group
     p = W.plan(4, 4096, 4096, 32, True, torch.bfloat16, route=W.ROUTE_DECODE, steps_per_wave=4)
     assert p.decode_mode == 2

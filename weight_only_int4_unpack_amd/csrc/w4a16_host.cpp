@@ -81,12 +81,19 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // selector
 // ---------------------------------------------------------------------------
 // Decode launch: 256 columns per workgroup, 4 wavefronts of L steps each.
-// L is the largest of 4, 2, 1 that still gives at least two workgroups per
-// CU (more bytes in flight per wavefront when the grid is large enough,
-// more wavefronts when it is not). Mode: fp16 with groups of 32 or 64 folds
+// L (1, 2, 4 or 8) is the smallest that keeps the wavefront count within two
+// resident wavefronts per SIMD, so every wavefront streams from the start and
+// none waits for a second round. Mode: fp16 with groups of 32 or 64 folds
 // the scale into each weight (cheap packed fp16 ops); otherwise the scale is
 // applied per group to the fp32 partial, with one group per wavefront when
 // the wavefront's steps cannot straddle a group boundary.
+int decode_ng_max(int64_t K, int32_t G, int64_t L) {
+  using namespace w4a16;
+  if ((int64_t)G == K) return 1;
+  const int64_t SG = G / kStepRows;
+  return (int)std::max<int64_t>(1, (kDecodeWaves * L) / SG + 1);
+}
+
 w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype, int num_cus,
                          int32_t L_forced, int32_t mode_forced, w4a16_plan_t* pl) {
   using namespace w4a16;
@@ -98,22 +105,18 @@ w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dty
   // wavefront
   const bool aligned = (N % 16 == 0) && (K % 8 == 0);
   int64_t L = L_forced;
+  if (L != 0 && L != 1 && L != 2 && L != 4 && L != 8)
+    return fail(W4A16_ERR_PLAN, "steps per wavefront must be 1, 2, 4 or 8 (got %lld)", (long long)L);
   if (!aligned && L > 1)
     return fail(W4A16_ERR_PLAN, "N %% 16 or K %% 8 nonzero: decode runs one step per wavefront");
-  if (L == 0 && !aligned) L = 1;
   if (L == 0) {
     L = 1;
-    for (int64_t cand : {4, 2}) {
-      if (NB * ceil_div(KS, kDecodeWaves * cand) >= 2 * (int64_t)num_cus) {
-        L = cand;
-        break;
-      }
-    }
+    const int64_t slots = 2 * 4 * (int64_t)num_cus;  // two wavefronts per SIMD
+    if (aligned)
+      while (L < kDecodeMaxSteps && ceil_div(KS, L) * NB > slots) L *= 2;
   }
-  if (L != 1 && L != 2 && L != 4)
-    return fail(W4A16_ERR_PLAN, "steps per wavefront must be 1, 2 or 4 (got %lld)", (long long)L);
   int32_t mode = mode_forced;
-  const bool fits_one = one_group || SG % L == 0;
+  const bool fits_one = one_group || (SG >= L && SG % L == 0);
   if (mode < 0) {
     if (dtype == W4A16_F16 && G <= 64 && !one_group)
       mode = 0;
@@ -134,7 +137,7 @@ w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dty
   pl->steps_per_wave = (int32_t)L;
   pl->grid = (int32_t)(NB * S);
   pl->threads = kDecodeThreads;
-  pl->lds_bytes = decode_lds_bytes((int)M);
+  pl->lds_bytes = decode_lds_bytes((int)M, decode_ng_max(K, G, L));
   pl->workspace_bytes = S > 1 ? (int64_t)(S * M * N * 4 + NB * 4) : 0;
   return W4A16_OK;
 }
@@ -297,6 +300,7 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, DeviceState* 
   if (pl.route == W4A16_ROUTE_NONE) return W4A16_OK;
   if (pl.route == W4A16_ROUTE_DECODE) {
     DecodeParams p{};
+    p.dq = dq_consts(g.dtype);
     p.a = (const uint16_t*)g.a;
     p.bq = (const uint32_t*)g.b_q;
     p.sc = (const uint16_t*)g.scales;
@@ -310,6 +314,7 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, DeviceState* 
     p.KS = (int32_t)ceil_div(g.K, kStepRows);
     p.SG = ((int64_t)g.G == g.K) ? p.KS : g.G / kStepRows;
     p.sg_shift = ((int64_t)g.G == g.K) ? -1 : (g.G == 32 ? 0 : g.G == 64 ? 1 : 2);
+    p.ng_max = decode_ng_max(g.K, g.G, pl.steps_per_wave);
     p.L = pl.steps_per_wave;
     p.S = pl.splits;
     p.NB = (int32_t)ceil_div(g.N, kDecodeCols);
@@ -324,6 +329,7 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, DeviceState* 
                       stream);
   } else {
     PrefillParams p{};
+    p.dq = dq_consts(g.dtype);
     p.a = (const uint16_t*)g.a;
     p.bq = (const uint32_t*)g.b_q;
     p.sc = (const uint16_t*)g.scales;
@@ -425,9 +431,9 @@ w4a16_status w4a16_dequant(const int32_t* b_q, const void* scales, const int32_t
   DeviceState* ds = nullptr;
   st = device_state(&ds);
   if (st != W4A16_OK) return st;
-  w4a16::DequantParams p{(const uint32_t*)b_q, (const uint16_t*)scales, (const uint32_t*)qzeros,
-                         (uint16_t*)w_out,     (int32_t)K,              (int32_t)N,
-                         group_size,           zp_bias};
+  w4a16::DequantParams p{w4a16::dq_consts(dtype), (const uint32_t*)b_q,  (const uint16_t*)scales,
+                         (const uint32_t*)qzeros,   (uint16_t*)w_out,       (int32_t)K,
+                         (int32_t)N,                group_size,             zp_bias};
   hipError_t e = w4a16::launch_dequant(p, dtype, qzeros != nullptr, (hipStream_t)stream);
   if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return W4A16_OK;

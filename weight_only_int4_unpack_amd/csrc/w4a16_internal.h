@@ -17,7 +17,7 @@ constexpr int kDecodeCols = 256;       // output columns per workgroup
 constexpr int kDecodeWaves = 4;        // wavefronts per workgroup
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr int kStepRows = 32;          // K rows per MFMA step
-constexpr int kDecodeMaxSteps = 4;     // most 32-row steps one wavefront loads at once
+constexpr int kDecodeMaxSteps = 8;     // most 32-row steps one wavefront streams
 constexpr int kAutoDecodeMaxM = 16;    // selector: decode for 1 <= M <= this
 
 // ---- prefill route (tiled MFMA)
@@ -28,11 +28,26 @@ constexpr int kPrefillLdsRowHalves = kPrefillBK + 8;  // padded A-tile row
 
 constexpr int kXcds = 8;               // MI355X: workgroups round-robin over 8 XCDs
 
-inline int decode_lds_bytes(int M) {
-  return kDecodeWaves * M * kDecodeCols * (int)sizeof(float);
+// partial sums of the 4 wavefronts, then the staged scales (halves) and
+// packed zero points (words) of at most ng_max groups
+inline int decode_lds_bytes(int M, int ng_max) {
+  return kDecodeWaves * M * kDecodeCols * (int)sizeof(float) + ng_max * kDecodeCols * 2 +
+         ng_max * (kDecodeCols / 8) * 4;
 }
 inline int prefill_lds_bytes(int BM) {
   return 2 * BM * kPrefillLdsRowHalves * 2;
+}
+
+// Constants of the nibble-to-float step, passed as kernel arguments so that
+// the compiler keeps them in registers (see the kernels' dequantisation).
+struct DqConsts {
+  uint32_t magic;  // 0x64006400 (fp16) or 0x43004300 (bf16)
+  uint32_t m_lo;   // 0x000F000F
+  uint32_t m_hi;   // 0x00F000F0
+  uint32_t zero;   // 0: mixed into the magic so that it lives in a vector register
+};
+inline DqConsts dq_consts(int dtype) {
+  return DqConsts{dtype == W4A16_F16 ? 0x64006400u : 0x43004300u, 0x000F000Fu, 0x00F000F0u, 0u};
 }
 
 struct GemmArgs {
@@ -46,6 +61,7 @@ struct GemmArgs {
 };
 
 struct DecodeParams {
+  DqConsts dq;
   const uint16_t* a;
   const uint32_t* bq;
   const uint16_t* sc;
@@ -57,12 +73,14 @@ struct DecodeParams {
   int32_t KS;         // K steps of 32 rows
   int32_t SG;         // steps per group
   int32_t sg_shift;   // log2(SG); -1 when one group spans every step
+  int32_t ng_max;     // most groups one workgroup's steps touch
   int32_t L;          // steps per wavefront
   int32_t S;          // splits across workgroups
   int32_t NB;         // column blocks
 };
 
 struct PrefillParams {
+  DqConsts dq;
   const uint16_t* a;
   const uint32_t* bq;
   const uint16_t* sc;
@@ -73,6 +91,7 @@ struct PrefillParams {
 };
 
 struct DequantParams {
+  DqConsts dq;
   const uint32_t* bq;
   const uint16_t* sc;
   const uint32_t* qz;

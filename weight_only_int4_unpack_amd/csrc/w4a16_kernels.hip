@@ -39,12 +39,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct F16 {
-  static constexpr uint32_t kMagic = 0x64006400u;
+  static constexpr bool kIsF16 = true;
   static constexpr float kBase = 1024.0f;
   static constexpr uint32_t kOnePair = 0x3C003C00u;
 };
 struct BF16 {
-  static constexpr uint32_t kMagic = 0x43004300u;
+  static constexpr bool kIsF16 = false;
   static constexpr float kBase = 128.0f;
   static constexpr uint32_t kOnePair = 0x3F803F80u;
 };
@@ -75,16 +75,30 @@ __device__ __forceinline__ uint16_t narrow(BF16, float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
+// The dequantisation masks and the dtype's magic pattern arrive as kernel
+// arguments (DqConsts, filled by the host), so the compiler cannot fold them:
+// with literal operands it would emit an AND and an OR (a gfx9 VOP3 takes no
+// two literals); with register operands it selects one v_and_or_b32.
+struct DqRegs {
+  uint32_t mag;    // T::kMagic
+  uint32_t m_lo;   // 0x000F000F
+  uint32_t m_hi;   // 0x00F000F0
+};
+// The magic is made per-lane (xor with threadIdx & 0) so that it is held in
+// a vector register: v_and_or_b32 reads at most one scalar operand here.
+__device__ __forceinline__ DqRegs dq_regs(const DqConsts& d) {
+  return DqRegs{d.magic ^ (threadIdx.x & d.zero), d.m_lo, d.m_hi};
+}
+
 // Pair {row r, row r+1} of column e (0..3) of Y as base + q (fp16, e odd:
 // base + 16 q).
 template <typename T, int E>
-__device__ __forceinline__ uint32_t magic_pair(uint32_t y) {
-  if constexpr (sizeof(T) && T::kBase == 1024.0f) {
-    constexpr uint32_t mask = (E & 1) ? 0x00F000F0u : 0x000F000Fu;
+__device__ __forceinline__ uint32_t magic_pair(uint32_t y, const DqRegs& k) {
+  if constexpr (T::kIsF16) {
     const uint32_t src = (E >= 2) ? (y >> 8) : y;
-    return (src & mask) | T::kMagic;
+    return (src & ((E & 1) ? k.m_hi : k.m_lo)) | k.mag;
   } else {
-    return ((y >> (4 * E)) & 0x000F000Fu) | T::kMagic;
+    return ((y >> (4 * E)) & k.m_lo) | k.mag;
   }
 }
 
@@ -128,8 +142,8 @@ __device__ __forceinline__ ColBF16 make_col(BF16, uint32_t s_bits, uint32_t z) {
 }
 
 template <int E>
-__device__ __forceinline__ uint32_t exact_pair(F16, uint32_t y, const ColF16& c) {
-  f16x2 h = __builtin_bit_cast(f16x2, magic_pair<F16, E>(y));
+__device__ __forceinline__ uint32_t exact_pair(F16, uint32_t y, const DqRegs& mag, const ColF16& c) {
+  f16x2 h = __builtin_bit_cast(f16x2, magic_pair<F16, E>(y, mag));
   if constexpr (E & 1) {
     const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
     h = __builtin_elementwise_fma(h, sixteenth, -c.bias);
@@ -140,8 +154,8 @@ __device__ __forceinline__ uint32_t exact_pair(F16, uint32_t y, const ColF16& c)
   return __builtin_bit_cast(uint32_t, h);
 }
 template <int E>
-__device__ __forceinline__ uint32_t exact_pair(BF16, uint32_t y, const ColBF16& c) {
-  const uint32_t p = magic_pair<BF16, E>(y);
+__device__ __forceinline__ uint32_t exact_pair(BF16, uint32_t y, const DqRegs& mag, const ColBF16& c) {
+  const uint32_t p = magic_pair<BF16, E>(y, mag);
   const float lo = __builtin_fmaf(__builtin_bit_cast(float, p << 16), c.scale, c.c);
   const float hi = __builtin_fmaf(__builtin_bit_cast(float, p & 0xFFFF0000u), c.scale, c.c);
   return (uint32_t)narrow(BF16{}, lo) | ((uint32_t)narrow(BF16{}, hi) << 16);
@@ -161,17 +175,20 @@ __device__ __forceinline__ uint32_t join_rows(uint32_t w0, uint32_t w1, int h) {
 
 // ---------------------------------------------------------------------------
 // Decode: M <= 16. A workgroup owns 256 output columns and a contiguous range
-// of 32-row K steps; its 4 wavefronts split the range, L steps each, and a
-// wavefront issues the loads of all its steps before it computes any. Lane
-// (g, c) loads, per step, rows 8g..8g+7 of words 2c, 2c+1 of the block (16
-// columns) and feeds 16 MFMAs (column offset t = 0..15: column 16c + t).
-// Loads never branch: row and column indices are clamped into the arrays;
-// rows past K meet a zero activation and columns past N are never stored.
+// of 4L steps of 32 K-rows; each of its 4 wavefronts streams L of them
+// through a ring of D = min(L, 4) register slots: the loads of D steps are in
+// flight from the start, and each slot is refilled with step j + D as soon as
+// step j has been consumed. Lane (g, c) loads, per step, rows 8g..8g+7 of
+// words 2c, 2c+1 of the block (16 columns) and feeds 16 MFMAs (column offset
+// t = 0..15: column 16c + t). Loads never branch: row and column indices are
+// clamped into the arrays; rows past K meet a zero activation and columns
+// past N are never stored. The scales and zero points of the groups the
+// workgroup touches are staged in LDS once.
 //
 // MODE selects where scale and zero point enter:
 //   kSit:    the MFMA operand is the exact dequantised weight RNE((q-z)s).
-//   kOneGrp: the operand is base + q (exact); all L steps of a wavefront lie
-//            in one group, whose scale and zero point are applied once:
+//   kOneGrp: the operand is base + q (exact); the wavefront's steps lie in
+//            one group, whose scale and zero point are applied once:
 //              sum_k a (q - z) s = s (sum_k a (base + q) - (base + z) sum_k a),
 //            with sum_k a from one extra MFMA against a ones operand.
 //   kMulti:  as kOneGrp, but a wavefront may span groups: each group's
@@ -184,17 +201,19 @@ __device__ __forceinline__ uint32_t join_rows(uint32_t w0, uint32_t w1, int h) {
 // sit dirty in a per-XCD L2, and they are read back with agent-scope loads.
 // ---------------------------------------------------------------------------
 enum { kSit = 0, kOneGrp = 1, kMulti = 2 };
+constexpr int kRing = 4;
 
 template <typename T, int E>
-__device__ __forceinline__ u32x4 magic_op(const uint32_t* y) {
-  return u32x4{magic_pair<T, E>(y[0]), magic_pair<T, E>(y[1]), magic_pair<T, E>(y[2]),
-               magic_pair<T, E>(y[3])};
+__device__ __forceinline__ u32x4 magic_op(const uint32_t* y, const DqRegs& mag) {
+  return u32x4{magic_pair<T, E>(y[0], mag), magic_pair<T, E>(y[1], mag),
+               magic_pair<T, E>(y[2], mag), magic_pair<T, E>(y[3], mag)};
 }
 template <typename T, int E>
-__device__ __forceinline__ u32x4 exact_op(const uint32_t* y, uint32_t s_bits, uint32_t z) {
+__device__ __forceinline__ u32x4 exact_op(const uint32_t* y, const DqRegs& mag, uint32_t s_bits,
+                                          uint32_t z) {
   const auto cc = make_col<E>(T{}, s_bits, z);
-  return u32x4{exact_pair<E>(T{}, y[0], cc), exact_pair<E>(T{}, y[1], cc),
-               exact_pair<E>(T{}, y[2], cc), exact_pair<E>(T{}, y[3], cc)};
+  return u32x4{exact_pair<E>(T{}, y[0], mag, cc), exact_pair<E>(T{}, y[1], mag, cc),
+               exact_pair<E>(T{}, y[2], mag, cc), exact_pair<E>(T{}, y[3], mag, cc)};
 }
 
 __device__ __forceinline__ uint32_t half_of(const u32x4 (&sv)[2], int t) {
@@ -202,10 +221,18 @@ __device__ __forceinline__ uint32_t half_of(const u32x4 (&sv)[2], int t) {
   return (t & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
+// One ring slot: the packed weights (8 rows x 2 words) and the activation
+// operand of one 32-row step.
+struct DecodeSlot {
+  u32x2 w[8];
+  u32x4 a;
+};
+
 // MT: M rounded up to 4, 8 or 16 (compile-time row count of the reductions).
 template <typename T, bool HAS_ZP, int MODE, bool ALIGNED, int L, int MT>
 __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams p) {
-  extern __shared__ float red[];
+  constexpr int D = L < kRing ? L : kRing;
+  extern __shared__ __attribute__((aligned(16))) float red[];
   __shared__ int last_flag;
 
   const int tid = threadIdx.x;
@@ -216,18 +243,87 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
   const int b = blockIdx.x % p.NB;
   const int s = blockIdx.x / p.NB;
   const int N8 = p.N >> 3;
+  const int M = p.M;
   const int word0 = b * (kDecodeCols / 8) + 2 * c;
-  const int col0 = word0 * 8;
   // clamped indices: every load below is in bounds without a branch
   const int wc0 = min(word0, N8 - 1);
   const int wc1 = min(word0 + 1, N8 - 1);
   const int wcv = ALIGNED ? min(word0, N8 - 2) : 0;  // 8-byte aligned pair
-  const int colv = ALIGNED ? min(col0, p.N - 16) : 0;
-  const int mrow = min(c, p.M - 1);
-  const bool a_live = c < p.M;
+  const int mrow = min(c, M - 1);
+  const bool a_live = c < M;
+  const uint16_t* arow = p.a + (int64_t)mrow * p.K;
+  const DqRegs mag = dq_regs(p.dq);
 
-  const int step_beg = (s * kDecodeWaves + wave) * L;
+  const int wg_beg = s * kDecodeWaves * L;
+  const int wg_last = min(wg_beg + kDecodeWaves * L, p.KS) - 1;
+  const int step_beg = wg_beg + wave * L;
   const int nsteps = max(0, min(L, p.KS - step_beg));
+  auto group_of = [&](int st) { return p.sg_shift < 0 ? 0 : (st >> p.sg_shift); };
+  const int g_lo = group_of(wg_beg);
+  const int ngroups = group_of(wg_last) - g_lo + 1;
+
+  // LDS: red[4][M][256] floats | scales[ng_max][256] halves | zeros[ng_max][32] words
+  uint16_t* lds_sc = (uint16_t*)(red + kDecodeWaves * M * kDecodeCols);
+  uint32_t* lds_z = (uint32_t*)(lds_sc + p.ng_max * kDecodeCols);
+
+  // ---- ring prologue: the first D steps' loads
+  auto issue = [&](int j, DecodeSlot& sl) {
+    const int st = min(step_beg + j, p.KS - 1);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int row = min(st * kStepRows + 8 * g + r, p.K - 1);
+      const uint32_t* src = p.bq + (int64_t)row * N8;
+      if constexpr (ALIGNED) {
+        sl.w[r] = *(const u32x2*)(src + wcv);
+      } else {
+        sl.w[r] = u32x2{src[wc0], src[wc1]};
+      }
+    }
+    const int k = st * kStepRows + 8 * g;
+    if constexpr (ALIGNED) {  // K % 8 == 0: a whole 8-element piece or none
+      const bool live = a_live && k < p.K;
+      sl.a = *(const u32x4*)(live ? (const void*)(arow + k) : (const void*)kZeroBlock);
+    } else {
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool live = a_live && k + e < p.K;
+        h[e] = *(live ? arow + k + e : (const uint16_t*)kZeroBlock);
+      }
+      sl.a = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                   h[6] | (h[7] << 16)};
+    }
+  };
+  DecodeSlot ring[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) issue(j, ring[j]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- stage this workgroup's scales and zero points in LDS
+  {
+    const int colc = min(b * kDecodeCols + tid, p.N - 1);
+    for (int gi = 0; gi < ngroups; ++gi)
+      lds_sc[gi * kDecodeCols + tid] = p.sc[(int64_t)(g_lo + gi) * p.N + colc];
+    if constexpr (HAS_ZP) {
+      for (int i = tid; i < ngroups * 32; i += kDecodeThreads) {
+        const int gi = i >> 5, wi = min(b * 32 + (i & 31), N8 - 1);
+        lds_z[i] = p.qz[(int64_t)(g_lo + gi) * N8 + wi];
+      }
+    }
+  }
+  __syncthreads();
+  auto lds_scales = [&](int st, u32x4 (&sv)[2], u32x2& zv) {
+    const int gi = group_of(st) - g_lo;
+    const uint16_t* sp = lds_sc + gi * kDecodeCols + 16 * c;
+    sv[0] = *(const u32x4*)sp;
+    sv[1] = *(const u32x4*)(sp + 8);
+    if constexpr (HAS_ZP) {
+      zv = *(const u32x2*)(lds_z + gi * 32 + 2 * c);
+    } else {
+      const uint32_t zb = (uint32_t)p.zp_bias * 0x11111111u;
+      zv = u32x2{zb, zb};
+    }
+  };
 
   f32x4 acc[16];
   f32x4 R[16];
@@ -239,143 +335,83 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
   }
   const u32x4 ones = u32x4{T::kOnePair, T::kOnePair, T::kOnePair, T::kOnePair};
 
-  // ---- issue the loads of all L steps. No load is predicated and no
-  // loaded register is overwritten before use (either would make the
-  // compiler wait for the load): steps past the range read clamped
-  // addresses and are skipped at compute time; activation rows past M or K
-  // read from a block of zeros instead.
-  u32x2 W[L][8];
-  u32x4 Aop[L];
-  u32x4 Sv[MODE == kOneGrp ? 1 : L][2];
-  u32x2 Zv[MODE == kOneGrp ? 1 : L];
-  const uint16_t* arow = p.a + (int64_t)mrow * p.K;
+  // ---- stream the steps
 #pragma unroll
   for (int j = 0; j < L; ++j) {
-    const int st = min(step_beg + j, p.KS - 1);
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int row = min(st * kStepRows + 8 * g + r, p.K - 1);
-      const uint32_t* src = p.bq + (int64_t)row * N8;
-      if constexpr (ALIGNED) {
-        W[j][r] = *(const u32x2*)(src + wcv);
-      } else {
-        W[j][r] = u32x2{src[wc0], src[wc1]};
-      }
-    }
-    const int k = st * kStepRows + 8 * g;
-    if constexpr (ALIGNED) {  // K % 8 == 0: a whole 8-element piece or none
-      const bool live = a_live && k < p.K;
-      Aop[j] = *(const u32x4*)(live ? (const void*)(arow + k) : (const void*)kZeroBlock);
-    } else {
-      uint32_t h[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const bool live = a_live && k + e < p.K;
-        h[e] = *(live ? arow + k + e : (const uint16_t*)kZeroBlock);
-      }
-      Aop[j] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                     h[6] | (h[7] << 16)};
-    }
-    if (MODE != kOneGrp || j == 0) {
-      const int jj = MODE == kOneGrp ? 0 : j;
-      const int grp = p.sg_shift < 0 ? 0 : (st >> p.sg_shift);
-      const uint16_t* sp = p.sc + (int64_t)grp * p.N;
-      if constexpr (ALIGNED) {
-        Sv[jj][0] = *(const u32x4*)(sp + colv);
-        Sv[jj][1] = *(const u32x4*)(sp + colv + 8);
-      } else {
-        uint32_t h[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) h[e] = sp[min(col0 + e, p.N - 1)];
-        Sv[jj][0] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                          h[6] | (h[7] << 16)};
-        Sv[jj][1] = u32x4{h[8] | (h[9] << 16), h[10] | (h[11] << 16), h[12] | (h[13] << 16),
-                          h[14] | (h[15] << 16)};
-      }
-      if constexpr (HAS_ZP) {
-        const uint32_t* zp = p.qz + (int64_t)grp * N8;
-        if constexpr (ALIGNED) {
-          Zv[jj] = *(const u32x2*)(zp + wcv);
-        } else {
-          Zv[jj] = u32x2{zp[wc0], zp[wc1]};
-        }
-      } else {
-        const uint32_t zb = (uint32_t)p.zp_bias * 0x11111111u;
-        Zv[jj] = u32x2{zb, zb};
-      }
-    }
-  }
-
-  // keep every load above this point: the whole range is in flight before
-  // the first wait
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- compute
-#pragma unroll
-  for (int j = 0; j < L; ++j) {
-    if (j >= nsteps) break;
+    DecodeSlot& sl = ring[j % D];
     const int st = step_beg + j;
-    uint32_t Y[2][2][4];  // [word][half][row pair]
+    if (j < nsteps) {
+      uint32_t Y[2][2][4];  // [word][half][row pair]
 #pragma unroll
-    for (int w = 0; w < 2; ++w)
+      for (int w = 0; w < 2; ++w)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Y[w][h][i] = join_rows(W[j][2 * i][w], W[j][2 * i + 1][w], h);
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const uint32_t* y = Y[t >> 3][(t >> 2) & 1];
+          for (int i = 0; i < 4; ++i) Y[w][h][i] = join_rows(sl.w[2 * i][w], sl.w[2 * i + 1][w], h);
       if constexpr (MODE == kSit) {
-        const uint32_t sb = half_of(Sv[j], t);
-        const uint32_t z = nib(Zv[j][t >> 3], t & 7);
-        u32x4 bop;
-        switch (t & 3) {
-          case 0: bop = exact_op<T, 0>(y, sb, z); break;
-          case 1: bop = exact_op<T, 1>(y, sb, z); break;
-          case 2: bop = exact_op<T, 2>(y, sb, z); break;
-          default: bop = exact_op<T, 3>(y, sb, z); break;
-        }
-        acc[t] = mfma<T>(Aop[j], bop, acc[t]);
-      } else {
-        u32x4 bop;
-        switch (t & 3) {
-          case 0: bop = magic_op<T, 0>(y); break;
-          case 1: bop = magic_op<T, 1>(y); break;
-          case 2: bop = magic_op<T, 2>(y); break;
-          default: bop = magic_op<T, 3>(y); break;
-        }
-        R[t] = mfma<T>(Aop[j], bop, R[t]);
-      }
-    }
-    if constexpr (MODE != kSit) {
-      Rs = mfma<T>(Aop[j], ones, Rs);
-      const bool group_last = p.sg_shift >= 0 && (((st + 1) & ((1 << p.sg_shift) - 1)) == 0);
-      const bool fold = (MODE == kMulti) ? (group_last || (j + 1 == nsteps)) : (j + 1 == nsteps);
-      if (fold) {
-        const int jj = MODE == kOneGrp ? 0 : j;
+        u32x4 sv[2];
+        u32x2 zv;
+        lds_scales(st, sv, zv);
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-          const bool odd16 = (T::kBase == 1024.0f) && (t & 1);
-          const float sc = widen(T{}, half_of(Sv[jj], t)) * (odd16 ? 0.0625f : 1.0f);
-          const float bias = T::kBase + (float)nib(Zv[jj][t >> 3], t & 7) * (odd16 ? 16.0f : 1.0f);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float part = __builtin_fmaf(-bias, Rs[v], R[t][v]);
-            if constexpr (MODE == kMulti) {
-              acc[t][v] = __builtin_fmaf(sc, part, acc[t][v]);
-            } else {
-              acc[t][v] = sc * part;
-            }
+          const uint32_t* y = Y[t >> 3][(t >> 2) & 1];
+          const uint32_t sb = half_of(sv, t);
+          const uint32_t z = nib(zv[t >> 3], t & 7);
+          u32x4 bop;
+          switch (t & 3) {
+            case 0: bop = exact_op<T, 0>(y, mag, sb, z); break;
+            case 1: bop = exact_op<T, 1>(y, mag, sb, z); break;
+            case 2: bop = exact_op<T, 2>(y, mag, sb, z); break;
+            default: bop = exact_op<T, 3>(y, mag, sb, z); break;
           }
-          if constexpr (MODE == kMulti) R[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          acc[t] = mfma<T>(sl.a, bop, acc[t]);
         }
-        if constexpr (MODE == kMulti) Rs = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const uint32_t* y = Y[t >> 3][(t >> 2) & 1];
+          u32x4 bop;
+          switch (t & 3) {
+            case 0: bop = magic_op<T, 0>(y, mag); break;
+            case 1: bop = magic_op<T, 1>(y, mag); break;
+            case 2: bop = magic_op<T, 2>(y, mag); break;
+            default: bop = magic_op<T, 3>(y, mag); break;
+          }
+          R[t] = mfma<T>(sl.a, bop, R[t]);
+        }
+        Rs = mfma<T>(sl.a, ones, Rs);
+        const bool group_last =
+            p.sg_shift >= 0 && (((st + 1) & ((1 << p.sg_shift) - 1)) == 0);
+        const bool fold = (MODE == kMulti) ? (group_last || (j + 1 == nsteps)) : (j + 1 == nsteps);
+        if (fold) {
+          u32x4 sv[2];
+          u32x2 zv;
+          lds_scales(st, sv, zv);
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            const bool odd16 = T::kIsF16 && (t & 1);
+            const float sc = widen(T{}, half_of(sv, t)) * (odd16 ? 0.0625f : 1.0f);
+            const float bias = T::kBase + (float)nib(zv[t >> 3], t & 7) * (odd16 ? 16.0f : 1.0f);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float part = __builtin_fmaf(-bias, Rs[v], R[t][v]);
+              if constexpr (MODE == kMulti) {
+                acc[t][v] = __builtin_fmaf(sc, part, acc[t][v]);
+              } else {
+                acc[t][v] = sc * part;
+              }
+            }
+            if constexpr (MODE == kMulti) R[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+          if constexpr (MODE == kMulti) Rs = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
       }
     }
+    if (j + D < L) issue(j + D, sl);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- the 4 wavefronts' partials meet in LDS: red[wave][m][256]
-  const int M = p.M;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int m = 4 * g + v;
@@ -561,6 +597,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
     }
   };
 
+  const DqRegs mag = dq_regs(p.dq);
   u32x4 a_next[BM / 32];
   BStep b_cur[2], b_next[2];
   load_a(0, a_next);
@@ -589,14 +626,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
         auto c1 = make_col<1>(T{}, bs.s.x >> 16, nib(bs.z, 1));
         auto c2 = make_col<2>(T{}, bs.s.y & 0xFFFFu, nib(bs.z, 2));
         auto c3 = make_col<3>(T{}, bs.s.y >> 16, nib(bs.z, 3));
-        bop[0] = u32x4{exact_pair<0>(T{}, Y[0], c0), exact_pair<0>(T{}, Y[1], c0),
-                       exact_pair<0>(T{}, Y[2], c0), exact_pair<0>(T{}, Y[3], c0)};
-        bop[1] = u32x4{exact_pair<1>(T{}, Y[0], c1), exact_pair<1>(T{}, Y[1], c1),
-                       exact_pair<1>(T{}, Y[2], c1), exact_pair<1>(T{}, Y[3], c1)};
-        bop[2] = u32x4{exact_pair<2>(T{}, Y[0], c2), exact_pair<2>(T{}, Y[1], c2),
-                       exact_pair<2>(T{}, Y[2], c2), exact_pair<2>(T{}, Y[3], c2)};
-        bop[3] = u32x4{exact_pair<3>(T{}, Y[0], c3), exact_pair<3>(T{}, Y[1], c3),
-                       exact_pair<3>(T{}, Y[2], c3), exact_pair<3>(T{}, Y[3], c3)};
+        bop[0] = u32x4{exact_pair<0>(T{}, Y[0], mag, c0), exact_pair<0>(T{}, Y[1], mag, c0),
+                       exact_pair<0>(T{}, Y[2], mag, c0), exact_pair<0>(T{}, Y[3], mag, c0)};
+        bop[1] = u32x4{exact_pair<1>(T{}, Y[0], mag, c1), exact_pair<1>(T{}, Y[1], mag, c1),
+                       exact_pair<1>(T{}, Y[2], mag, c1), exact_pair<1>(T{}, Y[3], mag, c1)};
+        bop[2] = u32x4{exact_pair<2>(T{}, Y[0], mag, c2), exact_pair<2>(T{}, Y[1], mag, c2),
+                       exact_pair<2>(T{}, Y[2], mag, c2), exact_pair<2>(T{}, Y[3], mag, c2)};
+        bop[3] = u32x4{exact_pair<3>(T{}, Y[0], mag, c3), exact_pair<3>(T{}, Y[1], mag, c3),
+                       exact_pair<3>(T{}, Y[2], mag, c3), exact_pair<3>(T{}, Y[3], mag, c3)};
       }
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
@@ -660,14 +697,15 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
   const uint16_t* sp = p.sc + (int64_t)grp * p.N + wc * 8;
   uint16_t* o0 = p.w + (int64_t)r0 * p.N + wc * 8;
   uint16_t* o1 = o0 + p.N;
+  const DqRegs mag = dq_regs(p.dq);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const uint32_t y = join_rows(w0, w1, h);
     uint32_t pr[4];
-    pr[0] = exact_pair<0>(T{}, y, make_col<0>(T{}, sp[4 * h + 0], nib(zw, 4 * h + 0)));
-    pr[1] = exact_pair<1>(T{}, y, make_col<1>(T{}, sp[4 * h + 1], nib(zw, 4 * h + 1)));
-    pr[2] = exact_pair<2>(T{}, y, make_col<2>(T{}, sp[4 * h + 2], nib(zw, 4 * h + 2)));
-    pr[3] = exact_pair<3>(T{}, y, make_col<3>(T{}, sp[4 * h + 3], nib(zw, 4 * h + 3)));
+    pr[0] = exact_pair<0>(T{}, y, mag, make_col<0>(T{}, sp[4 * h + 0], nib(zw, 4 * h + 0)));
+    pr[1] = exact_pair<1>(T{}, y, mag, make_col<1>(T{}, sp[4 * h + 1], nib(zw, 4 * h + 1)));
+    pr[2] = exact_pair<2>(T{}, y, mag, make_col<2>(T{}, sp[4 * h + 2], nib(zw, 4 * h + 2)));
+    pr[3] = exact_pair<3>(T{}, y, mag, make_col<3>(T{}, sp[4 * h + 3], nib(zw, 4 * h + 3)));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       o0[4 * h + e] = (uint16_t)(pr[e] & 0xFFFFu);
@@ -683,6 +721,12 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
 // ---------------------------------------------------------------------------
 template <typename T, bool Z, int MODE, bool AL, int L, int MT>
 static hipError_t decode_go(const DecodeParams& p, int grid, int lds, hipStream_t st) {
+  if (lds > 65536) {  // above the default dynamic LDS limit: raise it once
+    static const hipError_t once = hipFuncSetAttribute(
+        (const void*)decode_kernel<T, Z, MODE, AL, L, MT>,
+        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 64);
+    if (once != hipSuccess) return once;
+  }
   hipLaunchKernelGGL((decode_kernel<T, Z, MODE, AL, L, MT>), dim3(grid), dim3(kDecodeThreads),
                      lds, st, p);
   return hipGetLastError();
@@ -704,6 +748,7 @@ static hipError_t decode_l(const DecodeParams& p, int grid, int lds, hipStream_t
       case 1: return decode_mt<T, Z, MODE, AL, 1>(p, grid, lds, st);
       case 2: return decode_mt<T, Z, MODE, AL, 2>(p, grid, lds, st);
       case 4: return decode_mt<T, Z, MODE, AL, 4>(p, grid, lds, st);
+      case 8: return decode_mt<T, Z, MODE, AL, 8>(p, grid, lds, st);
       default: return hipErrorInvalidValue;
     }
   }
