@@ -147,15 +147,38 @@ def gemm(a: torch.Tensor, b_q: torch.Tensor, scales: torch.Tensor,
     elif (tuple(out.shape) != (M, N) or out.dtype != a.dtype or out.device != a.device
           or not out.is_contiguous()):
         raise ValueError("out must be a contiguous [M, N] tensor like a")
-    L = lib()
-    with torch.cuda.device(a.device):
-        args = (_ptr(a), _ptr(b_q), _ptr(scales), _ptr(qzeros), group_size, zp_bias,
-                _ptr(out), M, K, N, _DTYPE_CODE[a.dtype])
-        if plan is None:
-            _check(L.w4a16_gemm(*args, _stream(a.device)))
-        else:
-            _check(L.w4a16_gemm_planned(*args, ctypes.byref(plan), _stream(a.device)))
+    args = gemm_args(a, b_q, scales, qzeros, group_size, zp_bias, out)
+    if a.device.index == torch.cuda.current_device():
+        _run_gemm(args, plan)
+    else:
+        with torch.cuda.device(a.device):
+            _run_gemm(args, plan)
     return out
+
+
+def gemm_args(a, b_q, scales, qzeros, group_size, zp_bias, out):
+    """The C-ABI argument tuple of one GEMM (pointers, sizes, dtype, stream),
+    for callers that launch the same problem repeatedly without re-checking
+    shapes; pass it to ``launch``."""
+    M, K = a.shape
+    N = b_q.shape[1] * 8
+    return (_ptr(a), _ptr(b_q), _ptr(scales), _ptr(qzeros), group_size, zp_bias, _ptr(out),
+            M, K, N, _DTYPE_CODE[a.dtype], _stream(a.device))
+
+
+def _run_gemm(args, plan):
+    L = lib()
+    if plan is None:
+        _check(L.w4a16_gemm(*args))
+    else:
+        _check(L.w4a16_gemm_planned(*args[:-1], ctypes.byref(plan), args[-1]))
+
+
+def launch(args) -> None:
+    """Run a tuple made by ``gemm_args`` (on the stream it names)."""
+    st = lib().w4a16_gemm(*args)
+    if st != OK:
+        raise W4A16Error(st, last_error())
 
 
 def dequant(b_q: torch.Tensor, scales: torch.Tensor, qzeros: torch.Tensor | None = None,
