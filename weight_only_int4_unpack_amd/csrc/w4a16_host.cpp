@@ -144,11 +144,7 @@ w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dty
 
 void plan_prefill(int64_t M, int64_t N, w4a16_plan_t* pl) {
   using namespace w4a16;
-  int bm = 256;
-  if (M <= 64)
-    bm = 64;
-  else if (M <= 128)
-    bm = 128;
+  const int bm = kPrefillBM;
   const int64_t tm = ceil_div(M, bm), tn = ceil_div(N, kPrefillBN);
   const int64_t per_xcd = ceil_div(tm * tn, kXcds);
   pl->route = W4A16_ROUTE_PREFILL;
@@ -160,7 +156,7 @@ void plan_prefill(int64_t M, int64_t N, w4a16_plan_t* pl) {
   pl->steps_per_wave = 0;
   pl->grid = (int32_t)(per_xcd * kXcds);
   pl->threads = kPrefillThreads;
-  pl->lds_bytes = prefill_lds_bytes(bm);
+  pl->lds_bytes = prefill_lds_bytes();
   pl->workspace_bytes = 0;
 }
 
@@ -340,10 +336,11 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, DeviceState* 
     p.N = (int32_t)g.N;
     p.G = g.G;
     p.zp_bias = g.zp_bias;
+    p.g_shift = g.G == 32 ? 5 : g.G == 64 ? 6 : g.G == 128 ? 7 : 0;
     p.tiles_m = (int32_t)ceil_div(g.M, pl.block_m);
     p.tiles_n = (int32_t)ceil_div(g.N, kPrefillBN);
     p.per_xcd = pl.grid / kXcds;
-    e = launch_prefill(p, g.dtype, g.qzeros != nullptr, pl.block_m, pl.grid, stream);
+    e = launch_prefill(p, g.dtype, g.qzeros != nullptr, pl.grid, stream);
   }
   if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return W4A16_OK;

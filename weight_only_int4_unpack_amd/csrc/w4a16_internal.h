@@ -21,6 +21,7 @@ constexpr int kDecodeMaxSteps = 8;     // most 32-row steps one wavefront stream
 constexpr int kAutoDecodeMaxM = 16;    // selector: decode for 1 <= M <= this
 
 // ---- prefill route (tiled MFMA)
+constexpr int kPrefillBM = 64;         // rows per workgroup tile
 constexpr int kPrefillBN = 256;        // output columns per workgroup (4 waves x 64)
 constexpr int kPrefillBK = 64;         // K rows per pipeline stage
 constexpr int kPrefillThreads = 256;
@@ -34,8 +35,8 @@ inline int decode_lds_bytes(int M, int ng_max) {
   return kDecodeWaves * M * kDecodeCols * (int)sizeof(float) + ng_max * kDecodeCols * 2 +
          ng_max * (kDecodeCols / 8) * 4;
 }
-inline int prefill_lds_bytes(int BM) {
-  return 2 * BM * kPrefillLdsRowHalves * 2;
+inline int prefill_lds_bytes() {
+  return 2 * kPrefillBM * kPrefillLdsRowHalves * 2;
 }
 
 // Constants of the nibble-to-float step, passed as kernel arguments so that
@@ -87,6 +88,7 @@ struct PrefillParams {
   const uint32_t* qz;
   uint16_t* out;
   int32_t M, K, N, G, zp_bias;
+  int32_t g_shift;    // log2(G) when G is 32, 64 or 128 (unused when G == K)
   int32_t tiles_m, tiles_n, per_xcd;
 };
 
@@ -101,8 +103,7 @@ struct DequantParams {
 
 hipError_t launch_decode(const DecodeParams& p, int dtype, bool has_zp, int mode,
                          int grid, int lds_bytes, hipStream_t stream);
-hipError_t launch_prefill(const PrefillParams& p, int dtype, bool has_zp,
-                          int block_m, int grid, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, int dtype, bool has_zp, int grid, hipStream_t stream);
 hipError_t launch_dequant(const DequantParams& p, int dtype, bool has_zp,
                           hipStream_t stream);
 

@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "w4a16_internal.h"
 
 namespace w4a16 {
@@ -153,12 +155,15 @@ __device__ __forceinline__ uint32_t exact_pair(F16, uint32_t y, const DqRegs& ma
   h = h * c.scale;
   return __builtin_bit_cast(uint32_t, h);
 }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 template <int E>
 __device__ __forceinline__ uint32_t exact_pair(BF16, uint32_t y, const DqRegs& mag, const ColBF16& c) {
   const uint32_t p = magic_pair<BF16, E>(y, mag);
-  const float lo = __builtin_fmaf(__builtin_bit_cast(float, p << 16), c.scale, c.c);
-  const float hi = __builtin_fmaf(__builtin_bit_cast(float, p & 0xFFFF0000u), c.scale, c.c);
-  return (uint32_t)narrow(BF16{}, lo) | ((uint32_t)narrow(BF16{}, hi) << 16);
+  const f32x2 v = {__builtin_fmaf(__builtin_bit_cast(float, p << 16), c.scale, c.c),
+                   __builtin_fmaf(__builtin_bit_cast(float, p & 0xFFFF0000u), c.scale, c.c)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));  // one RNE each
 }
 
 __device__ __forceinline__ uint32_t nib(uint32_t w, int j) { return (w >> (4 * j)) & 0xFu; }
@@ -499,22 +504,48 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
     __hip_atomic_store(&p.counters[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A load from a wave-uniform base plus a per-lane 32-bit byte offset (lets
+// the compiler use the scalar-base form of the global load).
+template <typename V>
+__device__ __forceinline__ V ldg(const char* base, uint32_t off) {
+  return *(const V*)(base + off);
+}
+
 // ---------------------------------------------------------------------------
-// Prefill: workgroup tile BM x 256, K staged 64 rows at a time. The A tile
-// goes through LDS (double-buffered) and is read by all 4 wavefronts; each
-// wavefront owns 64 output columns and dequantises exactly the weights it
-// multiplies, straight into MFMA operands: lane (g, c) reads, per 32-row
-// step, rows 8g..8g+7 of columns 4c..4c+3 of its 64 (one 16-bit piece of a
-// packed word per row) and forms four operands (column 4c + t, t = 0..3).
-// Workgroup ids are spread so that the tiles of one XCD share A rows.
+// Prefill: workgroup tile 64 x 256, K staged 64 rows (two 32-row slabs) at a
+// time. The A tile goes through LDS (double-buffered) and is read by all 4
+// wavefronts; each wavefront owns 64 output columns and turns exactly the
+// weights it multiplies into MFMA operands: lane (g, c) reads, per slab,
+// rows 8g..8g+7 of columns 4c..4c+3 of its 64 (one 16-bit piece of a packed
+// word per row, two rows per register) and forms four operands (column
+// 4c + e, e = 0..3).
+//
+// Numerics (factored, as in the decode kernel's grouped modes): the operand
+// is the exact integer base + q (fp16, e odd: 1024 + 16q); one more MFMA
+// against a ones operand gives each row's activation sum over the slab. For
+// each group, in fp32,
+//     sum_k a (q - z) s = s' (part - (base + z') sum_k a),
+// with part = sum_k a (base + q) and s' = s, z' = z (fp16 e odd: s/16, 16z),
+// folded into the output accumulator at the group's last slab. No weight is
+// rounded to fp16/bf16: the products are exact and only fp32 sums round.
+// GS = G / 32 slabs per group (1, 2 or 4); GS = 0: one group spans all of K
+// and the fold is done once, on the output accumulator, at the end.
+//
+// Loads never branch: rows and columns are clamped into the arrays, rows past
+// M are computed and not stored, activation columns past K read a zero block.
+// The K loop is unrolled twice so the two weight buffers swap roles without
+// copies (a group of 4 slabs is exactly one unrolled body). Workgroup ids are
+// spread so that the tiles of one XCD share A rows. Two workgroups fit a CU.
+// KM = 0: K % 64 == 0 and no load is checked against K. KM = 1, 2: the
+// stage that holds row K - 1 clamps weight rows and reads a zero block past
+// K; activations load in 16-byte pieces (KM = 1, K % 8 == 0) or one at a time.
 // ---------------------------------------------------------------------------
-// PC (one group spanning all of K): the operand is the exact integer q - z
-// and each output column is multiplied by its scale once, in fp32, at the
-// end; no weight is rounded before the product.
-template <typename T, bool HAS_ZP, bool PC, int BM>
-__global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams p) {
+template <typename T, bool HAS_ZP, int GS, int KM>
+__global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillParams p) {
+  constexpr int BM = kPrefillBM;
   constexpr int RH = kPrefillLdsRowHalves;
   constexpr int MB = BM / 16;
+  constexpr int AP = BM / 32;  // 16-byte A pieces per thread per stage
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * RH];
 
   const int tid = threadIdx.x;
@@ -530,136 +561,217 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
   const int tn = tile % p.tiles_n;
   const int m0 = tm * BM;
   const int ncol = tn * kPrefillBN + wave * 64 + 4 * c;  // this lane's 4 columns
-  const bool ncol_ok = ncol < p.N;
+  const int ncolc = min(ncol, p.N - 4);
   const int N4 = p.N >> 2;  // 16-bit pieces per weight row
-  const uint16_t* bq16 = (const uint16_t*)p.bq;
-  const uint16_t* qz16 = (const uint16_t*)p.qz;
+  const uint16_t* bq16 = (const uint16_t*)p.bq + (ncolc >> 2);
   const int KT = (p.K + kPrefillBK - 1) / kPrefillBK;
-  const bool a_vec = (p.K & 7) == 0;
+  const DqRegs mag = dq_regs(p.dq);
+  const u32x4 ones = u32x4{T::kOnePair, T::kOnePair, T::kOnePair, T::kOnePair};
+  const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  f32x4 acc[MB][4];
+  f32x4 acc[MB][4];   // output accumulator
+  f32x4 part[MB][4];  // current group's sum of a (base + q)   (GS > 0)
+  f32x4 asum[MB];     // current group's (GS = 0: all of K's) sum of a
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
+  for (int i = 0; i < MB; ++i) {
+    asum[i] = zero4;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 4; ++t) acc[i][t] = zero4;
+  }
 
-  // ---- loaders
-  auto load_a = [&](int kt, u32x4 (&ar)[BM / 32]) {
+  // ---- loaders. Full stages (all 64 rows inside K) address every load as a
+  // wave-uniform base plus one per-lane 32-bit byte offset; the last stage,
+  // when K % 64 != 0, clamps weight rows and reads a zero block past K.
+  // Rows past M are clamped to M - 1 once, in the per-lane offsets.
+  uint32_t a_off[AP];
 #pragma unroll
-    for (int j = 0; j < BM / 32; ++j) {
-      const int row = j * 32 + (tid >> 3);
-      const int k = kt * kPrefillBK + (tid & 7) * 8;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (m0 + row < p.M) {
-        const uint16_t* src = p.a + (int64_t)(m0 + row) * p.K + k;
-        if (a_vec && k + 8 <= p.K) {
-          v = *(const u32x4*)src;
+  for (int j = 0; j < AP; ++j)
+    a_off[j] = (uint32_t)(((min(m0 + j * 32 + (tid >> 3), p.M - 1) - m0) * p.K + (tid & 7) * 8) * 2);
+  const char* a_base = (const char*)(p.a + (int64_t)m0 * p.K);
+  const uint32_t b_off = (uint32_t)((8 * g * N4 + (ncolc >> 2)) * 2);
+  const uint32_t s_off = (uint32_t)(ncolc * 2);
+  const uint32_t z_off = (uint32_t)((ncolc >> 2) * 2);
+  const int KF = p.K / kPrefillBK;  // full stages
+
+  auto load_a = [&](int kt, u32x4 (&ar)[AP]) {
+    if (KM == 0 || kt < KF) {
+#pragma unroll
+      for (int j = 0; j < AP; ++j) ar[j] = ldg<u32x4>(a_base + kt * (kPrefillBK * 2), a_off[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < AP; ++j) {
+        const int row = min(m0 + j * 32 + (tid >> 3), p.M - 1);
+        const int k = kt * kPrefillBK + (tid & 7) * 8;
+        const uint16_t* arow = p.a + (int64_t)row * p.K;
+        if constexpr (KM == 1) {
+          ar[j] = *(const u32x4*)(k < p.K ? (const void*)(arow + k) : (const void*)kZeroBlock);
         } else {
           uint32_t h[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) h[e] = (k + e < p.K) ? (uint32_t)src[e] : 0u;
-          v = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                    h[6] | (h[7] << 16)};
+          for (int e = 0; e < 8; ++e)
+            h[e] = *(k + e < p.K ? arow + k + e : (const uint16_t*)kZeroBlock);
+          ar[j] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                        h[6] | (h[7] << 16)};
         }
       }
-      ar[j] = v;
     }
   };
-  auto store_a = [&](int buf, const u32x4 (&ar)[BM / 32]) {
+  auto store_a = [&](int buf, const u32x4 (&ar)[AP]) {
 #pragma unroll
-    for (int j = 0; j < BM / 32; ++j) {
+    for (int j = 0; j < AP; ++j) {
       const int row = j * 32 + (tid >> 3);
       *(u32x4*)&As[buf][row * RH + (tid & 7) * 8] = ar[j];
     }
   };
-  // weights of one 32-row step: 8 rows x 16 bits, plus 4 scales and 4 zeros
-  struct BStep {
-    uint32_t q[8];
+  // One slab's weights (rows 8g..8g+7, two rows per register) and, for a
+  // slab that closes a group, that group's 4 scales and packed zero points.
+  struct Slab {
+    u16x2 q[4];
     u32x2 s;
     uint32_t z;
+    bool valid;
   };
-  auto load_b = [&](int k0, BStep& bs) {
+  // POS: slab position within the unrolled body (0..3)
+  auto load_slab = [&](int kt, int half, Slab& sl, auto posc) {
+    constexpr int POS = decltype(posc)::value;
+    constexpr bool closes = GS > 0 && (POS + 1) % (GS > 0 ? GS : 1) == 0;
+    const int k0 = kt * kPrefillBK + 32 * half;
+    if (KM == 0 || kt < KF) {
+      const char* rb = (const char*)p.bq + (int64_t)k0 * (N4 * 2);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int row = k0 + 8 * g + r;
-      bs.q[r] = (row < p.K && ncol_ok) ? (uint32_t)bq16[(int64_t)row * N4 + (ncol >> 2)] : 0u;
-    }
-    const int grp = PC ? 0 : min(k0, p.K - 1) / p.G;
-    if constexpr (PC) {
-      bs.s = u32x2{T::kOnePair, T::kOnePair};
+      for (int r = 0; r < 4; ++r)
+        sl.q[r] = u16x2{ldg<uint16_t>(rb + (int64_t)(2 * r) * (N4 * 2), b_off),
+                        ldg<uint16_t>(rb + (int64_t)(2 * r + 1) * (N4 * 2), b_off)};
     } else {
-      bs.s = ncol_ok ? *(const u32x2*)(p.sc + (int64_t)grp * p.N + ncol) : u32x2{0u, 0u};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int r0 = min(k0 + 8 * g + 2 * r, p.K - 1);
+        const int r1 = min(k0 + 8 * g + 2 * r + 1, p.K - 1);
+        sl.q[r] = u16x2{bq16[(int64_t)r0 * N4], bq16[(int64_t)r1 * N4]};
+      }
     }
-    if constexpr (HAS_ZP) {
-      bs.z = ncol_ok ? (uint32_t)qz16[(int64_t)grp * N4 + (ncol >> 2)] : 0u;
-    } else {
-      bs.z = (uint32_t)p.zp_bias * 0x1111u;
+    if constexpr (closes) {
+      const int grp = min(k0, p.K - 1) >> p.g_shift;
+      sl.s = ldg<u32x2>((const char*)p.sc + (int64_t)grp * p.N * 2, s_off);
+      if constexpr (HAS_ZP) sl.z = ldg<uint16_t>((const char*)p.qz + (int64_t)grp * N4 * 2, z_off);
+      sl.valid = KM == 0 || k0 < p.K;
     }
   };
+  // Fold a group's partial into the output accumulator, row blocks
+  // [I0, I1) (scales s_bits of the lane's 4 columns, their packed zero
+  // points z4). GS = 0: acc holds the partial itself.
+  auto col_consts = [&](u32x2 s_bits, uint32_t z4, bool valid, float (&sc)[4], float (&bias)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t sb = (e < 2 ? s_bits.x : s_bits.y) >> (16 * (e & 1));
+      const float z = (float)(HAS_ZP ? nib(z4, e) : (uint32_t)p.zp_bias);
+      const bool odd16 = T::kIsF16 && (e & 1);
+      sc[e] = valid ? widen(T{}, sb & 0xFFFFu) * (odd16 ? 0.0625f : 1.0f) : 0.f;
+      bias[e] = T::kBase + z * (odd16 ? 16.0f : 1.0f);
+    }
+  };
+  auto fold_block = [&](const float (&sc)[4], const float (&bias)[4], const f32x4& as,
+                        const f32x4 (&src)[4], f32x4 (&dst)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float d = __builtin_fmaf(-bias[e], as[v], src[e][v]);
+        dst[e][v] = GS > 0 ? __builtin_fmaf(sc[e], d, dst[e][v]) : sc[e] * d;
+      }
+  };
+  // The MFMAs of one slab (LDS buffer `buf`, 32-row half `ks`). With one
+  // slab per group (GS = 1) each row block is folded right after its MFMAs,
+  // so only one row block's partials are live.
+  auto slab = [&](int buf, int ks, const Slab& sl, auto posc) {
+    constexpr int POS = decltype(posc)::value;
+    constexpr bool opens = GS > 0 && POS % (GS > 0 ? GS : 1) == 0;
+    constexpr bool closes = GS > 0 && (POS + 1) % (GS > 0 ? GS : 1) == 0;
+    uint32_t Y[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Y[r] = __builtin_bit_cast(uint32_t, sl.q[r]);
+    u32x4 bop[4];
+    bop[0] = magic_op<T, 0>(Y, mag);
+    bop[1] = magic_op<T, 1>(Y, mag);
+    bop[2] = magic_op<T, 2>(Y, mag);
+    bop[3] = magic_op<T, 3>(Y, mag);
+    float sc[4], bias[4];
+    if constexpr (closes) col_consts(sl.s, HAS_ZP ? sl.z : 0u, sl.valid, sc, bias);
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const u32x4 aop = *(const u32x4*)&As[buf][(i * 16 + c) * RH + ks * 32 + 8 * g];
+      if constexpr (GS == 1) {
+        const f32x4 as = mfma<T>(aop, ones, zero4);
+        f32x4 pt[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pt[e] = mfma<T>(aop, bop[e], zero4);
+        fold_block(sc, bias, as, pt, acc[i]);
+      } else {
+        asum[i] = mfma<T>(aop, ones, opens ? zero4 : asum[i]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (GS > 0)
+            part[i][e] = mfma<T>(aop, bop[e], opens ? zero4 : part[i][e]);
+          else
+            acc[i][e] = mfma<T>(aop, bop[e], acc[i][e]);
+        }
+      }
+    }
+    if constexpr (closes && GS > 1) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) fold_block(sc, bias, asum[i], part[i], acc[i]);
+    }
+  };
+  // One stage (P: 0 or 1 within the unrolled body; LD: stage kt+1 exists):
+  // prefetch stage kt+1 (A to registers, weights to `nxt`), compute stage
+  // kt, publish the A tile.
+  u32x4 a_next[AP];
+  auto stage = [&](int kt, const Slab (&cur)[2], Slab (&nxt)[2], auto pc, auto ldc) {
+    constexpr int P = decltype(pc)::value;
+    constexpr bool LD = decltype(ldc)::value;
+    const int buf = kt & 1;
+    if constexpr (LD) {
+      load_a(kt + 1, a_next);
+      load_slab(kt + 1, 0, nxt[0], std::integral_constant<int, 2 * (1 - P)>{});
+      load_slab(kt + 1, 1, nxt[1], std::integral_constant<int, 2 * (1 - P) + 1>{});
+    }
+    slab(buf, 0, cur[0], std::integral_constant<int, 2 * P>{});
+    slab(buf, 1, cur[1], std::integral_constant<int, 2 * P + 1>{});
+    if constexpr (LD) store_a(buf ^ 1, a_next);
+    __syncthreads();
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using Yes = std::true_type;
+  using No = std::false_type;
 
-  const DqRegs mag = dq_regs(p.dq);
-  u32x4 a_next[BM / 32];
-  BStep b_cur[2], b_next[2];
+  Slab B0[2], B1[2];
   load_a(0, a_next);
-  load_b(0, b_cur[0]);
-  load_b(32, b_cur[1]);
+  load_slab(0, 0, B0[0], C0{});
+  load_slab(0, 1, B0[1], C1{});
   store_a(0, a_next);
   __syncthreads();
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < KT;
-    if (more) {
-      load_a(kt + 1, a_next);
-      load_b((kt + 1) * kPrefillBK, b_next[0]);
-      load_b((kt + 1) * kPrefillBK + 32, b_next[1]);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const BStep& bs = b_cur[ks];
-      uint32_t Y[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Y[i] = bs.q[2 * i] | (bs.q[2 * i + 1] << 16);
-      u32x4 bop[4];
-      {
-        auto c0 = make_col<0>(T{}, bs.s.x & 0xFFFFu, nib(bs.z, 0));
-        auto c1 = make_col<1>(T{}, bs.s.x >> 16, nib(bs.z, 1));
-        auto c2 = make_col<2>(T{}, bs.s.y & 0xFFFFu, nib(bs.z, 2));
-        auto c3 = make_col<3>(T{}, bs.s.y >> 16, nib(bs.z, 3));
-        bop[0] = u32x4{exact_pair<0>(T{}, Y[0], mag, c0), exact_pair<0>(T{}, Y[1], mag, c0),
-                       exact_pair<0>(T{}, Y[2], mag, c0), exact_pair<0>(T{}, Y[3], mag, c0)};
-        bop[1] = u32x4{exact_pair<1>(T{}, Y[0], mag, c1), exact_pair<1>(T{}, Y[1], mag, c1),
-                       exact_pair<1>(T{}, Y[2], mag, c1), exact_pair<1>(T{}, Y[3], mag, c1)};
-        bop[2] = u32x4{exact_pair<2>(T{}, Y[0], mag, c2), exact_pair<2>(T{}, Y[1], mag, c2),
-                       exact_pair<2>(T{}, Y[2], mag, c2), exact_pair<2>(T{}, Y[3], mag, c2)};
-        bop[3] = u32x4{exact_pair<3>(T{}, Y[0], mag, c3), exact_pair<3>(T{}, Y[1], mag, c3),
-                       exact_pair<3>(T{}, Y[2], mag, c3), exact_pair<3>(T{}, Y[3], mag, c3)};
-      }
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const u32x4 aop = *(const u32x4*)&As[buf][(i * 16 + c) * RH + ks * 32 + 8 * g];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[i][t] = mfma<T>(aop, bop[t], acc[i][t]);
-      }
-    }
-    if (more) {
-      store_a(buf ^ 1, a_next);
-      b_cur[0] = b_next[0];
-      b_cur[1] = b_next[1];
-    }
-    __syncthreads();
+  int kt = 0;
+  for (; kt + 2 < KT; kt += 2) {
+    stage(kt, B0, B1, C0{}, Yes{});
+    stage(kt + 1, B1, B0, C1{}, Yes{});
+  }
+  if (kt + 2 == KT) {
+    stage(kt, B0, B1, C0{}, Yes{});
+    stage(kt + 1, B1, B0, C1{}, No{});
+  } else {
+    stage(kt, B0, B1, C0{}, No{});
   }
 
-  // ---- epilogue: lane holds rows i*16 + 4g + v, columns ncol + t
-  if (!ncol_ok) return;
-  if constexpr (PC) {
+  // ---- epilogue: lane holds rows i*16 + 4g + v, columns ncol + e
+  if (ncol >= p.N) return;
+  if constexpr (GS == 0) {
     const u32x2 sv = *(const u32x2*)(p.sc + ncol);
-    const float sc[4] = {widen(T{}, sv.x & 0xFFFFu), widen(T{}, sv.x >> 16),
-                         widen(T{}, sv.y & 0xFFFFu), widen(T{}, sv.y >> 16)};
+    const uint32_t z4 = HAS_ZP ? ((const uint16_t*)p.qz)[ncol >> 2] : 0u;
+    float sc[4], bias[4];
+    col_consts(sv, z4, true, sc, bias);
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[i][t] *= sc[t];
+    for (int i = 0; i < MB; ++i) fold_block(sc, bias, asum[i], acc[i], acc[i]);
   }
 #pragma unroll
   for (int i = 0; i < MB; ++i)
@@ -776,31 +888,34 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, bool has_zp, int mode
                 : decode_mode<BF16, false>(p, mode, grid, lds, st);
 }
 
-template <typename T, bool Z, bool PC, int BM>
+template <typename T, bool Z, int GS, int KM>
 static hipError_t prefill_go(const PrefillParams& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_kernel<T, Z, PC, BM>), dim3(grid), dim3(kPrefillThreads), 0, st,
-                     p);
+  hipLaunchKernelGGL((prefill_kernel<T, Z, GS, KM>), dim3(grid), dim3(kPrefillThreads), 0, st, p);
   return hipGetLastError();
 }
-template <typename T, bool Z, bool PC>
-static hipError_t prefill_bm(const PrefillParams& p, int bm, int grid, hipStream_t st) {
-  switch (bm) {
-    case 256: return prefill_go<T, Z, PC, 256>(p, grid, st);
-    case 128: return prefill_go<T, Z, PC, 128>(p, grid, st);
-    case 64: return prefill_go<T, Z, PC, 64>(p, grid, st);
+template <typename T, bool Z, int GS>
+static hipError_t prefill_km(const PrefillParams& p, int grid, hipStream_t st) {
+  if (p.K % kPrefillBK == 0) return prefill_go<T, Z, GS, 0>(p, grid, st);
+  if constexpr (GS == 0) {
+    if (p.K % 8 != 0) return prefill_go<T, Z, GS, 2>(p, grid, st);
+  }
+  return prefill_go<T, Z, GS, 1>(p, grid, st);
+}
+template <typename T, bool Z>
+static hipError_t prefill_gs(const PrefillParams& p, int grid, hipStream_t st) {
+  if (p.G == p.K) return prefill_km<T, Z, 0>(p, grid, st);
+  switch (p.G) {
+    case 32: return prefill_km<T, Z, 1>(p, grid, st);
+    case 64: return prefill_km<T, Z, 2>(p, grid, st);
+    case 128: return prefill_km<T, Z, 4>(p, grid, st);
     default: return hipErrorInvalidValue;
   }
 }
-template <typename T, bool Z>
-static hipError_t prefill_pc(const PrefillParams& p, int bm, int grid, hipStream_t st) {
-  return (p.G == p.K) ? prefill_bm<T, Z, true>(p, bm, grid, st)
-                      : prefill_bm<T, Z, false>(p, bm, grid, st);
-}
-hipError_t launch_prefill(const PrefillParams& p, int dtype, bool has_zp, int bm, int grid,
+hipError_t launch_prefill(const PrefillParams& p, int dtype, bool has_zp, int grid,
                           hipStream_t st) {
   if (dtype == W4A16_F16)
-    return has_zp ? prefill_pc<F16, true>(p, bm, grid, st) : prefill_pc<F16, false>(p, bm, grid, st);
-  return has_zp ? prefill_pc<BF16, true>(p, bm, grid, st) : prefill_pc<BF16, false>(p, bm, grid, st);
+    return has_zp ? prefill_gs<F16, true>(p, grid, st) : prefill_gs<F16, false>(p, grid, st);
+  return has_zp ? prefill_gs<BF16, true>(p, grid, st) : prefill_gs<BF16, false>(p, grid, st);
 }
 
 template <typename T, bool Z>
