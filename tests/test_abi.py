@@ -162,7 +162,7 @@ def test_selector_prefill_tiles():
     p = W.plan(2048, 5120, 17408, 128, False, torch.bfloat16)
     assert (p.block_m, p.block_n, p.block_k) == (64, 256, 64)
     assert p.grid % 8 == 0 and p.grid >= 32 * 68
-    assert p.lds_bytes == 2 * 64 * 72 * 2
+    assert p.lds_bytes == 2 * 64 * 80 * 2
     assert W.plan(100, 4096, 4096, 32, True, torch.float16).grid == 2 * 16   # tiles, a multiple of 8
 
 

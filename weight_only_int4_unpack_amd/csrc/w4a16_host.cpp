@@ -340,6 +340,7 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, DeviceState* 
     p.tiles_m = (int32_t)ceil_div(g.M, pl.block_m);
     p.tiles_n = (int32_t)ceil_div(g.N, kPrefillBN);
     p.per_xcd = pl.grid / kXcds;
+    p.band = (int32_t)std::min<int64_t>(kPrefillBand, p.tiles_m);
     e = launch_prefill(p, g.dtype, g.qzeros != nullptr, pl.grid, stream);
   }
   if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

@@ -25,8 +25,9 @@ constexpr int kPrefillBM = 64;         // rows per workgroup tile
 constexpr int kPrefillBN = 256;        // output columns per workgroup (4 waves x 64)
 constexpr int kPrefillBK = 64;         // K rows per pipeline stage
 constexpr int kPrefillThreads = 256;
-constexpr int kPrefillLdsRowHalves = kPrefillBK + 8;  // padded A-tile row
+constexpr int kPrefillLdsRowHalves = kPrefillBK + 16;  // A-tile row: 160 B, no bank conflicts for the b128 operand reads
 
+constexpr int kPrefillBand = 8;        // tile rows per band of the tile order
 constexpr int kXcds = 8;               // MI355X: workgroups round-robin over 8 XCDs
 
 // partial sums of the 4 wavefronts, then the staged scales (halves) and
@@ -90,6 +91,7 @@ struct PrefillParams {
   int32_t M, K, N, G, zp_bias;
   int32_t g_shift;    // log2(G) when G is 32, 64 or 128 (unused when G == K)
   int32_t tiles_m, tiles_n, per_xcd;
+  int32_t band;       // tile rows per band of the workgroup -> tile order
 };
 
 struct DequantParams {

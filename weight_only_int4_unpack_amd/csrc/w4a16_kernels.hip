@@ -504,6 +504,32 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
     __hip_atomic_store(&p.counters[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Workgroup -> output tile. Workgroups go round-robin over the 8 XCDs, so
+// XCD x runs blockIdx x, x+8, ...; it is given the contiguous range
+// [x * per_xcd, (x + 1) * per_xcd) of a banded tile order: bands of `band`
+// tile rows, walked column by column, rows fastest. The ~64 tiles an XCD
+// runs at once then form a compact block (e.g. 8 rows x 8 columns), so the
+// activation rows and weight columns they read are shared in that XCD's L2.
+__device__ __forceinline__ bool prefill_tile(const PrefillParams& p, int& tm, int& tn) {
+  const int xcd = blockIdx.x % kXcds;
+  const int L = xcd * p.per_xcd + blockIdx.x / kXcds;
+  if (L >= p.tiles_m * p.tiles_n) return false;
+  const int full = p.tiles_m / p.band;          // bands of `band` rows
+  const int in_full = full * p.band * p.tiles_n;
+  if (L < in_full) {
+    const int b = L / (p.band * p.tiles_n);
+    const int r = L - b * p.band * p.tiles_n;
+    tn = r / p.band;
+    tm = b * p.band + (r - tn * p.band);
+  } else {
+    const int rows = p.tiles_m - full * p.band;  // last, shorter band
+    const int r = L - in_full;
+    tn = r / rows;
+    tm = full * p.band + (r - tn * rows);
+  }
+  return true;
+}
+
 // A load from a wave-uniform base plus a per-lane 32-bit byte offset (lets
 // the compiler use the scalar-base form of the global load).
 template <typename V>
@@ -554,11 +580,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
   const int g = lane >> 4;
   const int c = lane & 15;
 
-  const int xcd = blockIdx.x % kXcds;
-  const int tile = xcd * p.per_xcd + blockIdx.x / kXcds;
-  if (tile >= p.tiles_m * p.tiles_n) return;
-  const int tm = tile / p.tiles_n;
-  const int tn = tile % p.tiles_n;
+  int tm, tn;
+  if (!prefill_tile(p, tm, tn)) return;
   const int m0 = tm * BM;
   const int ncol = tn * kPrefillBN + wave * 64 + 4 * c;  // this lane's 4 columns
   const int ncolc = min(ncol, p.N - 4);
