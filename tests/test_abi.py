@@ -139,10 +139,11 @@ def test_selector_decode_shapes():
     assert p.steps_per_wave in (1, 2, 4, 8)
     assert p.splits * 4 * p.steps_per_wave >= 5120 // 32
     assert (p.splits - 1) * 4 * p.steps_per_wave < 5120 // 32        # no empty split
-    # 8 steps per wavefront span two groups of 4 steps: scale applied per group
-    assert p.steps_per_wave == 8 and p.decode_mode == 2
+    # 4 steps per wavefront (one group of 128 rows) at 3 wavefronts per SIMD:
+    # 680 workgroups resident at once; 8 steps would span two groups
+    assert p.steps_per_wave == 4 and p.decode_mode == 1 and p.grid == 680
     assert W.plan(1, 5120, 17408, 128, False, torch.bfloat16, route=W.ROUTE_DECODE,
-                  steps_per_wave=4).decode_mode == 1
+                  steps_per_wave=8).decode_mode == 2
     # K = 2112 is 66 steps of 32 rows; fp16 with groups of 64 folds the scale
     p = W.plan(8, 2112, 5120, 64, True, torch.float16)
     assert p.splits * 4 * p.steps_per_wave >= 66

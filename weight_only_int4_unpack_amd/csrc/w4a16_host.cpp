@@ -109,20 +109,29 @@ w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dty
     return fail(W4A16_ERR_PLAN, "steps per wavefront must be 1, 2, 4 or 8 (got %lld)", (long long)L);
   if (!aligned && L > 1)
     return fail(W4A16_ERR_PLAN, "N %% 16 or K %% 8 nonzero: decode runs one step per wavefront");
+  auto fits_one_of = [&](int64_t l) { return one_group || (SG >= l && SG % l == 0); };
+  auto auto_mode = [&](int64_t l) {
+    if (dtype == W4A16_F16 && G <= 64 && !one_group) return 0;
+    return fits_one_of(l) ? 1 : 2;
+  };
   if (L == 0) {
+    // the smallest L (most workgroups, shortest per-wavefront stream) whose
+    // grid is resident at once; wavefronts per SIMD: 3 for the modes with
+    // one accumulator set (<= 168 VGPRs), 2 for kMulti, fewer if LDS says so
     L = 1;
-    const int64_t slots = 2 * 4 * (int64_t)num_cus;  // two wavefronts per SIMD
-    if (aligned)
-      while (L < kDecodeMaxSteps && ceil_div(KS, L) * NB > slots) L *= 2;
+    if (aligned) {
+      for (;; L *= 2) {
+        const int m = mode_forced >= 0 ? mode_forced : auto_mode(L);
+        const int64_t lds = decode_lds_bytes((int)M, decode_ng_max(K, G, (int)L));
+        const int64_t by_lds = std::max<int64_t>(1, kLdsPerCu / std::max<int64_t>(1, lds));
+        const int64_t per_simd = std::min<int64_t>(m == 2 ? 2 : 3, by_lds);
+        if (L >= kDecodeMaxSteps || ceil_div(KS, L) * NB <= per_simd * 4 * (int64_t)num_cus) break;
+      }
+    }
   }
   int32_t mode = mode_forced;
-  const bool fits_one = one_group || (SG >= L && SG % L == 0);
-  if (mode < 0) {
-    if (dtype == W4A16_F16 && G <= 64 && !one_group)
-      mode = 0;
-    else
-      mode = fits_one ? 1 : 2;
-  }
+  const bool fits_one = fits_one_of(L);
+  if (mode < 0) mode = auto_mode(L);
   if (mode < 0 || mode > 2) return fail(W4A16_ERR_PLAN, "decode mode must be 0, 1 or 2");
   if (mode == 1 && !fits_one)
     return fail(W4A16_ERR_PLAN, "decode mode 1 needs the %lld steps of a wavefront inside one group",

@@ -28,7 +28,8 @@ constexpr int kPrefillThreads = 256;
 constexpr int kPrefillLdsRowHalves = kPrefillBK + 16;  // A-tile row: 160 B, no bank conflicts for the b128 operand reads
 
 constexpr int kPrefillBand = 8;        // tile rows per band of the tile order
-constexpr int kXcds = 8;               // MI355X: workgroups round-robin over 8 XCDs
+constexpr int kXcds = 8;
+constexpr int64_t kLdsPerCu = 160 * 1024;   // gfx950 LDS per CU               // MI355X: workgroups round-robin over 8 XCDs
 
 // partial sums of the 4 wavefronts, then the staged scales (halves) and
 // packed zero points (words) of at most ng_max groups

@@ -304,8 +304,37 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
   for (int j = 0; j < D; ++j) issue(j, ring[j]);
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- stage this workgroup's scales and zero points in LDS
-  {
+  // ---- kOneGrp: the lane's 16 scales and zero points of its wavefront's one
+  // group go straight to registers (used once, after the stream)
+  u32x4 sv1[2];
+  u32x2 zv1;
+  if constexpr (MODE == kOneGrp) {
+    const int grp = group_of(min(step_beg, p.KS - 1));
+    const int col_lane = b * kDecodeCols + 16 * c;
+    const uint16_t* srow = p.sc + (int64_t)grp * p.N;
+    if constexpr (ALIGNED) {  // N % 16 == 0: 16 scales in two aligned pieces
+      const uint16_t* sp = srow + min(col_lane, p.N - 16);
+      sv1[0] = *(const u32x4*)sp;
+      sv1[1] = *(const u32x4*)(sp + 8);
+    } else {
+      uint32_t h[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) h[e] = srow[min(col_lane + e, p.N - 1)];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        sv1[q] = u32x4{h[8 * q] | (h[8 * q + 1] << 16), h[8 * q + 2] | (h[8 * q + 3] << 16),
+                       h[8 * q + 4] | (h[8 * q + 5] << 16), h[8 * q + 6] | (h[8 * q + 7] << 16)};
+    }
+    if constexpr (HAS_ZP) {
+      const uint32_t* zp = p.qz + (int64_t)grp * N8;
+      zv1 = u32x2{zp[wc0], zp[wc1]};
+    } else {
+      const uint32_t zb = (uint32_t)p.zp_bias * 0x11111111u;
+      zv1 = u32x2{zb, zb};
+    }
+  }
+  // ---- the other modes stage this workgroup's scales and zero points in LDS
+  if constexpr (MODE != kOneGrp) {
     const int colc = min(b * kDecodeCols + tid, p.N - 1);
     for (int gi = 0; gi < ngroups; ++gi)
       lds_sc[gi * kDecodeCols + tid] = p.sc[(int64_t)(g_lo + gi) * p.N + colc];
@@ -316,7 +345,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
       }
     }
   }
-  __syncthreads();
+  if constexpr (MODE != kOneGrp) __syncthreads();
   auto lds_scales = [&](int st, u32x4 (&sv)[2], u32x2& zv) {
     const int gi = group_of(st) - g_lo;
     const uint16_t* sp = lds_sc + gi * kDecodeCols + 16 * c;
@@ -387,7 +416,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
         Rs = mfma<T>(sl.a, ones, Rs);
         const bool group_last =
             p.sg_shift >= 0 && (((st + 1) & ((1 << p.sg_shift) - 1)) == 0);
-        const bool fold = (MODE == kMulti) ? (group_last || (j + 1 == nsteps)) : (j + 1 == nsteps);
+        // kOneGrp folds once, in place, after the loop
+        const bool fold = (MODE == kMulti) && (group_last || (j + 1 == nsteps));
         if (fold) {
           u32x4 sv[2];
           u32x2 zv;
@@ -400,21 +430,34 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
               const float part = __builtin_fmaf(-bias, Rs[v], R[t][v]);
-              if constexpr (MODE == kMulti) {
-                acc[t][v] = __builtin_fmaf(sc, part, acc[t][v]);
-              } else {
-                acc[t][v] = sc * part;
-              }
+              acc[t][v] = __builtin_fmaf(sc, part, acc[t][v]);
             }
-            if constexpr (MODE == kMulti) R[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            R[t] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
-          if constexpr (MODE == kMulti) Rs = f32x4{0.f, 0.f, 0.f, 0.f};
+          Rs = f32x4{0.f, 0.f, 0.f, 0.f};
         }
       }
     }
     if (j + D < L) issue(j + D, sl);
     __builtin_amdgcn_sched_barrier(0);
   }
+  // kOneGrp: the wavefront's steps lie in one group; fold R in place (a
+  // wavefront without steps keeps its zero partial)
+  if constexpr (MODE == kOneGrp) {
+    if (nsteps > 0) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const bool odd16 = T::kIsF16 && (t & 1);
+        const float sc = widen(T{}, half_of(sv1, t)) * (odd16 ? 0.0625f : 1.0f);
+        const float bias = T::kBase + (float)nib(zv1[t >> 3], t & 7) * (odd16 ? 16.0f : 1.0f);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) R[t][v] = sc * __builtin_fmaf(-bias, Rs[v], R[t][v]);
+      }
+    }
+  }
+  f32x4 (&res)[16] = *[&]() -> f32x4 (*)[16] {
+    if constexpr (MODE == kOneGrp) return &R; else return &acc;
+  }();
 
   // ---- the 4 wavefronts' partials meet in LDS: red[wave][m][256]
 #pragma unroll
@@ -424,8 +467,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
       float* dst = red + (wave * M + m) * kDecodeCols + 16 * c;
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4)
-        *(f32x4*)(dst + 4 * t4) = f32x4{acc[4 * t4][v], acc[4 * t4 + 1][v], acc[4 * t4 + 2][v],
-                                        acc[4 * t4 + 3][v]};
+        *(f32x4*)(dst + 4 * t4) = f32x4{res[4 * t4][v], res[4 * t4 + 1][v], res[4 * t4 + 2][v],
+                                        res[4 * t4 + 3][v]};
     }
   }
   __syncthreads();
@@ -471,8 +514,9 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
   __syncthreads();
   if (!last_flag) return;
   // last arrival: add the S partials of every row in split order; QB splits'
-  // loads of all rows are in flight at once
-  constexpr int QB = (32 / MT) > 1 ? (32 / MT) : 1;
+  // loads of all rows are in flight at once (the stream's registers are free
+  // by now, so up to 96 loads per thread: one batch for S <= 96 / MT)
+  constexpr int QB = (96 / MT) > 1 ? (96 / MT) : 1;
   float sum[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) sum[m] = 0.f;
