@@ -84,6 +84,26 @@ def test_gemm_parity_grid(M, dtype, G, zp):
         assert_within_tolerance(got, want, dtype, f"M={M} {dtype} G={G} zp={zp} {label}")
 
 
+# ---------------------------------------------------------------- prefill tiles
+# Several 64 x 256 prefill tiles in both directions with ragged tails (M = 200
+# = 3 x 64 + 8, N = 520 = 2 x 256 + 8), every group span (G = 32, 64, 128 and
+# per-channel: 20, 10, 5 and 1 groups), both dtypes, with and without zero
+# points; K = 608 (K % 64 == 32) takes the variant that clamps the last stage.
+PREFILL_GRID = [(640, G, dtype, zp) for G in (32, 64, 128, 640) for dtype in ("fp16", "bf16")
+                for zp in (False, True)] + [(608, 32, "fp16", True), (608, 32, "bf16", False),
+                                            (608, 608, "bf16", True)]
+
+
+@pytest.mark.parametrize("K,G,dtype,zp", PREFILL_GRID)
+def test_prefill_tiles_parity(K, G, dtype, zp):
+    M, N = 200, 520
+    p = random_problem(M, K, N, G, dtype, zp, seed=K + G + (7 if zp else 0))
+    plan = _plan(p, W.ROUTE_PREFILL)
+    assert plan.block_m == 64 and plan.grid >= 4 * 3
+    got = dev_to_bits(p.gpu_gemm(plan=plan))
+    assert_within_tolerance(got, p.oracle_gemm(), dtype, f"K={K} G={G} {dtype} zp={zp}")
+
+
 # ---------------------------------------------------------------- workloads
 def _check_workload(name, rows=None, cols=None, routes=True):
     p = workload_problem(name)
