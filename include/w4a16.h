@@ -78,8 +78,9 @@ typedef struct {
                                1 = scale applied once per group, one group per
                                wavefront; 2 = as 1, several groups per
                                wavefront */
-  int32_t splits;           /* decode: K splits across workgroups */
-  int32_t steps_per_wave;   /* decode: 32-row K steps per wavefront (1, 2, 4, 8) */
+  int32_t splits;           /* K splits across workgroups (1 = none) */
+  int32_t steps_per_wave;   /* decode: 32-row K steps per wavefront (1, 2, 4, 8);
+                               prefill: 64-row K stages per workgroup */
   int32_t grid;             /* workgroups launched */
   int32_t threads;          /* threads per workgroup */
   int32_t lds_bytes;        /* LDS per workgroup */
@@ -127,7 +128,9 @@ w4a16_status w4a16_plan(int64_t M, int64_t K, int64_t N, int32_t group_size,
  * (W4A16_ROUTE_DECODE needs 1 <= M <= 16) and, for decode, the steps per
  * wavefront (1, 2, 4 or 8; 0 = selector's choice) and the decode mode
  * (0, 1, 2; -1 = selector's choice; mode 1 needs every wavefront's steps
- * inside one group) forced.
+ * inside one group) forced; for prefill, steps_per_wave forces the 64-row
+ * K stages per workgroup (0 = selector's choice; a multiple of 2 when
+ * G = 128 < K; at most 16 K splits result) and decode_mode is ignored.
  * Errors: those of w4a16_plan, and PLAN.
  */
 w4a16_status w4a16_plan_route(int64_t M, int64_t K, int64_t N,

@@ -125,9 +125,9 @@ def test_python_wrapper_validates_shapes():
 
 # ------------------------------------------------------------ selector
 def test_selector_routes_on_runtime_m():
-    for M in (1, 2, 4, 5, 6, 8, 16):
+    for M in (1, 2, 4, 5, 6, 8):
         assert W.plan(M, 4096, 4096, 32, True, torch.float16).route == W.ROUTE_DECODE
-    for M in (17, 64, 256, 2048, 4096):
+    for M in (9, 16, 17, 64, 256, 2048, 4096):
         assert W.plan(M, 4096, 4096, 32, True, torch.float16).route == W.ROUTE_PREFILL
     assert W.plan(0, 4096, 4096, 32, True, torch.float16).route == W.ROUTE_NONE
 
@@ -156,7 +156,7 @@ def test_selector_decode_shapes():
     p = W.plan(4, 4096, 4096, 32, True, torch.bfloat16, route=W.ROUTE_DECODE, steps_per_wave=4)
     assert p.decode_mode == 2
     # per-channel: one group spans every step
-    assert W.plan(16, 4096, 4096, 4096, True, torch.float16).decode_mode == 1
+    assert W.plan(8, 4096, 4096, 4096, True, torch.float16).decode_mode == 1
 
 
 def test_selector_prefill_tiles():
@@ -164,7 +164,31 @@ def test_selector_prefill_tiles():
     assert (p.block_m, p.block_n, p.block_k) == (64, 256, 64)
     assert p.grid % 8 == 0 and p.grid >= 32 * 68
     assert p.lds_bytes == 2 * 64 * 80 * 2
-    assert W.plan(100, 4096, 4096, 32, True, torch.float16).grid == 2 * 16   # tiles, a multiple of 8
+    assert p.splits == 1                       # 2176 tiles: no K split
+    q = W.plan(100, 4096, 4096, 32, True, torch.float16)
+    assert q.grid == 2 * 16 * q.splits and q.splits > 1     # 32 tiles, K split
+
+
+@pytest.mark.parametrize("M,K,N,G", [(64, 4096, 4096, 32), (256, 4096, 4096, 32),
+                                     (17, 640, 1032, 64), (200, 640, 520, 128),
+                                     (64, 608, 520, 32), (32, 5120, 17408, 128),
+                                     (16, 4096, 4096, 4096), (300, 2112, 5120, 64)])
+def test_selector_prefill_splits(M, K, N, G):
+    p = W.plan(M, K, N, G, True, torch.bfloat16, route=W.ROUTE_PREFILL)
+    tiles = -(-M // 64) * -(-N // 256)
+    KT = -(-K // 64)
+    S, ks = p.splits, p.steps_per_wave
+    assert 1 <= S <= 32
+    assert S * ks >= KT and (S - 1) * ks < KT             # every split has stages
+    if G == 128 and G != K:
+        assert ks % 2 == 0                               # whole groups of 128 rows
+    if S > 1:
+        assert tiles < 512 and ks >= 2
+        assert p.workspace_bytes >= S * -(-M // 64) * 64 * N * 4
+    # a forced split reproduces exactly; invalid ones are rejected
+    f = W.plan(M, K, N, G, True, torch.bfloat16, route=W.ROUTE_PREFILL, steps_per_wave=ks)
+    assert (f.splits, f.steps_per_wave, f.grid) == (S, ks, p.grid)
+    assert p.grid % 8 == 0 and p.grid >= tiles * S
 
 
 def test_forced_routes_and_errors():
@@ -186,6 +210,15 @@ def test_forced_routes_and_errors():
     assert W.plan(4, 2120, 520, 2120, True, torch.float16).steps_per_wave == 1
     with pytest.raises(W.W4A16Error):
         W.plan(4, 2120, 520, 2120, True, torch.float16, route=W.ROUTE_DECODE, steps_per_wave=2)
+
+
+def test_prefill_forced_split_errors():
+    with pytest.raises(W.W4A16Error):     # 3 stages would cut a 128-row group
+        W.plan(64, 4096, 4096, 128, False, torch.bfloat16, route=W.ROUTE_PREFILL, steps_per_wave=3)
+    with pytest.raises(W.W4A16Error):     # 64 stages, 1 per split: 64 > 32 splits
+        W.plan(64, 4096, 4096, 32, False, torch.bfloat16, route=W.ROUTE_PREFILL, steps_per_wave=1)
+    p = W.plan(64, 4096, 4096, 32, False, torch.bfloat16, route=W.ROUTE_PREFILL, steps_per_wave=16)
+    assert p.splits == 4 and p.grid == 64
 
 
 def test_planned_call_rejects_mismatched_plan():

@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -115,18 +116,36 @@ w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dty
     return fits_one_of(l) ? 1 : 2;
   };
   if (L == 0) {
-    // the smallest L (most workgroups, shortest per-wavefront stream) whose
-    // grid is resident at once; wavefronts per SIMD: 3 for the modes with
-    // one accumulator set (<= 168 VGPRs), 2 for kMulti, fewer if LDS says so
+    // Among the L whose whole grid is resident at once (wavefronts per SIMD:
+    // 3 for the modes with one accumulator set, <= 168 VGPRs; 2 for kMulti;
+    // fewer if LDS says so), take the one whose workgroup count is closest,
+    // by ratio, to max(NB, weight bytes / 32 KiB): large problems want many
+    // short streams for bandwidth, small ones few K-splits, since each split
+    // adds a cross-workgroup hand-off to the critical path. Ties go to the
+    // smaller L. (Measured on MI355X: 4 steps at 5120 x 17408, 2 at
+    // 2112 x 5120 and 4096 x 4096, no split for the 256 x 512 tiny shape.)
     L = 1;
     if (aligned) {
-      for (;; L *= 2) {
-        const int m = mode_forced >= 0 ? mode_forced : auto_mode(L);
-        const int64_t lds = decode_lds_bytes((int)M, decode_ng_max(K, G, (int)L));
+      const double bytes = (double)K * (double)N / 2.0;
+      const double target = std::max<double>((double)NB, bytes / 32768.0);
+      double best = 1e300;
+      bool any = false;
+      for (int64_t l = 1; l <= kDecodeMaxSteps; l *= 2) {
+        const int m = mode_forced >= 0 ? mode_forced : auto_mode(l);
+        if (m == 1 && !fits_one_of(l)) continue;
+        const int64_t lds = decode_lds_bytes((int)M, decode_ng_max(K, G, (int)l));
         const int64_t by_lds = std::max<int64_t>(1, kLdsPerCu / std::max<int64_t>(1, lds));
         const int64_t per_simd = std::min<int64_t>(m == 2 ? 2 : 3, by_lds);
-        if (L >= kDecodeMaxSteps || ceil_div(KS, L) * NB <= per_simd * 4 * (int64_t)num_cus) break;
+        const int64_t grid = ceil_div(KS, kDecodeWaves * l) * NB;
+        if (ceil_div(KS, l) * NB > per_simd * 4 * (int64_t)num_cus) continue;  // not resident
+        const double d = std::fabs(std::log((double)grid / target));
+        if (d < best - 1e-9) {
+          best = d;
+          L = l;
+          any = true;
+        }
       }
+      if (!any) L = kDecodeMaxSteps;  // nothing resident: longest streams
     }
   }
   int32_t mode = mode_forced;
@@ -151,22 +170,51 @@ w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dty
   return W4A16_OK;
 }
 
-void plan_prefill(int64_t M, int64_t N, w4a16_plan_t* pl) {
+// Prefill: 64 x 256 tiles. When there are fewer tiles than two per CU, K is
+// split across workgroups (whole groups per split, at least two 64-row
+// stages each) so that about two workgroups per CU run; each split writes an
+// fp32 partial and a second, fully parallel kernel adds them in split order.
+w4a16_status plan_prefill(int64_t M, int64_t K, int64_t N, int32_t G, int num_cus,
+                          int32_t ks_forced, w4a16_plan_t* pl) {
   using namespace w4a16;
-  const int bm = kPrefillBM;
-  const int64_t tm = ceil_div(M, bm), tn = ceil_div(N, kPrefillBN);
-  const int64_t per_xcd = ceil_div(tm * tn, kXcds);
+  const int64_t tm = ceil_div(M, kPrefillBM), tn = ceil_div(N, kPrefillBN);
+  const int64_t tiles = tm * tn;
+  const int64_t KT = ceil_div(K, kPrefillBK);
+  const int64_t unit = ((int64_t)G != K && G == 128) ? 2 : 1;  // stages per group
+  int64_t S = 1, ks = KT;
+  const int64_t want = 2 * (int64_t)num_cus;
+  if (ks_forced != 0) {
+    if (ks_forced < 0 || ks_forced % unit != 0)
+      return fail(W4A16_ERR_PLAN, "prefill stages per workgroup must be a positive multiple of %lld",
+                  (long long)unit);
+    ks = std::min<int64_t>(ks_forced, KT);
+    S = ceil_div(KT, ks);
+    if (S > kPrefillMaxSplits)
+      return fail(W4A16_ERR_PLAN, "%lld stages per workgroup give %lld K splits (at most %d)",
+                  (long long)ks_forced, (long long)S, kPrefillMaxSplits);
+    if (S == 1) ks = KT;
+  } else if (tiles < want) {
+    const int64_t s_max = std::max<int64_t>(1, std::min<int64_t>(kPrefillMaxSplits, KT / (2 * unit)));
+    const int64_t s0 = std::min<int64_t>(s_max, ceil_div(want, tiles));
+    if (s0 > 1) {
+      ks = ceil_div(ceil_div(KT, s0), unit) * unit;
+      S = ceil_div(KT, ks);
+    }
+  }
+  const int64_t units = tiles * S;
+  const int64_t per_xcd = ceil_div(units, kXcds);
   pl->route = W4A16_ROUTE_PREFILL;
-  pl->block_m = bm;
+  pl->block_m = kPrefillBM;
   pl->block_n = kPrefillBN;
   pl->block_k = kPrefillBK;
   pl->decode_mode = 0;
-  pl->splits = 1;
-  pl->steps_per_wave = 0;
+  pl->splits = (int32_t)S;
+  pl->steps_per_wave = (int32_t)ks;
   pl->grid = (int32_t)(per_xcd * kXcds);
   pl->threads = kPrefillThreads;
   pl->lds_bytes = prefill_lds_bytes();
-  pl->workspace_bytes = 0;
+  pl->workspace_bytes = S > 1 ? (int64_t)(S * tm * kPrefillBM * N * 4) : 0;
+  return W4A16_OK;
 }
 
 w4a16_status make_plan(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype, int32_t num_cus,
@@ -188,7 +236,8 @@ w4a16_status make_plan(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype
     st = plan_decode(M, K, N, G, dtype, num_cus, L, mode, pl);
     if (st != W4A16_OK) return st;
   } else if (route == W4A16_ROUTE_PREFILL) {
-    plan_prefill(M, N, pl);
+    st = plan_prefill(M, K, N, G, num_cus, L, pl);
+    if (st != W4A16_OK) return st;
   } else {
     return fail(W4A16_ERR_PLAN, "unknown route %d", (int)route);
   }
@@ -199,8 +248,7 @@ w4a16_status make_plan(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype
 w4a16_status check_plan(const w4a16_plan_t* pl, int64_t M, int64_t K, int64_t N, int32_t G,
                         int32_t dtype) {
   w4a16_plan_t ref;
-  w4a16_status st = make_plan(M, K, N, G, dtype, 256, pl->route,
-                              pl->route == W4A16_ROUTE_DECODE ? pl->steps_per_wave : 0,
+  w4a16_status st = make_plan(M, K, N, G, dtype, 256, pl->route, pl->steps_per_wave,
                               pl->route == W4A16_ROUTE_DECODE ? pl->decode_mode : -1, &ref);
   if (st != W4A16_OK) return st;
   if (std::memcmp(&ref, pl, sizeof(ref)) != 0)
@@ -348,9 +396,29 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, DeviceState* 
     p.g_shift = g.G == 32 ? 5 : g.G == 64 ? 6 : g.G == 128 ? 7 : 0;
     p.tiles_m = (int32_t)ceil_div(g.M, pl.block_m);
     p.tiles_n = (int32_t)ceil_div(g.N, kPrefillBN);
+    p.tiles = p.tiles_m * p.tiles_n;
     p.per_xcd = pl.grid / kXcds;
     p.band = (int32_t)std::min<int64_t>(kPrefillBand, p.tiles_m);
+    p.S = pl.splits;
+    p.kt_split = pl.steps_per_wave;
+    const int32_t Mp = p.tiles_m * kPrefillBM;
+    if (pl.splits > 1) {
+      const size_t part = (size_t)pl.splits * Mp * g.N * sizeof(float);
+      w4a16_status st = ensure_workspace(ds, part, 0);
+      if (st != W4A16_OK) return st;
+      p.ws = ds->partials;
+    }
     e = launch_prefill(p, g.dtype, g.qzeros != nullptr, pl.grid, stream);
+    if (e == hipSuccess && pl.splits > 1) {
+      PrefillReduceParams r{};
+      r.ws = ds->partials;
+      r.out = (uint16_t*)g.out;
+      r.M = (int32_t)g.M;
+      r.N = (int32_t)g.N;
+      r.Mp = Mp;
+      r.S = pl.splits;
+      e = launch_prefill_reduce(r, g.dtype, stream);
+    }
   }
   if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return W4A16_OK;

@@ -18,7 +18,7 @@ constexpr int kDecodeWaves = 4;        // wavefronts per workgroup
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr int kStepRows = 32;          // K rows per MFMA step
 constexpr int kDecodeMaxSteps = 8;     // most 32-row steps one wavefront streams
-constexpr int kAutoDecodeMaxM = 16;    // selector: decode for 1 <= M <= this
+constexpr int kAutoDecodeMaxM = 8;     // selector: decode for 1 <= M <= this (prefill with K splits wins above)
 
 // ---- prefill route (tiled MFMA)
 constexpr int kPrefillBM = 64;         // rows per workgroup tile
@@ -27,9 +27,10 @@ constexpr int kPrefillBK = 64;         // K rows per pipeline stage
 constexpr int kPrefillThreads = 256;
 constexpr int kPrefillLdsRowHalves = kPrefillBK + 16;  // A-tile row: 160 B, no bank conflicts for the b128 operand reads
 
-constexpr int kPrefillBand = 8;        // tile rows per band of the tile order
-constexpr int kXcds = 8;
-constexpr int64_t kLdsPerCu = 160 * 1024;   // gfx950 LDS per CU               // MI355X: workgroups round-robin over 8 XCDs
+constexpr int kPrefillBand = 8;         // tile rows per band of the tile order
+constexpr int kPrefillMaxSplits = 32;   // most K splits of one prefill tile
+constexpr int kXcds = 8;                // MI355X: workgroups round-robin over 8 XCDs
+constexpr int64_t kLdsPerCu = 160 * 1024;  // gfx950 LDS per CU
 
 // partial sums of the 4 wavefronts, then the staged scales (halves) and
 // packed zero points (words) of at most ng_max groups
@@ -91,8 +92,16 @@ struct PrefillParams {
   uint16_t* out;
   int32_t M, K, N, G, zp_bias;
   int32_t g_shift;    // log2(G) when G is 32, 64 or 128 (unused when G == K)
-  int32_t tiles_m, tiles_n, per_xcd;
+  int32_t tiles_m, tiles_n, tiles, per_xcd;
   int32_t band;       // tile rows per band of the workgroup -> tile order
+  int32_t S;          // K splits (1: no cross-workgroup hand-off)
+  int32_t kt_split;   // 64-row K stages per split
+  float* ws;          // fp32 partials [S][tiles_m * 64][N] (S > 1)
+};
+struct PrefillReduceParams {
+  const float* ws;    // [S][Mp][N] fp32 partials
+  uint16_t* out;      // [M][N]
+  int32_t M, N, Mp, S;
 };
 
 struct DequantParams {
@@ -107,6 +116,7 @@ struct DequantParams {
 hipError_t launch_decode(const DecodeParams& p, int dtype, bool has_zp, int mode,
                          int grid, int lds_bytes, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int dtype, bool has_zp, int grid, hipStream_t stream);
+hipError_t launch_prefill_reduce(const PrefillReduceParams& p, int dtype, hipStream_t stream);
 hipError_t launch_dequant(const DequantParams& p, int dtype, bool has_zp,
                           hipStream_t stream);
 

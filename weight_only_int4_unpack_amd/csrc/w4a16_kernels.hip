@@ -548,16 +548,19 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
     __hip_atomic_store(&p.counters[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Workgroup -> output tile. Workgroups go round-robin over the 8 XCDs, so
-// XCD x runs blockIdx x, x+8, ...; it is given the contiguous range
-// [x * per_xcd, (x + 1) * per_xcd) of a banded tile order: bands of `band`
-// tile rows, walked column by column, rows fastest. The ~64 tiles an XCD
-// runs at once then form a compact block (e.g. 8 rows x 8 columns), so the
+// Workgroup -> (output tile, K split). Workgroups go round-robin over the 8
+// XCDs, so XCD x runs blockIdx x, x+8, ...; it is given the contiguous range
+// [x * per_xcd, (x + 1) * per_xcd) of the units, which are ordered split by
+// split and, within a split, in a banded tile order: bands of `band` tile
+// rows, walked column by column, rows fastest. The ~64 tiles an XCD runs at
+// once then form a compact block (e.g. 8 rows x 8 columns), so the
 // activation rows and weight columns they read are shared in that XCD's L2.
-__device__ __forceinline__ bool prefill_tile(const PrefillParams& p, int& tm, int& tn) {
+__device__ __forceinline__ bool prefill_tile(const PrefillParams& p, int& tm, int& tn, int& split) {
   const int xcd = blockIdx.x % kXcds;
-  const int L = xcd * p.per_xcd + blockIdx.x / kXcds;
-  if (L >= p.tiles_m * p.tiles_n) return false;
+  int L = xcd * p.per_xcd + blockIdx.x / kXcds;
+  if (L >= p.tiles * p.S) return false;
+  split = L / p.tiles;  // units with one split index are consecutive
+  L -= split * p.tiles;
   const int full = p.tiles_m / p.band;          // bands of `band` rows
   const int in_full = full * p.band * p.tiles_n;
   if (L < in_full) {
@@ -610,7 +613,7 @@ __device__ __forceinline__ V ldg(const char* base, uint32_t off) {
 // stage that holds row K - 1 clamps weight rows and reads a zero block past
 // K; activations load in 16-byte pieces (KM = 1, K % 8 == 0) or one at a time.
 // ---------------------------------------------------------------------------
-template <typename T, bool HAS_ZP, int GS, int KM>
+template <typename T, bool HAS_ZP, int GS, int KM, bool SPLIT>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillParams p) {
   constexpr int BM = kPrefillBM;
   constexpr int RH = kPrefillLdsRowHalves;
@@ -624,14 +627,17 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
   const int g = lane >> 4;
   const int c = lane & 15;
 
-  int tm, tn;
-  if (!prefill_tile(p, tm, tn)) return;
+  int tm, tn, split;
+  if (!prefill_tile(p, tm, tn, split)) return;
   const int m0 = tm * BM;
   const int ncol = tn * kPrefillBN + wave * 64 + 4 * c;  // this lane's 4 columns
   const int ncolc = min(ncol, p.N - 4);
   const int N4 = p.N >> 2;  // 16-bit pieces per weight row
   const uint16_t* bq16 = (const uint16_t*)p.bq + (ncolc >> 2);
   const int KT = (p.K + kPrefillBK - 1) / kPrefillBK;
+  // this workgroup's K stages [kt_beg, kt_end): whole groups per split
+  const int kt_beg = SPLIT ? split * p.kt_split : 0;
+  const int kt_end = SPLIT ? min(KT, kt_beg + p.kt_split) : KT;
   const DqRegs mag = dq_regs(p.dq);
   const u32x4 ones = u32x4{T::kOnePair, T::kOnePair, T::kOnePair, T::kOnePair};
   const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -813,17 +819,18 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
   using No = std::false_type;
 
   Slab B0[2], B1[2];
-  load_a(0, a_next);
-  load_slab(0, 0, B0[0], C0{});
-  load_slab(0, 1, B0[1], C1{});
-  store_a(0, a_next);
+  load_a(kt_beg, a_next);
+  load_slab(kt_beg, 0, B0[0], C0{});
+  load_slab(kt_beg, 1, B0[1], C1{});
+  store_a(kt_beg & 1, a_next);
   __syncthreads();
-  int kt = 0;
-  for (; kt + 2 < KT; kt += 2) {
+  // kt_beg is even whenever a group spans two stages, so P = 0 opens groups
+  int kt = kt_beg;
+  for (; kt + 2 < kt_end; kt += 2) {
     stage(kt, B0, B1, C0{}, Yes{});
     stage(kt + 1, B1, B0, C1{}, Yes{});
   }
-  if (kt + 2 == KT) {
+  if (kt + 2 == kt_end) {
     stage(kt, B0, B1, C0{}, Yes{});
     stage(kt + 1, B1, B0, C1{}, No{});
   } else {
@@ -831,28 +838,72 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
   }
 
   // ---- epilogue: lane holds rows i*16 + 4g + v, columns ncol + e
-  if (ncol >= p.N) return;
-  if constexpr (GS == 0) {
-    const u32x2 sv = *(const u32x2*)(p.sc + ncol);
-    const uint32_t z4 = HAS_ZP ? ((const uint16_t*)p.qz)[ncol >> 2] : 0u;
+  const bool col_ok = ncol < p.N;
+  if constexpr (GS == 0) {  // one group: fold this split's sums (the fold is linear)
+    const u32x2 sv = *(const u32x2*)(p.sc + ncolc);
+    const uint32_t z4 = HAS_ZP ? ((const uint16_t*)p.qz)[ncolc >> 2] : 0u;
     float sc[4], bias[4];
     col_consts(sv, z4, true, sc, bias);
 #pragma unroll
     for (int i = 0; i < MB; ++i) fold_block(sc, bias, asum[i], acc[i], acc[i]);
   }
+  auto store_out = [&](int row, float x0, float x1, float x2, float x3) {
+    const uint32_t lo = (uint32_t)narrow(T{}, x0) | ((uint32_t)narrow(T{}, x1) << 16);
+    const uint32_t hi = (uint32_t)narrow(T{}, x2) | ((uint32_t)narrow(T{}, x3) << 16);
+    *(u32x2*)(p.out + (int64_t)row * p.N + ncol) = u32x2{lo, hi};
+  };
+  if constexpr (!SPLIT) {
+    if (!col_ok) return;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = m0 + i * 16 + 4 * g + v;
+        if (row < p.M) store_out(row, acc[i][0][v], acc[i][1][v], acc[i][2][v], acc[i][3][v]);
+      }
+    return;
+  }
+  // ---- K split: this split's fp32 partial goes to ws[split][row][col] (rows
+  // padded to whole tiles); prefill_reduce_kernel, launched next on the same
+  // stream, adds the splits in order.
+  if constexpr (SPLIT) {
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int row = m0 + i * 16 + 4 * g + v;
-      if (row < p.M) {
-        const uint32_t lo = (uint32_t)narrow(T{}, acc[i][0][v]) |
-                            ((uint32_t)narrow(T{}, acc[i][1][v]) << 16);
-        const uint32_t hi = (uint32_t)narrow(T{}, acc[i][2][v]) |
-                            ((uint32_t)narrow(T{}, acc[i][3][v]) << 16);
-        *(u32x2*)(p.out + (int64_t)row * p.N + ncol) = u32x2{lo, hi};
-      }
+      float* d = p.ws + ((int64_t)split * p.tiles_m * BM + row) * p.N + ncolc;
+      if (col_ok)
+        *(f32x4*)d = f32x4{acc[i][0][v], acc[i][1][v], acc[i][2][v], acc[i][3][v]};
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill K-split reduction: out[m][n] = cast(sum over splits in order of
+// ws[s][m][n]); one thread per 4 adjacent outputs, all splits' loads in
+// flight at once (S <= 16).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillReduceParams p) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 4-column piece
+  const int N4 = p.N >> 2;
+  if (q >= (int64_t)p.M * N4) return;
+  const int m = (int)(q / N4);
+  const int n = (int)(q - (int64_t)m * N4) * 4;
+  const int64_t split_stride = (int64_t)p.Mp * p.N;
+  const float* src = p.ws + (int64_t)m * p.N + n;
+  f32x4 v[kPrefillMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kPrefillMaxSplits; ++s)
+    if (s < p.S) v[s] = *(const f32x4*)(src + s * split_stride);
+  f32x4 sum = v[0];
+#pragma unroll
+  for (int s = 1; s < kPrefillMaxSplits; ++s)
+    if (s < p.S) sum += v[s];
+  const uint32_t lo = (uint32_t)narrow(T{}, sum[0]) | ((uint32_t)narrow(T{}, sum[1]) << 16);
+  const uint32_t hi = (uint32_t)narrow(T{}, sum[2]) | ((uint32_t)narrow(T{}, sum[3]) << 16);
+  *(u32x2*)(p.out + (int64_t)m * p.N + n) = u32x2{lo, hi};
 }
 
 // ---------------------------------------------------------------------------
@@ -957,7 +1008,12 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, bool has_zp, int mode
 
 template <typename T, bool Z, int GS, int KM>
 static hipError_t prefill_go(const PrefillParams& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_kernel<T, Z, GS, KM>), dim3(grid), dim3(kPrefillThreads), 0, st, p);
+  if (p.S > 1)
+    hipLaunchKernelGGL((prefill_kernel<T, Z, GS, KM, true>), dim3(grid), dim3(kPrefillThreads), 0,
+                       st, p);
+  else
+    hipLaunchKernelGGL((prefill_kernel<T, Z, GS, KM, false>), dim3(grid), dim3(kPrefillThreads), 0,
+                       st, p);
   return hipGetLastError();
 }
 template <typename T, bool Z, int GS>
@@ -977,6 +1033,15 @@ static hipError_t prefill_gs(const PrefillParams& p, int grid, hipStream_t st) {
     case 128: return prefill_km<T, Z, 4>(p, grid, st);
     default: return hipErrorInvalidValue;
   }
+}
+hipError_t launch_prefill_reduce(const PrefillReduceParams& p, int dtype, hipStream_t st) {
+  const int64_t pieces = (int64_t)p.M * (p.N / 4);
+  const int grid = (int)((pieces + 255) / 256);
+  if (dtype == W4A16_F16)
+    hipLaunchKernelGGL((prefill_reduce_kernel<F16>), dim3(grid), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((prefill_reduce_kernel<BF16>), dim3(grid), dim3(256), 0, st, p);
+  return hipGetLastError();
 }
 hipError_t launch_prefill(const PrefillParams& p, int dtype, bool has_zp, int grid,
                           hipStream_t st) {
