@@ -155,6 +155,28 @@ __device__ __forceinline__ uint32_t exact_pair(F16, uint32_t y, const DqRegs& ma
   h = h * c.scale;
   return __builtin_bit_cast(uint32_t, h);
 }
+// fp16 pair of column e as the exact integer q - z (no scale): the prefill
+// operand when the scale is applied to fp32 sums instead.
+template <int E>
+__device__ __forceinline__ uint32_t int_pair(uint32_t y, const DqRegs& mag, f16x2 bias) {
+  f16x2 h = __builtin_bit_cast(f16x2, magic_pair<F16, E>(y, mag));
+  if constexpr (E & 1) {
+    const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    h = __builtin_elementwise_fma(h, sixteenth, -bias);
+  } else {
+    h = h - bias;
+  }
+  return __builtin_bit_cast(uint32_t, h);
+}
+// The bias {b, b} is built from z's bits: fp16 1024 + z is 0x6400 | z, and
+// 64 + z (e odd: (1024 + 16q) / 16 - (64 + z)) is 0x5400 | 16z.
+template <int E>
+__device__ __forceinline__ u32x4 int_op(const uint32_t* y, const DqRegs& mag, uint32_t z) {
+  const uint32_t b = (E & 1) ? (0x5400u | (z << 4)) : (0x6400u | z);
+  const f16x2 bias = __builtin_bit_cast(f16x2, b * 0x10001u);
+  return u32x4{int_pair<E>(y[0], mag, bias), int_pair<E>(y[1], mag, bias),
+               int_pair<E>(y[2], mag, bias), int_pair<E>(y[3], mag, bias)};
+}
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -167,6 +189,14 @@ __device__ __forceinline__ uint32_t exact_pair(BF16, uint32_t y, const DqRegs& m
 }
 
 __device__ __forceinline__ uint32_t nib(uint32_t w, int j) { return (w >> (4 * j)) & 0xFu; }
+
+// A scale as a plain fp32 register (xor with threadIdx & 0): keeps the
+// compiler from folding its fp16 -> fp32 conversion into every FMA that uses
+// it as a mixed-precision v_fma_mix_f32, which measured at a fraction of the
+// rate of v_fma_f32 in the folds (fp16 prefill at 4096^3: 387 -> 217 us).
+__device__ __forceinline__ float plain_f32(float x, uint32_t zero) {
+  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) ^ (threadIdx.x & zero));
+}
 
 // 16 bytes of zeros: the load source of activation operands that lie past M
 // or K, so that no loaded register has to be cleared afterwards.
@@ -425,7 +455,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
 #pragma unroll
           for (int t = 0; t < 16; ++t) {
             const bool odd16 = T::kIsF16 && (t & 1);
-            const float sc = widen(T{}, half_of(sv, t)) * (odd16 ? 0.0625f : 1.0f);
+            const float sc =
+                plain_f32(widen(T{}, half_of(sv, t)) * (odd16 ? 0.0625f : 1.0f), p.dq.zero);
             const float bias = T::kBase + (float)nib(zv[t >> 3], t & 7) * (odd16 ? 16.0f : 1.0f);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
@@ -448,7 +479,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
         const bool odd16 = T::kIsF16 && (t & 1);
-        const float sc = widen(T{}, half_of(sv1, t)) * (odd16 ? 0.0625f : 1.0f);
+        const float sc =
+            plain_f32(widen(T{}, half_of(sv1, t)) * (odd16 ? 0.0625f : 1.0f), p.dq.zero);
         const float bias = T::kBase + (float)nib(zv1[t >> 3], t & 7) * (odd16 ? 16.0f : 1.0f);
 #pragma unroll
         for (int v = 0; v < 4; ++v) R[t][v] = sc * __builtin_fmaf(-bias, Rs[v], R[t][v]);
@@ -641,6 +673,9 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
   const DqRegs mag = dq_regs(p.dq);
   const u32x4 ones = u32x4{T::kOnePair, T::kOnePair, T::kOnePair, T::kOnePair};
   const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
+  // fp16: the operand is the exact integer q - z (one packed subtract or FMA
+  // per pair), so no activation sums are needed; bf16 keeps base + q.
+  constexpr bool kIntOp = T::kIsF16;
 
   f32x4 acc[MB][4];   // output accumulator
   f32x4 part[MB][4];  // current group's sum of a (base + q)   (GS > 0)
@@ -723,23 +758,28 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
         sl.q[r] = u16x2{bq16[(int64_t)r0 * N4], bq16[(int64_t)r1 * N4]};
       }
     }
+    const int grp = GS == 0 ? 0 : (min(k0, p.K - 1) >> p.g_shift);
     if constexpr (closes) {
-      const int grp = min(k0, p.K - 1) >> p.g_shift;
       sl.s = ldg<u32x2>((const char*)p.sc + (int64_t)grp * p.N * 2, s_off);
-      if constexpr (HAS_ZP) sl.z = ldg<uint16_t>((const char*)p.qz + (int64_t)grp * N4 * 2, z_off);
       sl.valid = KM == 0 || k0 < p.K;
     }
+    // zero points: where the scale is applied (factored form), or with every
+    // slab's weights (fp16 integer operand)
+    if constexpr (HAS_ZP && (closes || kIntOp))
+      sl.z = ldg<uint16_t>((const char*)p.qz + (int64_t)grp * N4 * 2, z_off);
   };
-  // Fold a group's partial into the output accumulator, row blocks
-  // [I0, I1) (scales s_bits of the lane's 4 columns, their packed zero
-  // points z4). GS = 0: acc holds the partial itself.
+  // Fold a group's partial into the output accumulator (scales s_bits of the
+  // lane's 4 columns, their packed zero points z4). GS = 0: acc holds the
+  // partial itself. fp16 (integer operand q - z): acc += s * part; bf16
+  // (operand base + q): acc += s' * (part - (base + z') * sum a).
   auto col_consts = [&](u32x2 s_bits, uint32_t z4, bool valid, float (&sc)[4], float (&bias)[4]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t sb = (e < 2 ? s_bits.x : s_bits.y) >> (16 * (e & 1));
       const float z = (float)(HAS_ZP ? nib(z4, e) : (uint32_t)p.zp_bias);
-      const bool odd16 = T::kIsF16 && (e & 1);
-      sc[e] = valid ? widen(T{}, sb & 0xFFFFu) * (odd16 ? 0.0625f : 1.0f) : 0.f;
+      const bool odd16 = !kIntOp && T::kIsF16 && (e & 1);
+      sc[e] = plain_f32(valid ? widen(T{}, sb & 0xFFFFu) * (odd16 ? 0.0625f : 1.0f) : 0.f,
+                        p.dq.zero);
       bias[e] = T::kBase + z * (odd16 ? 16.0f : 1.0f);
     }
   };
@@ -749,7 +789,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
     for (int e = 0; e < 4; ++e)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float d = __builtin_fmaf(-bias[e], as[v], src[e][v]);
+        const float d = kIntOp ? src[e][v] : __builtin_fmaf(-bias[e], as[v], src[e][v]);
         dst[e][v] = GS > 0 ? __builtin_fmaf(sc[e], d, dst[e][v]) : sc[e] * d;
       }
   };
@@ -764,23 +804,31 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
 #pragma unroll
     for (int r = 0; r < 4; ++r) Y[r] = __builtin_bit_cast(uint32_t, sl.q[r]);
     u32x4 bop[4];
-    bop[0] = magic_op<T, 0>(Y, mag);
-    bop[1] = magic_op<T, 1>(Y, mag);
-    bop[2] = magic_op<T, 2>(Y, mag);
-    bop[3] = magic_op<T, 3>(Y, mag);
+    if constexpr (kIntOp) {
+      const uint32_t z4 = HAS_ZP ? sl.z : (uint32_t)p.zp_bias * 0x1111u;
+      bop[0] = int_op<0>(Y, mag, nib(z4, 0));
+      bop[1] = int_op<1>(Y, mag, nib(z4, 1));
+      bop[2] = int_op<2>(Y, mag, nib(z4, 2));
+      bop[3] = int_op<3>(Y, mag, nib(z4, 3));
+    } else {
+      bop[0] = magic_op<T, 0>(Y, mag);
+      bop[1] = magic_op<T, 1>(Y, mag);
+      bop[2] = magic_op<T, 2>(Y, mag);
+      bop[3] = magic_op<T, 3>(Y, mag);
+    }
     float sc[4], bias[4];
     if constexpr (closes) col_consts(sl.s, HAS_ZP ? sl.z : 0u, sl.valid, sc, bias);
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       const u32x4 aop = *(const u32x4*)&As[buf][(i * 16 + c) * RH + ks * 32 + 8 * g];
       if constexpr (GS == 1) {
-        const f32x4 as = mfma<T>(aop, ones, zero4);
+        const f32x4 as = kIntOp ? zero4 : mfma<T>(aop, ones, zero4);
         f32x4 pt[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) pt[e] = mfma<T>(aop, bop[e], zero4);
         fold_block(sc, bias, as, pt, acc[i]);
       } else {
-        asum[i] = mfma<T>(aop, ones, opens ? zero4 : asum[i]);
+        if constexpr (!kIntOp) asum[i] = mfma<T>(aop, ones, opens ? zero4 : asum[i]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if constexpr (GS > 0)
