@@ -271,6 +271,8 @@ def test_canaries_and_inputs_untouched(M):
     (17, 640, 1032, 64, "fp16", False),     # first prefill M, ragged N
     (129, 2120, 520, 2120, "bf16", True),   # ragged M, K and N on prefill
     (255, 64, 256, 32, "fp16", True),       # a single K tile
+    (1, 256, 66048, 128, "bf16", False),    # 258 column blocks: the counter split-K hand-off
+    (3, 512, 66048, 64, "fp16", True),      # same, fp16 with zero points
 ])
 def test_edge_shapes(M, K, N, G, dtype, zp):
     p = random_problem(M, K, N, G, dtype, zp, seed=M + K + N)

@@ -263,8 +263,10 @@ struct DeviceState {
   bool probed = false;
   bool ok = false;
   int num_cus = 0;
-  float* partials = nullptr;      // split-K fp32 partials, [S, M, N]
+  float* partials = nullptr;      // decode split-K fp32 partials, [S, M, N]
   size_t partial_bytes = 0;
+  float* prefill_ws = nullptr;    // prefill K-split fp32 partials, [S, M_pad, N]
+  size_t prefill_bytes = 0;
   int32_t* counters = nullptr;    // arrival counters, one per column block
   size_t counter_n = 0;
 };
@@ -346,6 +348,31 @@ w4a16_status ensure_workspace(DeviceState* ds, size_t partial_bytes, size_t coun
   return W4A16_OK;
 }
 
+// Scratch for the prefill K-split partials, kept apart from the decode
+// split-K scratch so that growing one never waits on the other's users.
+w4a16_status ensure_prefill_ws(DeviceState* ds, size_t bytes) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (ds->prefill_bytes >= bytes) return W4A16_OK;
+  if (hipDeviceSynchronize() != hipSuccess) {  // other streams may still use the old buffer
+    (void)hipGetLastError();
+    return fail(W4A16_ERR_HIP, "device synchronisation before growing the scratch failed");
+  }
+  if (ds->prefill_ws && hipFree(ds->prefill_ws) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(W4A16_ERR_HIP, "freeing the old prefill partials failed");
+  }
+  ds->prefill_ws = nullptr;
+  ds->prefill_bytes = 0;
+  const size_t sz = std::max<size_t>(bytes, (size_t)8 << 20);
+  if (hipMalloc((void**)&ds->prefill_ws, sz) != hipSuccess) {
+    (void)hipGetLastError();
+    ds->prefill_ws = nullptr;
+    return fail(W4A16_ERR_HIP, "hipMalloc of %zu bytes of prefill partials failed", sz);
+  }
+  ds->prefill_bytes = sz;
+  return W4A16_OK;
+}
+
 w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, DeviceState* ds,
                  hipStream_t stream) {
   using namespace w4a16;
@@ -404,14 +431,14 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, DeviceState* 
     const int32_t Mp = p.tiles_m * kPrefillBM;
     if (pl.splits > 1) {
       const size_t part = (size_t)pl.splits * Mp * g.N * sizeof(float);
-      w4a16_status st = ensure_workspace(ds, part, 0);
+      w4a16_status st = ensure_prefill_ws(ds, part);
       if (st != W4A16_OK) return st;
-      p.ws = ds->partials;
+      p.ws = ds->prefill_ws;
     }
     e = launch_prefill(p, g.dtype, g.qzeros != nullptr, pl.grid, stream);
     if (e == hipSuccess && pl.splits > 1) {
       PrefillReduceParams r{};
-      r.ws = ds->partials;
+      r.ws = ds->prefill_ws;
       r.out = (uint16_t*)g.out;
       r.M = (int32_t)g.M;
       r.N = (int32_t)g.N;
