@@ -156,6 +156,10 @@ w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dty
     return fail(W4A16_ERR_PLAN, "decode mode 1 needs the %lld steps of a wavefront inside one group",
                 (long long)L);
   const int64_t S = ceil_div(KS, kDecodeWaves * L);
+  // the kernel addresses the split-K partials with 32-bit byte offsets
+  if (S > 1 && S * M * N * 4 >= (int64_t(1) << 32))
+    return fail(W4A16_ERR_PLAN, "decode split-K partials (%lld splits x %lld x %lld fp32) exceed 4 GiB",
+                (long long)S, (long long)M, (long long)N);
   pl->route = W4A16_ROUTE_DECODE;
   pl->block_m = kDecodeMaxM;
   pl->block_n = kDecodeCols;

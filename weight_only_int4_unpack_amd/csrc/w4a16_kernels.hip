@@ -256,6 +256,33 @@ __device__ __forceinline__ uint32_t half_of(const u32x4 (&sv)[2], int t) {
   return (t & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
+// Four adjacent fp32 partials (base + off bytes) as two 8-byte write-through
+// (agent-scope) stores and loads: the values bypass the per-XCD L2s, so a
+// workgroup on any XCD reads what another wrote once the arrival counter says
+// it is there. The scratch buffer is below 4 GiB, so a 32-bit offset from a
+// uniform base addresses it.
+__device__ __forceinline__ void store_wt4(float* base, uint32_t off, f32x4 v) {
+  uint64_t* d = (uint64_t*)((char*)base + off);
+  __hip_atomic_store(d, __builtin_bit_cast(uint64_t, f32x2{v[0], v[1]}), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(d + 1, __builtin_bit_cast(uint64_t, f32x2{v[2], v[3]}), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4 load_wt4(const float* base, uint32_t off) {
+  const uint64_t* s = (const uint64_t*)((const char*)base + off);
+  const f32x2 lo = __builtin_bit_cast(
+      f32x2, __hip_atomic_load(s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  const f32x2 hi = __builtin_bit_cast(
+      f32x2, __hip_atomic_load(s + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return f32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+// Four adjacent outputs, rounded to the activation type, in one 8-byte store.
+template <typename T>
+__device__ __forceinline__ void store_out4(T, uint16_t* dst, f32x4 v) {
+  *(u32x2*)dst = u32x2{(uint32_t)narrow(T{}, v[0]) | ((uint32_t)narrow(T{}, v[1]) << 16),
+                       (uint32_t)narrow(T{}, v[2]) | ((uint32_t)narrow(T{}, v[3]) << 16)};
+}
+
 // One ring slot: the packed weights (8 rows x 2 words) and the activation
 // operand of one 32-row step.
 struct DecodeSlot {
@@ -505,34 +532,41 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
   }
   __syncthreads();
 
-  // thread tid owns column b*256 + tid of every row
-  const int col = b * kDecodeCols + tid;
-  const bool col_ok = col < p.N;
-  const int colc = min(col, p.N - 1);
-  float part[MT];
+  // Wavefront w owns rows w, w + 4, ... (< M) and lane l columns b*256 + 4l
+  // .. 4l + 3 of them: 16-byte LDS reads and 8-byte global accesses keep this
+  // epilogue short, which matters because the last arrival of a column block
+  // runs it once, from a cold instruction cache, on the kernel's critical path.
+  constexpr int RPT = MT / 4;  // rows per wavefront
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int col4 = b * kDecodeCols + 4 * lane;
+  const bool col_ok = col4 < p.N;  // N % 8 == 0: all four columns or none
+  const uint32_t lane_off = (uint32_t)min(col4, p.N - 4) * 4u;  // bytes
+  const uint32_t row_bytes = (uint32_t)p.N * 4u;
+  f32x4 part[RPT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
+  for (int r = 0; r < RPT; ++r) {
+    const int m = wv + 4 * r;
     if (m < M) {
-      float v = red[m * kDecodeCols + tid];
+      f32x4 v = *(const f32x4*)(red + m * kDecodeCols + 4 * lane);
 #pragma unroll
-      for (int w = 1; w < kDecodeWaves; ++w) v += red[(w * M + m) * kDecodeCols + tid];
-      part[m] = v;
+      for (int w = 1; w < kDecodeWaves; ++w)
+        v += *(const f32x4*)(red + (w * M + m) * kDecodeCols + 4 * lane);
+      part[r] = v;
     }
   }
   if (p.S == 1) {
     if (col_ok) {
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-        if (m < M) p.out[(int64_t)m * p.N + col] = narrow(T{}, part[m]);
+      for (int r = 0; r < RPT; ++r)
+        if (wv + 4 * r < M) store_out4(T{}, p.out + (int64_t)(wv + 4 * r) * p.N + col4, part[r]);
     }
     return;
   }
   if (col_ok) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
-      if (m < M)
-        __hip_atomic_store(&p.ws[((int64_t)s * M + m) * p.N + col], part[m], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    for (int r = 0; r < RPT; ++r)
+      if (wv + 4 * r < M)
+        store_wt4(p.ws, (uint32_t)(s * M + wv + 4 * r) * row_bytes + lane_off, part[r]);
   }
   // every write-through store of this thread has completed before the
   // barrier, so the counter cannot run ahead of the partials
@@ -545,39 +579,38 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
   }
   __syncthreads();
   if (!last_flag) return;
-  // last arrival: add the S partials of every row in split order; QB splits'
-  // loads of all rows are in flight at once (the stream's registers are free
-  // by now, so up to 96 loads per thread: one batch for S <= 96 / MT)
-  constexpr int QB = (96 / MT) > 1 ? (96 / MT) : 1;
-  float sum[MT];
+  // last arrival: add the S partials of each row in split order, QB splits'
+  // loads of all the wavefront's rows in flight at once
+  if (tid == 0)
+    __hip_atomic_store(&p.counters[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (wv >= M) return;
+  constexpr int QB = RPT <= 2 ? 16 : 4;
+  f32x4 sum[RPT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) sum[m] = 0.f;
+  for (int r = 0; r < RPT; ++r) sum[r] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int q0 = 0; q0 < p.S; q0 += QB) {
-    float tq[QB][MT];
+    f32x4 tq[QB][RPT];
 #pragma unroll
     for (int u = 0; u < QB; ++u) {
       const int q = min(q0 + u, p.S - 1);
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-        if (m < M)
-          tq[u][m] = __hip_atomic_load(&p.ws[((int64_t)q * M + m) * p.N + colc], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+      for (int r = 0; r < RPT; ++r)
+        if (wv + 4 * r < M)
+          tq[u][r] = load_wt4(p.ws, (uint32_t)(q * M + wv + 4 * r) * row_bytes + lane_off);
     }
 #pragma unroll
     for (int u = 0; u < QB; ++u)
       if (q0 + u < p.S) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
-          if (m < M) sum[m] += tq[u][m];
+        for (int r = 0; r < RPT; ++r)
+          if (wv + 4 * r < M) sum[r] += tq[u][r];
       }
   }
   if (col_ok) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
-      if (m < M) p.out[(int64_t)m * p.N + col] = narrow(T{}, sum[m]);
+    for (int r = 0; r < RPT; ++r)
+      if (wv + 4 * r < M) store_out4(T{}, p.out + (int64_t)(wv + 4 * r) * p.N + col4, sum[r]);
   }
-  if (tid == 0)
-    __hip_atomic_store(&p.counters[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Workgroup -> (output tile, K split). Workgroups go round-robin over the 8
