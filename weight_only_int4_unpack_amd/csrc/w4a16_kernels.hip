@@ -579,8 +579,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
   }
   __syncthreads();
   if (!last_flag) return;
-  // last arrival: add the S partials of each row in split order, QB splits'
-  // loads of all the wavefront's rows in flight at once
+  // last arrival: add the S partials of each row in split order, up to QB
+  // splits' loads of all the wavefront's rows in flight at once
   if (tid == 0)
     __hip_atomic_store(&p.counters[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (wv >= M) return;
@@ -592,11 +592,13 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
     f32x4 tq[QB][RPT];
 #pragma unroll
     for (int u = 0; u < QB; ++u) {
-      const int q = min(q0 + u, p.S - 1);
+      const int q = q0 + u;
+      if (q < p.S) {
 #pragma unroll
-      for (int r = 0; r < RPT; ++r)
-        if (wv + 4 * r < M)
-          tq[u][r] = load_wt4(p.ws, (uint32_t)(q * M + wv + 4 * r) * row_bytes + lane_off);
+        for (int r = 0; r < RPT; ++r)
+          if (wv + 4 * r < M)
+            tq[u][r] = load_wt4(p.ws, (uint32_t)(q * M + wv + 4 * r) * row_bytes + lane_off);
+      }
     }
 #pragma unroll
     for (int u = 0; u < QB; ++u)
