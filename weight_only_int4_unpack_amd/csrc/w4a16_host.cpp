@@ -170,7 +170,7 @@ w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dty
   pl->grid = (int32_t)(NB * S);
   pl->threads = kDecodeThreads;
   pl->lds_bytes = decode_lds_bytes((int)M, decode_ng_max(K, G, L));
-  pl->workspace_bytes = S > 1 ? (int64_t)(S * M * N * 4 + NB * 4) : 0;
+  pl->workspace_bytes = S > 1 ? (int64_t)(S * M * N * 4 + NB * kDecodeWaves * 4) : 0;
   return W4A16_OK;
 }
 
@@ -271,7 +271,7 @@ struct DeviceState {
   size_t partial_bytes = 0;
   float* prefill_ws = nullptr;    // prefill K-split fp32 partials, [S, M_pad, N]
   size_t prefill_bytes = 0;
-  int32_t* counters = nullptr;    // arrival counters, one per column block
+  int32_t* counters = nullptr;    // arrival counters, one per (column block, wavefront)
   size_t counter_n = 0;
 };
 std::mutex g_mu;
@@ -303,8 +303,8 @@ w4a16_status device_state(DeviceState** out) {
 
 // Grows the device's split-K scratch. The partials need no initial value;
 // the arrival counters live in a buffer of their own that is zeroed when it
-// is allocated and that every launch leaves at zero (the last workgroup of
-// each column block resets its counter), so shapes of different size never
+// is allocated and that every launch leaves at zero (the last arrival on a
+// counter resets it), so shapes of different size never
 // see each other's data in a counter slot.
 w4a16_status ensure_workspace(DeviceState* ds, size_t partial_bytes, size_t counter_n) {
   std::lock_guard<std::mutex> lk(g_mu);
@@ -404,7 +404,7 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, DeviceState* 
     p.NB = (int32_t)ceil_div(g.N, kDecodeCols);
     if (pl.splits > 1) {
       const size_t part = (size_t)pl.splits * g.M * g.N * sizeof(float);
-      w4a16_status st = ensure_workspace(ds, part, (size_t)p.NB);
+      w4a16_status st = ensure_workspace(ds, part, (size_t)p.NB * kDecodeWaves);
       if (st != W4A16_OK) return st;
       p.ws = ds->partials;
       p.counters = ds->counters;

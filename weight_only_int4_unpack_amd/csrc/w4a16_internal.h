@@ -72,7 +72,7 @@ struct DecodeParams {
   const uint32_t* qz;
   uint16_t* out;
   float* ws;          // [S, M, N] fp32 partials (S > 1)
-  int32_t* counters;  // [NB] arrival counters, zero between launches
+  int32_t* counters;  // [NB][4] arrival counters per wavefront, zero between launches
   int32_t M, K, N, G, zp_bias;
   int32_t KS;         // K steps of 32 rows
   int32_t SG;         // steps per group

@@ -295,7 +295,6 @@ template <typename T, bool HAS_ZP, int MODE, bool ALIGNED, int L, int MT>
 __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams p) {
   constexpr int D = L < kRing ? L : kRing;
   extern __shared__ __attribute__((aligned(16))) float red[];
-  __shared__ int last_flag;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -510,7 +509,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
             plain_f32(widen(T{}, half_of(sv1, t)) * (odd16 ? 0.0625f : 1.0f), p.dq.zero);
         const float bias = T::kBase + (float)nib(zv1[t >> 3], t & 7) * (odd16 ? 16.0f : 1.0f);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) R[t][v] = sc * __builtin_fmaf(-bias, Rs[v], R[t][v]);
+        for (int v = 0; v < 4; ++v)
+          if (v < M) R[t][v] = sc * __builtin_fmaf(-bias, Rs[v], R[t][v]);
       }
     }
   }
@@ -562,28 +562,27 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
     }
     return;
   }
+  // Wavefront wv hands its rows over on its own: it publishes them, waits
+  // until its stores are complete, and counts itself in on the counter of
+  // (column block, wavefront); the last of the S arrivals adds them up.
+  if (wv >= M) return;  // no rows
   if (col_ok) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
       if (wv + 4 * r < M)
         store_wt4(p.ws, (uint32_t)(s * M + wv + 4 * r) * row_bytes + lane_off, part[r]);
   }
-  // every write-through store of this thread has completed before the
-  // barrier, so the counter cannot run ahead of the partials
+  // vmcnt counts the whole wavefront's stores: once it reads zero, every
+  // lane's partials have completed, so the counter cannot run ahead of them
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = __hip_atomic_fetch_add(&p.counters[b], 1, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = (prev == p.S - 1);
-  }
-  __syncthreads();
-  if (!last_flag) return;
+  int32_t* counter = p.counters + b * kDecodeWaves + wv;
+  int prev = 0;
+  if (lane == 0)
+    prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (__builtin_amdgcn_readfirstlane(prev) != p.S - 1) return;
   // last arrival: add the S partials of each row in split order, up to QB
   // splits' loads of all the wavefront's rows in flight at once
-  if (tid == 0)
-    __hip_atomic_store(&p.counters[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (wv >= M) return;
+  if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   constexpr int QB = RPT <= 2 ? 16 : 4;
   f32x4 sum[RPT];
 #pragma unroll
