@@ -256,25 +256,20 @@ __device__ __forceinline__ uint32_t half_of(const u32x4 (&sv)[2], int t) {
   return (t & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
-// Four adjacent fp32 partials (base + off bytes) as two 8-byte write-through
-// (agent-scope) stores and loads: the values bypass the per-XCD L2s, so a
-// workgroup on any XCD reads what another wrote once the arrival counter says
-// it is there. The scratch buffer is below 4 GiB, so a 32-bit offset from a
-// uniform base addresses it.
-__device__ __forceinline__ void store_wt4(float* base, uint32_t off, f32x4 v) {
-  uint64_t* d = (uint64_t*)((char*)base + off);
-  __hip_atomic_store(d, __builtin_bit_cast(uint64_t, f32x2{v[0], v[1]}), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(d + 1, __builtin_bit_cast(uint64_t, f32x2{v[2], v[3]}), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+// Four adjacent fp32 partials at byte offset `off` of the split-K scratch,
+// stored and loaded as one 16-byte buffer access with the sc1 cache policy
+// (write-through on stores, a fresh read past the per-XCD L2 on loads): a
+// workgroup on any XCD reads what another wrote once the arrival counter
+// says it is there. The buffer's record count bounds every access.
+constexpr int kSc1 = 16;  // cache-policy operand: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t scratch_rsrc(float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ f32x4 load_wt4(const float* base, uint32_t off) {
-  const uint64_t* s = (const uint64_t*)((const char*)base + off);
-  const f32x2 lo = __builtin_bit_cast(
-      f32x2, __hip_atomic_load(s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  const f32x2 hi = __builtin_bit_cast(
-      f32x2, __hip_atomic_load(s + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  return f32x4{lo[0], lo[1], hi[0], hi[1]};
+__device__ __forceinline__ void store_wt4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kSc1);
+}
+__device__ __forceinline__ f32x4 load_wt4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kSc1));
 }
 // Four adjacent outputs, rounded to the activation type, in one 8-byte store.
 template <typename T>
@@ -542,6 +537,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
   const bool col_ok = col4 < p.N;  // N % 8 == 0: all four columns or none
   const uint32_t lane_off = (uint32_t)min(col4, p.N - 4) * 4u;  // bytes
   const uint32_t row_bytes = (uint32_t)p.N * 4u;
+  // the planner keeps the S x M x N fp32 partials below 4 GiB
+  const __amdgpu_buffer_rsrc_t wsr = scratch_rsrc(p.ws, (uint32_t)(p.S * M) * row_bytes);
   f32x4 part[RPT];
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
@@ -570,7 +567,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
       if (wv + 4 * r < M)
-        store_wt4(p.ws, (uint32_t)(s * M + wv + 4 * r) * row_bytes + lane_off, part[r]);
+        store_wt4(wsr, (uint32_t)(s * M + wv + 4 * r) * row_bytes + lane_off, part[r]);
   }
   // vmcnt counts the whole wavefront's stores: once it reads zero, every
   // lane's partials have completed, so the counter cannot run ahead of them
@@ -596,7 +593,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
 #pragma unroll
         for (int r = 0; r < RPT; ++r)
           if (wv + 4 * r < M)
-            tq[u][r] = load_wt4(p.ws, (uint32_t)(q * M + wv + 4 * r) * row_bytes + lane_off);
+            tq[u][r] = load_wt4(wsr, (uint32_t)(q * M + wv + 4 * r) * row_bytes + lane_off);
       }
     }
 #pragma unroll
