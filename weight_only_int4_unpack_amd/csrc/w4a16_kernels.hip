@@ -198,10 +198,11 @@ __device__ __forceinline__ float plain_f32(float x, uint32_t zero) {
   return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) ^ (threadIdx.x & zero));
 }
 
-// 16 bytes of zeros: the load source of activation operands that lie past M
-// or K, so that no loaded register has to be cleared afterwards.
-__device__ __attribute__((aligned(16))) const uint32_t kZeroBlock[4] = {0u, 0u, 0u, 0u};
-
+// Activation loads read an in-bounds (clamped) address and clear the value
+// afterwards where it lies past K. Selecting between the activation pointer
+// and a zero block instead would make the load a flat one, and a pending flat
+// load makes the compiler wait for every outstanding load (vmcnt(0)) before
+// the first use of any of them, so nothing would overlap the stream.
 // Two rows' half-words h (0: columns 0..3, 1: columns 4..7) of words w0, w1
 // joined into one Y word (row of w0 in the low half).
 __device__ __forceinline__ uint32_t join_rows(uint32_t w0, uint32_t w1, int h) {
@@ -305,8 +306,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
   const int wc0 = min(word0, N8 - 1);
   const int wc1 = min(word0 + 1, N8 - 1);
   const int wcv = ALIGNED ? min(word0, N8 - 2) : 0;  // 8-byte aligned pair
+  // rows c >= M load row M - 1: their MFMA rows are computed and never stored
   const int mrow = min(c, M - 1);
-  const bool a_live = c < M;
   const uint16_t* arow = p.a + (int64_t)mrow * p.K;
   const DqRegs mag = dq_regs(p.dq);
 
@@ -337,14 +338,14 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
     }
     const int k = st * kStepRows + 8 * g;
     if constexpr (ALIGNED) {  // K % 8 == 0: a whole 8-element piece or none
-      const bool live = a_live && k < p.K;
-      sl.a = *(const u32x4*)(live ? (const void*)(arow + k) : (const void*)kZeroBlock);
+      const u32x4 v = *(const u32x4*)(arow + min(k, p.K - 8));
+      sl.a = k < p.K ? v : u32x4{0u, 0u, 0u, 0u};
     } else {
       uint32_t h[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const bool live = a_live && k + e < p.K;
-        h[e] = *(live ? arow + k + e : (const uint16_t*)kZeroBlock);
+        const uint32_t v = arow[min(k + e, p.K - 1)];
+        h[e] = k + e < p.K ? v : 0u;
       }
       sl.a = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
                    h[6] | (h[7] << 16)};
@@ -668,12 +669,12 @@ __device__ __forceinline__ V ldg(const char* base, uint32_t off) {
 // and the fold is done once, on the output accumulator, at the end.
 //
 // Loads never branch: rows and columns are clamped into the arrays, rows past
-// M are computed and not stored, activation columns past K read a zero block.
+// M are computed and not stored, activation columns past K are cleared.
 // The K loop is unrolled twice so the two weight buffers swap roles without
 // copies (a group of 4 slabs is exactly one unrolled body). Workgroup ids are
 // spread so that the tiles of one XCD share A rows. Two workgroups fit a CU.
 // KM = 0: K % 64 == 0 and no load is checked against K. KM = 1, 2: the
-// stage that holds row K - 1 clamps weight rows and reads a zero block past
+// stage that holds row K - 1 clamps weight rows and clears activations past
 // K; activations load in 16-byte pieces (KM = 1, K % 8 == 0) or one at a time.
 // ---------------------------------------------------------------------------
 template <typename T, bool HAS_ZP, int GS, int KM, bool SPLIT>
@@ -720,7 +721,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
 
   // ---- loaders. Full stages (all 64 rows inside K) address every load as a
   // wave-uniform base plus one per-lane 32-bit byte offset; the last stage,
-  // when K % 64 != 0, clamps weight rows and reads a zero block past K.
+  // when K % 64 != 0, clamps weight rows and clears activations past K.
   // Rows past M are clamped to M - 1 once, in the per-lane offsets.
   uint32_t a_off[AP];
 #pragma unroll
@@ -743,12 +744,15 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
         const int k = kt * kPrefillBK + (tid & 7) * 8;
         const uint16_t* arow = p.a + (int64_t)row * p.K;
         if constexpr (KM == 1) {
-          ar[j] = *(const u32x4*)(k < p.K ? (const void*)(arow + k) : (const void*)kZeroBlock);
+          const u32x4 v = *(const u32x4*)(arow + min(k, p.K - 8));
+          ar[j] = k < p.K ? v : u32x4{0u, 0u, 0u, 0u};
         } else {
           uint32_t h[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            h[e] = *(k + e < p.K ? arow + k + e : (const uint16_t*)kZeroBlock);
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t v = arow[min(k + e, p.K - 1)];
+            h[e] = k + e < p.K ? v : 0u;
+          }
           ar[j] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
                         h[6] | (h[7] << 16)};
         }
