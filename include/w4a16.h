@@ -103,6 +103,24 @@ w4a16_status w4a16_gemm(const void* a, const int32_t* b_q, const void* scales,
                         int64_t N, int32_t dtype, void* stream);
 
 /*
+ * w4a16_gemm_bias - as w4a16_gemm, plus a bias row: out[m,n] =
+ * RNE(fp32(sum_k a[m,k] w[k,n]) + fp32(bias[n])), the bias added to the
+ * fp32 result before the one rounding to the output type and indexed by
+ * the output column only (PR #40977 "RDNA hybrid W4A16", Code section: the
+ * test's reference adds bias.float() to the fp32 product before the cast;
+ * its Review section reports the prior kernel indexing the bias by a row
+ * count, out of bounds). bias: device pointer to N values of `dtype`,
+ * 16-byte aligned, owned by the caller, never written; NULL gives exactly
+ * w4a16_gemm. Errors: those of w4a16_gemm (ALIGN for a misaligned bias).
+ */
+w4a16_status w4a16_gemm_bias(const void* a, const int32_t* b_q,
+                             const void* scales, const int32_t* qzeros,
+                             int32_t group_size, int32_t zp_bias,
+                             const void* bias, void* out, int64_t M,
+                             int64_t K, int64_t N, int32_t dtype,
+                             void* stream);
+
+/*
  * w4a16_gemm_planned - as w4a16_gemm, but runs the launch in `plan`
  * (obtained from w4a16_plan or w4a16_plan_route, possibly with another
  * route or split forced). The plan is checked against the problem first.

@@ -27,6 +27,11 @@ and section; "Code" is the page's key-source-snippet section):
 * GEMM in fp32: ``A.float() @ W`` then one round-to-nearest-even cast to the
   activation dtype (PR #40977 Code section, reference function's last two
   lines).
+* Optional bias ``[N]`` in the activation dtype: widened to fp32 and added
+  to the fp32 product, by output column, before that one cast (PR #40977
+  Code section: the reference adds ``bias.float()`` to the fp32 result;
+  its Review section reports the prior kernel's bias indexed out of bounds
+  by a row count, so the index here is the column alone).
 * Rejections (PR #43731 "TritonW4A16LinearKernel as CUDA fallback", Code
   section ``can_implement``): activations not fp16/bf16, N not a multiple
   of 8, unsupported group size unless it equals the full K. The supported
@@ -189,31 +194,43 @@ def dequant_tile(b_q, scales_bits, qzeros, group_size: int, zp_bias: int,
 # GEMM
 # --------------------------------------------------------------------------
 def gemm_f32(a_bits, b_q, scales_bits, qzeros, group_size: int,
-             zp_bias: int, dtype: str, rows=None, cols=None) -> np.ndarray:
-    """fp32 product ``float(A) @ W32`` (optionally only some rows/columns)."""
+             zp_bias: int, dtype: str, rows=None, cols=None,
+             bias_bits=None) -> np.ndarray:
+    """fp32 product ``float(A) @ W32`` (optionally only some rows/columns),
+    plus ``float(bias)`` per output column when a bias is given."""
     A = to_f32(a_bits, dtype)
     if rows is not None:
         A = A[np.asarray(rows, dtype=np.int64)]
     W = dequant_fp32(b_q, scales_bits, qzeros, group_size, zp_bias, dtype,
                      cols=cols)
-    return A @ W
+    C = A @ W
+    if bias_bits is not None:
+        b = to_f32(bias_bits, dtype)
+        if cols is not None:
+            b = b[np.asarray(cols, dtype=np.int64)]
+        C = C + b[None, :]
+    return C
 
 
 def gemm(a_bits, b_q, scales_bits, qzeros, group_size: int, zp_bias: int,
-         dtype: str, rows=None, cols=None) -> np.ndarray:
-    """Output bits in the activation dtype: RNE of the fp32 product."""
+         dtype: str, rows=None, cols=None, bias_bits=None) -> np.ndarray:
+    """Output bits in the activation dtype: RNE of the fp32 product (plus
+    bias)."""
     return rne_bits(gemm_f32(a_bits, b_q, scales_bits, qzeros, group_size,
-                             zp_bias, dtype, rows=rows, cols=cols), dtype)
+                             zp_bias, dtype, rows=rows, cols=cols,
+                             bias_bits=bias_bits), dtype)
 
 
 def bruteforce_f64(a_bits, b_q, scales_bits, qzeros, group_size: int,
-                   zp_bias: int, dtype: str) -> np.ndarray:
+                   zp_bias: int, dtype: str, bias_bits=None) -> np.ndarray:
     """fp64 triple loop over plain Python numbers; tiny shapes only.
 
     Every weight is taken straight from its word with integer shifts, so
-    this shares no vectorised indexing with ``dequant_fp32``.
+    this shares no vectorised indexing with ``dequant_fp32``. A bias is
+    added to each output's fp64 sum.
     """
     A = to_f32(a_bits, dtype).astype(np.float64)
+    B = None if bias_bits is None else to_f32(bias_bits, dtype).astype(np.float64)
     S = to_f32(scales_bits, dtype).astype(np.float64)
     bq = np.asarray(b_q, dtype=np.int64) & 0xFFFFFFFF
     qz = None if qzeros is None else np.asarray(qzeros, dtype=np.int64) & 0xFFFFFFFF
@@ -228,7 +245,7 @@ def bruteforce_f64(a_bits, b_q, scales_bits, qzeros, group_size: int,
                 g = k // group_size
                 z = zp_bias if qz is None else (int(qz[g, n // 8]) >> (4 * (n % 8))) & 15
                 acc += float(A[m, k]) * float(q - z) * float(S[g, n])
-            out[m, n] = acc
+            out[m, n] = acc if B is None else acc + float(B[n])
     return out
 
 

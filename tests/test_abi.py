@@ -18,7 +18,7 @@ HAS_GPU = torch.cuda.is_available()
 def test_library_exports_every_header_symbol():
     L = W.lib()
     names = W.header_functions()
-    assert {"w4a16_gemm", "w4a16_gemm_planned", "w4a16_plan", "w4a16_plan_route",
+    assert {"w4a16_gemm", "w4a16_gemm_bias", "w4a16_gemm_planned", "w4a16_plan", "w4a16_plan_route",
             "w4a16_dequant", "w4a16_pack_int4", "w4a16_unpack_int4", "w4a16_last_error",
             "w4a16_version"} <= set(names)
     for n in names:
@@ -82,6 +82,23 @@ def _gemm(a=FAKE, b=FAKE, s=FAKE, z=None, G=128, zp=8, out=FAKE, M=4, K=256, N=5
 def test_gemm_rejections(kw, status):
     assert _gemm(**kw) == status
     assert W.last_error() != ""
+
+
+def _gemm_bias(bias, a=FAKE, out=FAKE, M=4, K=256, N=512, dt=W.F16):
+    return W.lib().w4a16_gemm_bias(a, FAKE, FAKE, None, 128, 8, bias, out, M, K, N, dt, None)
+
+
+def test_gemm_bias_checks():
+    # a misaligned bias is rejected before any device work; shape, NULL and
+    # M = 0 rules are those of w4a16_gemm
+    assert _gemm_bias(ctypes.c_void_p(0x10002)) == W.ERR_ALIGN
+    assert "bias" in W.last_error()
+    assert _gemm_bias(FAKE, N=516) == W.ERR_SHAPE
+    assert _gemm_bias(FAKE, a=None) == W.ERR_NULL
+    assert _gemm_bias(FAKE, M=0, a=None, out=None) == W.OK
+    if not HAS_GPU:   # a valid call (with or without bias) reaches the device check
+        assert _gemm_bias(FAKE) == W.ERR_DEVICE
+        assert _gemm_bias(None) == W.ERR_DEVICE
 
 
 def test_group_64_is_kept_not_substituted():

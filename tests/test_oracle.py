@@ -264,6 +264,80 @@ def test_bruteforce_fp64_tiny(dtype, has_zp, G):
     assert np.all(np.abs(C32 - C64) <= bound)
 
 
+# ---------------------------------------------------------------- bias
+@pytest.mark.parametrize("dtype", [O.F16, O.BF16])
+def test_bias_alone_when_product_is_zero(dtype):
+    # zero activations, or q == z, make the fp32 product exactly 0; the
+    # output is then the bias itself, bit for bit (0 + b = b, and b is already
+    # representable, so the one rounding leaves it unchanged)
+    M, K, N, G = 3, 256, 64, 128
+    d, b_q, _ = _rand_problem(M, K, N, G, dtype, False, 21)
+    bias = synthetic.random_bits((N,), dtype, 22, 3.0)
+    a0 = np.zeros((M, K), np.uint16)
+    out = O.gemm(a0, b_q, d["s_bits"], None, G, 8, dtype, bias_bits=bias)
+    assert np.array_equal(out, np.broadcast_to(bias, (M, N)))
+    q8 = O.pack_int4(np.full((K, N), 8, np.uint8))
+    out = O.gemm(d["a_bits"], q8, d["s_bits"], None, G, 8, dtype, bias_bits=bias)
+    assert np.array_equal(out, np.broadcast_to(bias, (M, N)))
+
+
+def test_bias_is_indexed_by_column():
+    # a one-hot bias on column n0 with zero activations lights exactly that
+    # output column in every row (a row-indexed bias would light a row)
+    M, K, N, G = 4, 128, 48, 32
+    d, b_q, qz = _rand_problem(M, K, N, G, O.F16, True, 23)
+    for n0 in (0, 3, 17, 47):
+        b = np.zeros(N, np.float32)
+        b[n0] = 1.0
+        out = O.gemm(np.zeros((M, K), np.uint16), b_q, d["s_bits"], qz, G, 8, O.F16,
+                     bias_bits=O.rne_bits(b, O.F16))
+        want = np.zeros((M, N), np.float32)
+        want[:, n0] = 1.0
+        assert np.array_equal(O.to_f32(out, O.F16), want)
+
+
+@pytest.mark.parametrize("dtype", [O.F16, O.BF16])
+def test_bias_exact_integer_case(dtype):
+    # exact operands (A in {-1,0,1}, S = 2^-4) and a bias of multiples of 2^-4:
+    # the result is a small multiple of 2^-4, exact in every type, and equals
+    # the rational sum
+    M, K, N, G = 3, 256, 24, 64
+    rng = np.random.default_rng(24)
+    a = np.zeros((M, K), np.float32)
+    for m in range(M):
+        idx = rng.choice(K, size=12, replace=False)
+        a[m, idx] = rng.choice([-1.0, 1.0], size=12)
+    q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    bias = rng.integers(-64, 65, size=N).astype(np.float32) / 16
+    s_bits = O.rne_bits(np.full((K // G, N), 1.0 / 16, np.float32), dtype)
+    out = O.gemm(O.rne_bits(a, dtype), O.pack_int4(q), s_bits, None, G, 8, dtype,
+                 bias_bits=O.rne_bits(bias, dtype))
+    for m in range(M):
+        for n in range(N):
+            exact = Fraction(float(bias[n]))
+            for k in np.nonzero(a[m])[0]:
+                exact += Fraction(int(a[m, k])) * (int(q[k, n]) - 8) * Fraction(1, 16)
+            assert Fraction(float(O.to_f32(out[m:m + 1, n:n + 1], dtype)[0, 0])) == exact
+
+
+def test_bias_bruteforce_fp64_and_zero_bias():
+    M, K, N, G = 2, 128, 16, 32
+    d, b_q, qz = _rand_problem(M, K, N, G, O.BF16, True, 25)
+    bias = synthetic.random_bits((N,), O.BF16, 26, 2.0)
+    C32 = O.gemm_f32(d["a_bits"], b_q, d["s_bits"], qz, G, 8, O.BF16,
+                     bias_bits=bias).astype(np.float64)
+    C64 = O.bruteforce_f64(d["a_bits"], b_q, d["s_bits"], qz, G, 8, O.BF16, bias_bits=bias)
+    A64 = O.to_f32(d["a_bits"], O.BF16).astype(np.float64)
+    W64 = O.dequant_fp32(b_q, d["s_bits"], qz, G, 8, O.BF16).astype(np.float64)
+    B64 = O.to_f32(bias, O.BF16).astype(np.float64)
+    bound = (K + 1) * 2.0 ** -24 * ((np.abs(A64) @ np.abs(W64)) + np.abs(B64)) + 1e-30
+    assert np.all(np.abs(C32 - C64) <= bound)
+    # a bias of zeros changes nothing, bit for bit
+    zero = np.zeros(N, np.uint16)
+    assert np.array_equal(O.gemm(d["a_bits"], b_q, d["s_bits"], qz, G, 8, O.BF16, bias_bits=zero),
+                          O.gemm(d["a_bits"], b_q, d["s_bits"], qz, G, 8, O.BF16))
+
+
 # ---------------------------------------------------------------- pages
 def test_pages_shape_contract():
     g = json.load(open(os.path.join(GOLDEN, "pages_shape_contract.json")))

@@ -389,6 +389,7 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, DeviceState* 
     p.bq = (const uint32_t*)g.b_q;
     p.sc = (const uint16_t*)g.scales;
     p.qz = (const uint32_t*)g.qzeros;
+    p.bias = (const uint16_t*)g.bias;
     p.out = (uint16_t*)g.out;
     p.M = (int32_t)g.M;
     p.K = (int32_t)g.K;
@@ -418,6 +419,7 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, DeviceState* 
     p.bq = (const uint32_t*)g.b_q;
     p.sc = (const uint16_t*)g.scales;
     p.qz = (const uint32_t*)g.qzeros;
+    p.bias = pl.splits > 1 ? nullptr : (const uint16_t*)g.bias;  // split: the reduction adds it
     p.out = (uint16_t*)g.out;
     p.M = (int32_t)g.M;
     p.K = (int32_t)g.K;
@@ -443,6 +445,7 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, DeviceState* 
     if (e == hipSuccess && pl.splits > 1) {
       PrefillReduceParams r{};
       r.ws = ds->prefill_ws;
+      r.bias = (const uint16_t*)g.bias;
       r.out = (uint16_t*)g.out;
       r.M = (int32_t)g.M;
       r.N = (int32_t)g.N;
@@ -456,14 +459,15 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, DeviceState* 
 }
 
 w4a16_status gemm_common(const void* a, const int32_t* b_q, const void* scales,
-                         const int32_t* qzeros, int32_t G, int32_t zp_bias, void* out, int64_t M,
-                         int64_t K, int64_t N, int32_t dtype, const w4a16_plan_t* forced,
-                         void* stream) {
+                         const int32_t* qzeros, int32_t G, int32_t zp_bias, const void* bias,
+                         void* out, int64_t M, int64_t K, int64_t N, int32_t dtype,
+                         const w4a16_plan_t* forced, void* stream) {
   w4a16_status st = check_shape(M, K, N, G, dtype);
   if (st != W4A16_OK) return st;
   if (M == 0) return W4A16_OK;
   st = check_ptrs(a, b_q, scales, qzeros, out, zp_bias);
   if (st != W4A16_OK) return st;
+  if (bias && !aligned16(bias)) return fail(W4A16_ERR_ALIGN, "bias must be 16-byte aligned");
   if (forced) {
     st = check_plan(forced, M, K, N, G, dtype);
     if (st != W4A16_OK) return st;
@@ -485,7 +489,7 @@ w4a16_status gemm_common(const void* a, const int32_t* b_q, const void* scales,
                    (long long)M, (long long)K, (long long)N, (int)G, pl.route, pl.block_m, pl.splits,
                    pl.steps_per_wave, pl.decode_mode, pl.grid);
   }
-  w4a16::GemmArgs g{a, b_q, scales, qzeros, out, M, K, N, G, zp_bias, dtype};
+  w4a16::GemmArgs g{a, b_q, scales, qzeros, bias, out, M, K, N, G, zp_bias, dtype};
   return run(g, pl, ds, (hipStream_t)stream);
 }
 
@@ -496,8 +500,16 @@ extern "C" {
 w4a16_status w4a16_gemm(const void* a, const int32_t* b_q, const void* scales,
                         const int32_t* qzeros, int32_t group_size, int32_t zp_bias, void* out,
                         int64_t M, int64_t K, int64_t N, int32_t dtype, void* stream) {
-  return gemm_common(a, b_q, scales, qzeros, group_size, zp_bias, out, M, K, N, dtype, nullptr,
-                     stream);
+  return gemm_common(a, b_q, scales, qzeros, group_size, zp_bias, nullptr, out, M, K, N, dtype,
+                     nullptr, stream);
+}
+
+w4a16_status w4a16_gemm_bias(const void* a, const int32_t* b_q, const void* scales,
+                             const int32_t* qzeros, int32_t group_size, int32_t zp_bias,
+                             const void* bias, void* out, int64_t M, int64_t K, int64_t N,
+                             int32_t dtype, void* stream) {
+  return gemm_common(a, b_q, scales, qzeros, group_size, zp_bias, bias, out, M, K, N, dtype,
+                     nullptr, stream);
 }
 
 w4a16_status w4a16_gemm_planned(const void* a, const int32_t* b_q, const void* scales,
@@ -505,8 +517,8 @@ w4a16_status w4a16_gemm_planned(const void* a, const int32_t* b_q, const void* s
                                 void* out, int64_t M, int64_t K, int64_t N, int32_t dtype,
                                 const w4a16_plan_t* plan, void* stream) {
   if (!plan) return fail(W4A16_ERR_NULL, "plan must be non-NULL");
-  return gemm_common(a, b_q, scales, qzeros, group_size, zp_bias, out, M, K, N, dtype, plan,
-                     stream);
+  return gemm_common(a, b_q, scales, qzeros, group_size, zp_bias, nullptr, out, M, K, N, dtype,
+                     plan, stream);
 }
 
 w4a16_status w4a16_plan(int64_t M, int64_t K, int64_t N, int32_t group_size, int32_t has_zp,

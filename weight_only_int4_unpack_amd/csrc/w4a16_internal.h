@@ -59,6 +59,7 @@ struct GemmArgs {
   const int32_t* b_q;
   const void* scales;
   const int32_t* qzeros;  // nullable
+  const void* bias;       // nullable: [N] in the activation dtype, added in fp32
   void* out;
   int64_t M, K, N;
   int32_t G, zp_bias, dtype;
@@ -70,6 +71,7 @@ struct DecodeParams {
   const uint32_t* bq;
   const uint16_t* sc;
   const uint32_t* qz;
+  const uint16_t* bias;  // nullable [N]
   uint16_t* out;
   float* ws;          // [S, M, N] fp32 partials (S > 1)
   int32_t* counters;  // [NB][4] arrival counters per wavefront, zero between launches
@@ -89,6 +91,7 @@ struct PrefillParams {
   const uint32_t* bq;
   const uint16_t* sc;
   const uint32_t* qz;
+  const uint16_t* bias;  // nullable [N] (unused when S > 1: the reduction adds it)
   uint16_t* out;
   int32_t M, K, N, G, zp_bias;
   int32_t g_shift;    // log2(G) when G is 32, 64 or 128 (unused when G == K)
@@ -100,6 +103,7 @@ struct PrefillParams {
 };
 struct PrefillReduceParams {
   const float* ws;    // [S][Mp][N] fp32 partials
+  const uint16_t* bias;  // nullable [N]
   uint16_t* out;      // [M][N]
   int32_t M, N, Mp, S;
 };

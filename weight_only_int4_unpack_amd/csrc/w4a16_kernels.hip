@@ -279,6 +279,17 @@ __device__ __forceinline__ void store_out4(T, uint16_t* dst, f32x4 v) {
                        (uint32_t)narrow(T{}, v[2]) | ((uint32_t)narrow(T{}, v[3]) << 16)};
 }
 
+// Bias of four adjacent output columns widened to fp32 (zeros without bias).
+// It is added to the fp32 result before the one rounding to the output type,
+// indexed by output column only (never by row).
+template <typename T>
+__device__ __forceinline__ f32x4 bias4(T, const uint16_t* bias, int col) {
+  if (bias == nullptr) return f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x2 b = *(const u32x2*)(bias + col);
+  return f32x4{widen(T{}, b.x & 0xFFFFu), widen(T{}, b.x >> 16), widen(T{}, b.y & 0xFFFFu),
+               widen(T{}, b.y >> 16)};
+}
+
 // One ring slot: the packed weights (8 rows x 2 words) and the activation
 // operand of one 32-row step.
 struct DecodeSlot {
@@ -554,9 +565,11 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
   }
   if (p.S == 1) {
     if (col_ok) {
+      const f32x4 bv = bias4(T{}, p.bias, col4);
 #pragma unroll
       for (int r = 0; r < RPT; ++r)
-        if (wv + 4 * r < M) store_out4(T{}, p.out + (int64_t)(wv + 4 * r) * p.N + col4, part[r]);
+        if (wv + 4 * r < M)
+          store_out4(T{}, p.out + (int64_t)(wv + 4 * r) * p.N + col4, part[r] + bv);
     }
     return;
   }
@@ -606,9 +619,11 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
       }
   }
   if (col_ok) {
+    const f32x4 bv = bias4(T{}, p.bias, col4);
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
-      if (wv + 4 * r < M) store_out4(T{}, p.out + (int64_t)(wv + 4 * r) * p.N + col4, sum[r]);
+      if (wv + 4 * r < M)
+        store_out4(T{}, p.out + (int64_t)(wv + 4 * r) * p.N + col4, sum[r] + bv);
   }
 }
 
@@ -937,12 +952,15 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
   };
   if constexpr (!SPLIT) {
     if (!col_ok) return;
+    const f32x4 bv = bias4(T{}, p.bias, ncol);
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = m0 + i * 16 + 4 * g + v;
-        if (row < p.M) store_out(row, acc[i][0][v], acc[i][1][v], acc[i][2][v], acc[i][3][v]);
+        if (row < p.M)
+          store_out(row, acc[i][0][v] + bv[0], acc[i][1][v] + bv[1], acc[i][2][v] + bv[2],
+                    acc[i][3][v] + bv[3]);
       }
     return;
   }
@@ -964,8 +982,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
 
 // ---------------------------------------------------------------------------
 // Prefill K-split reduction: out[m][n] = cast(sum over splits in order of
-// ws[s][m][n]); one thread per 4 adjacent outputs, all splits' loads in
-// flight at once (S <= 16).
+// ws[s][m][n] + bias[n]); one thread per 4 adjacent outputs, all splits'
+// loads in flight at once.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillReduceParams p) {
@@ -984,6 +1002,7 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillReduceParams
 #pragma unroll
   for (int s = 1; s < kPrefillMaxSplits; ++s)
     if (s < p.S) sum += v[s];
+  sum += bias4(T{}, p.bias, n);
   const uint32_t lo = (uint32_t)narrow(T{}, sum[0]) | ((uint32_t)narrow(T{}, sum[1]) << 16);
   const uint32_t hi = (uint32_t)narrow(T{}, sum[2]) | ((uint32_t)narrow(T{}, sum[3]) << 16);
   *(u32x2*)(p.out + (int64_t)m * p.N + n) = u32x2{lo, hi};

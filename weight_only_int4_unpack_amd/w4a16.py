@@ -66,6 +66,7 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     L.w4a16_gemm.argtypes = [vp, vp, vp, vp, i32, i32, vp, i64, i64, i64, i32, vp]
+    L.w4a16_gemm_bias.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, i64, i64, i64, i32, vp]
     L.w4a16_gemm_planned.argtypes = [vp, vp, vp, vp, i32, i32, vp, i64, i64, i64, i32,
                                      ctypes.POINTER(Plan), vp]
     L.w4a16_plan.argtypes = [i64, i64, i64, i32, i32, i32, i32, ctypes.POINTER(Plan)]
@@ -74,7 +75,7 @@ def lib() -> ctypes.CDLL:
     L.w4a16_dequant.argtypes = [vp, vp, vp, i32, i32, vp, i64, i64, i32, vp]
     L.w4a16_pack_int4.argtypes = [vp, i64, i64, vp]
     L.w4a16_unpack_int4.argtypes = [vp, i64, i64, vp]
-    for f in ("w4a16_gemm", "w4a16_gemm_planned", "w4a16_plan", "w4a16_plan_route",
+    for f in ("w4a16_gemm", "w4a16_gemm_bias", "w4a16_gemm_planned", "w4a16_plan", "w4a16_plan_route",
               "w4a16_dequant", "w4a16_pack_int4", "w4a16_unpack_int4"):
         getattr(L, f).restype = ctypes.c_int
     L.w4a16_last_error.restype = ctypes.c_char_p
@@ -139,9 +140,19 @@ def _shapes(a, b_q, scales, qzeros, group_size):
 
 def gemm(a: torch.Tensor, b_q: torch.Tensor, scales: torch.Tensor,
          qzeros: torch.Tensor | None = None, group_size: int = 128, zp_bias: int = 8,
-         out: torch.Tensor | None = None, plan: Plan | None = None) -> torch.Tensor:
-    """``a @ dequant(b_q, scales, qzeros)`` on the GPU, in ``a``'s dtype."""
+         out: torch.Tensor | None = None, plan: Plan | None = None,
+         bias: torch.Tensor | None = None) -> torch.Tensor:
+    """``a @ dequant(b_q, scales, qzeros) (+ bias)`` on the GPU, in ``a``'s dtype.
+
+    ``bias`` (optional, ``[N]`` in ``a``'s dtype) is added to the fp32 result
+    before the cast (PR #40977 "RDNA hybrid W4A16", Code section)."""
     M, K, N = _shapes(a, b_q, scales, qzeros, group_size)
+    if bias is not None:
+        if plan is not None:
+            raise ValueError("a forced plan runs without bias")
+        if (bias.dim() != 1 or bias.shape[0] != N or bias.dtype != a.dtype
+                or bias.device != a.device or not bias.is_contiguous()):
+            raise ValueError(f"bias must be a contiguous [{N}] tensor of a's dtype and device")
     if out is None:
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
     elif (tuple(out.shape) != (M, N) or out.dtype != a.dtype or out.device != a.device
@@ -149,10 +160,10 @@ def gemm(a: torch.Tensor, b_q: torch.Tensor, scales: torch.Tensor,
         raise ValueError("out must be a contiguous [M, N] tensor like a")
     args = gemm_args(a, b_q, scales, qzeros, group_size, zp_bias, out)
     if a.device.index == torch.cuda.current_device():
-        _run_gemm(args, plan)
+        _run_gemm(args, plan, bias)
     else:
         with torch.cuda.device(a.device):
-            _run_gemm(args, plan)
+            _run_gemm(args, plan, bias)
     return out
 
 
@@ -166,9 +177,11 @@ def gemm_args(a, b_q, scales, qzeros, group_size, zp_bias, out):
             M, K, N, _DTYPE_CODE[a.dtype], _stream(a.device))
 
 
-def _run_gemm(args, plan):
+def _run_gemm(args, plan, bias=None):
     L = lib()
-    if plan is None:
+    if bias is not None:
+        _check(L.w4a16_gemm_bias(*args[:6], _ptr(bias), *args[6:]))
+    elif plan is None:
         _check(L.w4a16_gemm(*args))
     else:
         _check(L.w4a16_gemm_planned(*args[:-1], ctypes.byref(plan), args[-1]))
