@@ -6,3 +6,4 @@ a missing build raises immediately: there is no fallback path.
 """
 from . import synthetic  # noqa: F401  (random inputs only; no arithmetic)
 from . import w4a16  # noqa: F401  (binding; loads the library on first call)
+from . import op  # noqa: F401  (registers torch.ops.w4a16.gemm; calls go through the binding)
