@@ -99,13 +99,13 @@ struct PrefillParams {
   int32_t band;       // tile rows per band of the workgroup -> tile order
   int32_t S;          // K splits (1: no cross-workgroup hand-off)
   int32_t kt_split;   // 64-row K stages per split
-  float* ws;          // fp32 partials [S][tiles_m * 64][N] (S > 1)
+  float* ws;          // fp32 partials [S][M][N] (S > 1)
 };
 struct PrefillReduceParams {
-  const float* ws;    // [S][Mp][N] fp32 partials
+  const float* ws;    // [S][M][N] fp32 partials
   const uint16_t* bias;  // nullable [N]
   uint16_t* out;      // [M][N]
-  int32_t M, N, Mp, S;
+  int32_t M, N, S;
 };
 
 struct DequantParams {

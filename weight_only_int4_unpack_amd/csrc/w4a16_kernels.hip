@@ -964,17 +964,18 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
       }
     return;
   }
-  // ---- K split: this split's fp32 partial goes to ws[split][row][col] (rows
-  // padded to whole tiles); prefill_reduce_kernel, launched next on the same
-  // stream, adds the splits in order.
+  // ---- K split: this split's fp32 partial goes to ws[split][row][col] for
+  // the M real rows only (rows of the tile past M are never written);
+  // prefill_reduce_kernel, launched next on the same stream, adds the splits
+  // in order.
   if constexpr (SPLIT) {
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int row = m0 + i * 16 + 4 * g + v;
-      float* d = p.ws + ((int64_t)split * p.tiles_m * BM + row) * p.N + ncolc;
-      if (col_ok)
+      float* d = p.ws + ((int64_t)split * p.M + row) * p.N + ncolc;
+      if (col_ok && row < p.M)
         *(f32x4*)d = f32x4{acc[i][0][v], acc[i][1][v], acc[i][2][v], acc[i][3][v]};
     }
   }
@@ -992,7 +993,7 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillReduceParams
   if (q >= (int64_t)p.M * N4) return;
   const int m = (int)(q / N4);
   const int n = (int)(q - (int64_t)m * N4) * 4;
-  const int64_t split_stride = (int64_t)p.Mp * p.N;
+  const int64_t split_stride = (int64_t)p.M * p.N;
   const float* src = p.ws + (int64_t)m * p.N + n;
   f32x4 v[kPrefillMaxSplits];
 #pragma unroll
