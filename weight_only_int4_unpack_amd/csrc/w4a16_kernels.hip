@@ -794,7 +794,22 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
     constexpr int POS = decltype(posc)::value;
     constexpr bool closes = GS > 0 && (POS + 1) % (GS > 0 ? GS : 1) == 0;
     const int k0 = kt * kPrefillBK + 32 * half;
-    if (KM == 0 || kt < KF) {
+    if ((KM == 0 || kt < KF) && GS >= 2) {
+      // buffer loads: a resource based at row k0 (scalar), the lane's fixed
+      // byte offset, and a scalar row offset per load, so that no load needs
+      // vector address arithmetic (global loads here cost one 64-bit add
+      // each; bf16 G = 128 at the 2048 x 5120 x 17408 shape: 439 -> 425 us).
+      // With one slab per group (GS = 1) the kernel sits at the register
+      // limit and the compiler then issues these loads one pair at a time,
+      // so that case, and the per-channel one (GS = 0, not measured faster),
+      // keep the global loads below.
+      const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((const char*)p.bq + (int64_t)k0 * (N4 * 2)), 0, -1, 0x00020000);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        sl.q[r] = u16x2{__builtin_amdgcn_raw_buffer_load_b16(br, (int)b_off, (2 * r) * (N4 * 2), 0),
+                        __builtin_amdgcn_raw_buffer_load_b16(br, (int)b_off, (2 * r + 1) * (N4 * 2), 0)};
+    } else if (KM == 0 || kt < KF) {
       const char* rb = (const char*)p.bq + (int64_t)k0 * (N4 * 2);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
