@@ -177,6 +177,22 @@ __device__ __forceinline__ u32x4 int_op(const uint32_t* y, const DqRegs& mag, ui
   return u32x4{int_pair<E>(y[0], mag, bias), int_pair<E>(y[1], mag, bias),
                int_pair<E>(y[2], mag, bias), int_pair<E>(y[3], mag, bias)};
 }
+// fp16 operand RNE((q - z) * s) of column e: the exact integer q - z (as in
+// int_op) times the scale in one packed multiply, which rounds once. Same
+// value as exact_pair (and the oracle's rounded tile), with the bias and the
+// scale pair built from bits.
+template <int E>
+__device__ __forceinline__ u32x4 tile_op(const uint32_t* y, const DqRegs& mag, uint32_t z,
+                                         uint32_t s_bits) {
+  const uint32_t b = (E & 1) ? (0x5400u | (z << 4)) : (0x6400u | z);
+  const f16x2 bias = __builtin_bit_cast(f16x2, b * 0x10001u);
+  const f16x2 sc = __builtin_bit_cast(f16x2, (s_bits & 0xFFFFu) * 0x10001u);
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, int_pair<E>(y[i], mag, bias)) * sc);
+  return r;
+}
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -720,9 +736,18 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
   const DqRegs mag = dq_regs(p.dq);
   const u32x4 ones = u32x4{T::kOnePair, T::kOnePair, T::kOnePair, T::kOnePair};
   const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
-  // fp16: the operand is the exact integer q - z (one packed subtract or FMA
-  // per pair), so no activation sums are needed; bf16 keeps base + q.
-  constexpr bool kIntOp = T::kIsF16;
+  // Unsplit fp16 with groups of 32 or 64 rows (GS = 1, 2): the operand is
+  // the weight itself, RNE_fp16((q - z) * s) (relative error 2^-11 per
+  // weight), so no per-group fold is needed; folding every 32 or 64 rows made
+  // these shapes bound by the fold's fp32 FMAs (4096^3, G = 32: 207 -> 187
+  // us). The K-split kernel serves small, latency-bound tile counts, where
+  // the scale multiply in front of the MFMAs measured slower than the fold
+  // behind them (M = 256: 33.5 -> 38.9 us), so it keeps the integer operand.
+  // Other fp16 groups: the operand is the exact integer q - z (one packed
+  // subtract or FMA per pair), so no activation sums are needed; bf16 keeps
+  // base + q.
+  constexpr bool kTile = T::kIsF16 && (GS == 1 || GS == 2) && !SPLIT;
+  constexpr bool kIntOp = T::kIsF16 && !kTile;
 
   f32x4 acc[MB][4];   // output accumulator
   f32x4 part[MB][4];  // current group's sum of a (base + q)   (GS > 0)
@@ -824,13 +849,13 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
       }
     }
     const int grp = GS == 0 ? 0 : (min(k0, p.K - 1) >> p.g_shift);
-    if constexpr (closes) {
+    if constexpr (closes || kTile) {
       sl.s = ldg<u32x2>((const char*)p.sc + (int64_t)grp * p.N * 2, s_off);
       sl.valid = KM == 0 || k0 < p.K;
     }
     // zero points: where the scale is applied (factored form), or with every
-    // slab's weights (fp16 integer operand)
-    if constexpr (HAS_ZP && (closes || kIntOp))
+    // slab's weights (fp16 integer or weight operand)
+    if constexpr (HAS_ZP && (closes || kIntOp || kTile))
       sl.z = ldg<uint16_t>((const char*)p.qz + (int64_t)grp * N4 * 2, z_off);
   };
   // Fold a group's partial into the output accumulator (scales s_bits of the
@@ -869,7 +894,22 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
 #pragma unroll
     for (int r = 0; r < 4; ++r) Y[r] = __builtin_bit_cast(uint32_t, sl.q[r]);
     u32x4 bop[4];
-    if constexpr (kIntOp) {
+    if constexpr (kTile) {
+      // rows past K (K tail) meet zero activations; their clamped weights and
+      // scales are finite, so they add exact zeros
+      const uint32_t z4 = HAS_ZP ? sl.z : (uint32_t)p.zp_bias * 0x1111u;
+      bop[0] = tile_op<0>(Y, mag, nib(z4, 0), sl.s.x);
+      bop[1] = tile_op<1>(Y, mag, nib(z4, 1), sl.s.x >> 16);
+      bop[2] = tile_op<2>(Y, mag, nib(z4, 2), sl.s.y);
+      bop[3] = tile_op<3>(Y, mag, nib(z4, 3), sl.s.y >> 16);
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const u32x4 aop = *(const u32x4*)&As[buf][(i * 16 + c) * RH + ks * 32 + 8 * g];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][e] = mfma<T>(aop, bop[e], acc[i][e]);
+      }
+      return;
+    } else if constexpr (kIntOp) {
       const uint32_t z4 = HAS_ZP ? sl.z : (uint32_t)p.zp_bias * 0x1111u;
       bop[0] = int_op<0>(Y, mag, nib(z4, 0));
       bop[1] = int_op<1>(Y, mag, nib(z4, 1));
