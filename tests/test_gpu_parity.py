@@ -104,6 +104,25 @@ def test_prefill_tiles_parity(K, G, dtype, zp):
     assert_within_tolerance(got, p.oracle_gemm(), dtype, f"K={K} G={G} {dtype} zp={zp}")
 
 
+# bf16 prefill with groups of 128 over a long K (8576 = 67 groups), unsplit
+# and with forced K splits of 35 and 3 groups, so that splits start at group
+# offsets other than 0; tolerance against the oracle and the exact-arithmetic
+# case bit for bit.
+@pytest.mark.parametrize("stages", [0, 70, 6])
+def test_prefill_bf16_long_k_splits(stages):
+    M, K, N, G = 100, 8576, 520, 128
+    p = random_problem(M, K, N, G, "bf16", False, seed=300 + stages)
+    plan = W.plan(M, K, N, G, False, torch.bfloat16, route=W.ROUTE_PREFILL,
+                  steps_per_wave=stages if stages else K // 64)
+    assert plan.splits == (1 if stages == 0 else -(-(K // 64) // stages))
+    got = dev_to_bits(p.gpu_gemm(plan=plan))
+    assert_within_tolerance(got, p.oracle_gemm(), "bf16", f"stages={stages}")
+    q = _exact_problem(M, K, N, G, "bf16", False, seed=310 + stages)
+    got = dev_to_bits(q.gpu_gemm(plan=plan))
+    want = q.oracle_gemm()
+    assert np.array_equal(got, want), f"stages={stages}: {int((got != want).sum())} differ"
+
+
 # ---------------------------------------------------------------- workloads
 def _check_workload(name, rows=None, cols=None, routes=True):
     p = workload_problem(name)
