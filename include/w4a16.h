@@ -24,6 +24,7 @@
  *                     bits [4j, 4j+4) (LSB first)
  *   scales  [K/G, N]  same dtype as a
  *   qzeros  [K/G, N/8] int32 packed like b_q, or NULL (symmetric: z = zp_bias)
+ *   bias    [N]       same dtype as a, or NULL (w4a16_gemm_bias only)
  *   out     [M, N]    same dtype as a
  *
  * Conventions:

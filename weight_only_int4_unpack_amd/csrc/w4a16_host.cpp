@@ -272,7 +272,7 @@ struct DeviceState {
   int num_cus = 0;
   float* partials = nullptr;      // decode split-K fp32 partials, [S, M, N]
   size_t partial_bytes = 0;
-  float* prefill_ws = nullptr;    // prefill K-split fp32 partials, [S, M_pad, N]
+  float* prefill_ws = nullptr;    // prefill K-split fp32 partials, [S, M, N]
   size_t prefill_bytes = 0;
   int32_t* counters = nullptr;    // arrival counters, one per (column block, wavefront)
   size_t counter_n = 0;
