@@ -299,9 +299,11 @@ def main():
                       "launches": res},
         }
         if names == ["decode_m1", "decode_m5"] and not args.no_prefill_extra:
-            _, pg, pres = run_workload(["prefill"], 10, 2, rotate, torch, W, synthetic)
+            # 20 graph-replayed steps after 10 warm-up launches (the first
+            # launches of a fresh process run measurably slower)
+            _, pg, pres = run_workload(["prefill"], 20, 10, rotate, torch, W, synthetic)
             pf = pres[0]
-            pus = 1e3 * pg / 10
+            pus = 1e3 * pg / 20
             tf = pf["flops"] / (pus * 1e-6) / 1e12
             line["extra"] = {"prefill": {"tflops": round(tf, 1),
                                          "frac_of_mfma_peak": round(tf / MFMA_PEAK_TFLOPS, 4),
