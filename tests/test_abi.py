@@ -161,10 +161,14 @@ def test_selector_decode_shapes():
     assert p.steps_per_wave == 4 and p.decode_mode == 1 and p.grid == 680
     assert W.plan(1, 5120, 17408, 128, False, torch.bfloat16, route=W.ROUTE_DECODE,
                   steps_per_wave=8).decode_mode == 2
-    # K = 2112 is 66 steps of 32 rows; fp16 with groups of 64 folds the scale
+    # K = 2112 is 66 steps of 32 rows; groups of 64 hold a wavefront's 2 steps,
+    # so the exact operand with one in-place fold (mode 1) applies
     p = W.plan(8, 2112, 5120, 64, True, torch.float16)
     assert p.splits * 4 * p.steps_per_wave >= 66
-    assert p.decode_mode == 0
+    assert p.steps_per_wave == 2 and p.decode_mode == 1
+    # fp16 groups of 32 with 2 steps per wavefront: the rounded weight (mode 0)
+    q = W.plan(1, 4096, 4096, 32, True, torch.float16)
+    assert q.steps_per_wave == 2 and q.decode_mode == 0
     assert p.workspace_bytes >= p.splits * 8 * 5120 * 4 or p.splits == 1
     # partials of 4 wavefronts, then scales and packed zeros of the staged groups
     ng = 4 * p.steps_per_wave // 2 + 1

@@ -111,9 +111,14 @@ w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dty
   if (!aligned && L > 1)
     return fail(W4A16_ERR_PLAN, "N %% 16 or K %% 8 nonzero: decode runs one step per wavefront");
   auto fits_one_of = [&](int64_t l) { return one_group || (SG >= l && SG % l == 0); };
+  // One group per wavefront: mode 1 (exact operand, one in-place fold after
+  // the stream). Otherwise fp16 with groups of up to 64 rows feeds the rounded
+  // weight (mode 0), and the rest fold per group (mode 2). (Measured on
+  // MI355X: K=2112, N=5120, fp16, G=64, M=8: mode 1 9.45 us, mode 0 10.7 us;
+  // K=N=4096, fp16, G=32, 2 steps per wavefront: mode 0 8.9 us, mode 2 9.6 us.)
   auto auto_mode = [&](int64_t l) {
-    if (dtype == W4A16_F16 && G <= 64 && !one_group) return 0;
-    return fits_one_of(l) ? 1 : 2;
+    if (fits_one_of(l)) return 1;
+    return (dtype == W4A16_F16 && G <= 64) ? 0 : 2;
   };
   if (L == 0) {
     // Among the L whose whole grid is resident at once (wavefronts per SIMD:
