@@ -147,6 +147,12 @@ def test_selector_routes_on_runtime_m():
     for M in (9, 16, 17, 64, 256, 2048, 4096):
         assert W.plan(M, 4096, 4096, 32, True, torch.float16).route == W.ROUTE_PREFILL
     assert W.plan(0, 4096, 4096, 32, True, torch.float16).route == W.ROUTE_NONE
+    # per-channel scales: decode up to 16 rows, with fewer splits above 8 rows
+    for M in (9, 12, 16):
+        p = W.plan(M, 4096, 4096, 4096, True, torch.float16)
+        assert p.route == W.ROUTE_DECODE and p.decode_mode == 1 and p.steps_per_wave == 4
+    assert W.plan(8, 4096, 4096, 4096, True, torch.float16).steps_per_wave == 2
+    assert W.plan(17, 4096, 4096, 4096, True, torch.float16).route == W.ROUTE_PREFILL
 
 
 def test_selector_decode_shapes():

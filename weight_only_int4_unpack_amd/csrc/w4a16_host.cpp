@@ -132,7 +132,11 @@ w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dty
     L = 1;
     if (aligned) {
       const double bytes = (double)K * (double)N / 2.0;
-      const double target = std::max<double>((double)NB, bytes / 32768.0);
+      // above 8 rows each split's hand-off carries twice the partials: aim at
+      // half the workgroups (K = N = 4096, M = 16: 4 steps per wavefront,
+      // 8 splits, 16.2 us, against 17.2 us with 2 steps and 16 splits)
+      const double target = std::max<double>((double)NB, bytes / 32768.0) /
+                            (M > w4a16::kAutoDecodeMaxM ? 2.0 : 1.0);
       double best = 1e300;
       bool any = false;
       for (int64_t l = 1; l <= kDecodeMaxSteps; l *= 2) {
@@ -240,7 +244,14 @@ w4a16_status make_plan(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype
     pl->route = W4A16_ROUTE_NONE;
     return W4A16_OK;
   }
-  if (route == 0) route = (M <= w4a16::kAutoDecodeMaxM) ? W4A16_ROUTE_DECODE : W4A16_ROUTE_PREFILL;
+  // Decode for M <= 8; per-channel scales (one group) also up to 16 rows,
+  // where the decode kernel's single in-place fold beat the prefill's K-split
+  // route (K = N = 4096, M = 16: 12.0 vs 12.9 us; M = 12: 11.4 vs 12.5 us).
+  // With groups of 32 the prefill route stays faster at M = 12 and 16.
+  if (route == 0)
+    route = (M <= w4a16::kAutoDecodeMaxM || (M <= w4a16::kDecodeMaxM && (int64_t)G == K))
+                ? W4A16_ROUTE_DECODE
+                : W4A16_ROUTE_PREFILL;
   if (route == W4A16_ROUTE_DECODE) {
     if (M > w4a16::kDecodeMaxM)
       return fail(W4A16_ERR_PLAN, "decode route needs M <= %d (got %lld)", w4a16::kDecodeMaxM,
