@@ -139,7 +139,8 @@ def time_graph(launches, steps, torch):
                 for L in launches:
                     L()
     torch.cuda.synchronize()
-    g.replay()                      # untimed warm replay
+    for _ in range(3):              # untimed warm replays (clocks settle)
+        g.replay()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
