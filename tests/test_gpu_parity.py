@@ -123,6 +123,17 @@ def test_prefill_bf16_long_k_splits(stages):
     assert np.array_equal(got, want), f"stages={stages}: {int((got != want).sum())} differ"
 
 
+# per-channel scales take the decode route up to 16 rows (fewer splits above
+# 8 rows); aligned and ragged shapes, through the selector's own plan
+@pytest.mark.parametrize("M", [9, 12, 16])
+@pytest.mark.parametrize("K,N,dtype", [(4096, 4096, "fp16"), (2120, 520, "bf16")])
+def test_per_channel_decode_route_mid_m(M, K, N, dtype):
+    p = random_problem(M, K, N, K, dtype, True, seed=400 + M + K)
+    plan = W.plan(M, K, N, K, True, TORCH_DT[dtype])
+    assert plan.route == W.ROUTE_DECODE and plan.decode_mode == 1
+    assert_within_tolerance(dev_to_bits(p.gpu_gemm()), p.oracle_gemm(), dtype, f"M={M} K={K}")
+
+
 # ---------------------------------------------------------------- workloads
 def _check_workload(name, rows=None, cols=None, routes=True):
     p = workload_problem(name)
