@@ -38,7 +38,19 @@ and section; "Code" is the page's key-source-snippet section):
   set {32, 64, 128} is not printed on the pages; it is the reading taken for
   the group sizes this build serves.
 
-Pins: every function here is checked by ``tests/test_oracle.py`` against
+* K-packed layout (the hybrid path's single weight buffer; PR #40977 "RDNA
+  hybrid W4A16", Impl. item 4 and the Code section's module docstring):
+  int32 ``[N, K/8]``, eight K values of one column per word, in ExLlama's
+  shuffled nibble order. The pages name the order but do not print it. The
+  reading taken here is the one the shuffle exists for: nibble p holds K
+  offset ``(0, 2, 4, 6, 1, 3, 5, 7)[p]``, so that masking the word shifted
+  right by 4i with 0x000F000F leaves K values 2i and 2i+1 in the two 16-bit
+  halves, a packed pair of consecutive K. Scales are ``[N, K/G]`` and zero
+  points, when given, ``[N, K/G]`` uint8 (values 0..15), column-major like
+  the weights (the test's reference takes ``[N, K//G]`` scales and zero
+  points, Code section); the zero points' storage type is not given and
+  one byte each is the reading taken.
+* Pins: every function here is checked by ``tests/test_oracle.py`` against
 facts other than itself (printed pack vectors of the stated convention,
 closed forms, invariants, torch's own bf16/fp16 casts, exact integer
 arithmetic and an fp64 brute force). No function is "parity unpinned".
@@ -247,6 +259,76 @@ def bruteforce_f64(a_bits, b_q, scales_bits, qzeros, group_size: int,
                 acc += float(A[m, k]) * float(q - z) * float(S[g, n])
             out[m, n] = acc if B is None else acc + float(B[n])
     return out
+
+
+# --------------------------------------------------------------------------
+# K-packed layout [N, K/8] with the ExLlama nibble order
+# --------------------------------------------------------------------------
+EXLLAMA_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)  # K offset held by nibble p of a word
+
+
+def pack_int4_kshuffle(q_nk) -> np.ndarray:
+    """uint4 ``[N, K]`` (0..15, K % 8 == 0) -> int32 ``[N, K/8]``: word c of
+    row n holds K values 8c..8c+7, nibble p holding offset EXLLAMA_ORDER[p]."""
+    q = np.asarray(q_nk)
+    if q.ndim != 2 or q.shape[1] % 8 != 0:
+        raise ValueError("q must be [N, K] with K a multiple of 8")
+    if q.size and (q.min() < 0 or q.max() > 15):
+        raise ValueError("values must lie in 0..15")
+    g = q.astype(np.uint32).reshape(q.shape[0], q.shape[1] // 8, 8)
+    w = np.zeros(g.shape[:2], dtype=np.uint32)
+    for p, off in enumerate(EXLLAMA_ORDER):
+        w |= g[:, :, off] << np.uint32(4 * p)
+    return w.view(np.int32)
+
+
+def unpack_int4_kshuffle(w_nk8) -> np.ndarray:
+    """int32 ``[N, K/8]`` -> uint8 ``[N, K]``, inverse of pack_int4_kshuffle."""
+    w = np.asarray(w_nk8, dtype=np.int32).view(np.uint32)
+    out = np.zeros((w.shape[0], w.shape[1], 8), dtype=np.uint8)
+    for p, off in enumerate(EXLLAMA_ORDER):
+        out[:, :, off] = (w >> np.uint32(4 * p)) & np.uint32(15)
+    return out.reshape(w.shape[0], w.shape[1] * 8)
+
+
+def dequant_kpacked_fp32(w_nk8, scales_nkg_bits, zeros_nkg, group_size: int,
+                         zp_bias: int, dtype: str, cols=None) -> np.ndarray:
+    """W32[k, n] = (q[n, k] - z[n, k // G]) * s[n, k // G] in fp32, returned
+    as ``[K, N]`` (the orientation of the product); ``cols`` optionally
+    selects output columns."""
+    w = np.asarray(w_nk8, dtype=np.int32)
+    if cols is not None:
+        cols = np.asarray(cols, dtype=np.int64)
+        w = w[cols]
+    Q = unpack_int4_kshuffle(w).astype(np.float32)          # [n, K]
+    S = to_f32(scales_nkg_bits, dtype)
+    if cols is not None:
+        S = S[cols]
+    if zeros_nkg is None:
+        Z = np.full(S.shape, float(zp_bias), dtype=np.float32)
+    else:
+        Z = np.asarray(zeros_nkg, dtype=np.uint8)
+        Z = (Z[cols] if cols is not None else Z).astype(np.float32)
+    g = np.arange(Q.shape[1]) // group_size
+    return ((Q - Z[:, g]) * S[:, g]).T
+
+
+def gemm_kpacked(a_bits, w_nk8, scales_nkg_bits, zeros_nkg, group_size: int,
+                 zp_bias: int, dtype: str, rows=None, cols=None,
+                 bias_bits=None) -> np.ndarray:
+    """Output bits of ``A @ W (+ bias)`` for K-packed weights: fp32 product,
+    bias added in fp32 by column, one RNE cast (as ``gemm``)."""
+    A = to_f32(a_bits, dtype)
+    if rows is not None:
+        A = A[np.asarray(rows, dtype=np.int64)]
+    C = A @ dequant_kpacked_fp32(w_nk8, scales_nkg_bits, zeros_nkg, group_size,
+                                 zp_bias, dtype, cols=cols)
+    if bias_bits is not None:
+        b = to_f32(bias_bits, dtype)
+        if cols is not None:
+            b = b[np.asarray(cols, dtype=np.int64)]
+        C = C + b[None, :]
+    return rne_bits(C, dtype)
 
 
 def within_tolerance(got_bits, want_bits, dtype: str,

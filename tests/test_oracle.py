@@ -264,6 +264,83 @@ def test_bruteforce_fp64_tiny(dtype, has_zp, G):
     assert np.all(np.abs(C32 - C64) <= bound)
 
 
+# ------------------------------------------------- K-packed (ExLlama) layout
+def test_kshuffle_printed_vector():
+    # K values 0..7 in order: nibbles p = 0..7 hold offsets 0,2,4,6,1,3,5,7,
+    # so the hex digits read from the top are 7,5,3,1,6,4,2,0
+    w = O.pack_int4_kshuffle(np.arange(8, dtype=np.uint8)[None, :])
+    assert int(w[0, 0]) == 0x75316420
+    assert O.unpack_int4_kshuffle(np.array([[0x75316420]], np.int32)).tolist() == [list(range(8))]
+
+
+def test_kshuffle_pairs_are_consecutive_k():
+    # the property the shuffle exists for: (word >> 4i) & 0x000F000F holds K
+    # values 2i (low half) and 2i + 1 (high half) of the word's eight
+    rng = np.random.default_rng(7)
+    q = rng.integers(0, 16, size=(11, 64), dtype=np.uint8)
+    w = O.pack_int4_kshuffle(q).view(np.uint32).astype(np.int64)
+    for c in range(8):
+        for i in range(4):
+            pair = (w[:, c] >> (4 * i)) & 0x000F000F
+            assert np.array_equal(pair & 0xFFFF, q[:, 8 * c + 2 * i])
+            assert np.array_equal(pair >> 16, q[:, 8 * c + 2 * i + 1])
+
+
+def test_kshuffle_roundtrip_and_rejections():
+    rng = np.random.default_rng(8)
+    q = rng.integers(0, 16, size=(5, 96), dtype=np.uint8)
+    assert np.array_equal(O.unpack_int4_kshuffle(O.pack_int4_kshuffle(q)), q)
+    x = rng.integers(-2**31, 2**31, size=(7, 9), dtype=np.int64).astype(np.int32)
+    assert np.array_equal(O.pack_int4_kshuffle(O.unpack_int4_kshuffle(x)), x)
+    with pytest.raises(ValueError):
+        O.pack_int4_kshuffle(np.zeros((2, 12), np.uint8))
+    with pytest.raises(ValueError):
+        O.pack_int4_kshuffle(np.full((1, 8), 16, np.int32))
+
+
+@pytest.mark.parametrize("dtype,has_zp,G", [(O.BF16, False, 128), (O.F16, True, 32),
+                                            (O.BF16, True, 64), (O.F16, False, 256)])
+def test_kpacked_matches_bruteforce_of_same_weights(dtype, has_zp, G):
+    # the same uint4 matrix stored both ways: the K-packed dequantisation is
+    # the N-packed one transposed, and the product agrees with the fp64 brute
+    # force (which pulls each weight from its N-packed word with shifts)
+    M, K, N = 3, 256, 24
+    d, b_q, qz = _rand_problem(M, K, N, G, dtype, has_zp, 11)
+    w = O.pack_int4_kshuffle(d["q"].T)
+    s_nk = np.ascontiguousarray(d["s_bits"].T)
+    z_nk = None if d["z"] is None else np.ascontiguousarray(d["z"].T).astype(np.uint8)
+    W_k = O.dequant_kpacked_fp32(w, s_nk, z_nk, G, 8, dtype)
+    W_n = O.dequant_fp32(b_q, d["s_bits"], qz, G, 8, dtype)
+    assert np.array_equal(W_k, W_n)
+    C64 = O.bruteforce_f64(d["a_bits"], b_q, d["s_bits"], qz, G, 8, dtype)
+    got = O.to_f32(O.gemm_kpacked(d["a_bits"], w, s_nk, z_nk, G, 8, dtype), dtype)
+    assert np.all(np.abs(got - C64) <= 2.0 ** -7 * np.abs(C64) + 1e-6)
+
+
+def test_kpacked_columns_bias_and_integers():
+    # exact integer case: a, q - z and s = 1/4 make every product exact, so the
+    # output (with an integer bias, by column) equals exact integer arithmetic
+    rng = np.random.default_rng(12)
+    M, K, N, G = 2, 64, 16, 32
+    a = rng.integers(-3, 4, size=(M, K)).astype(np.float32)
+    q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    z = rng.integers(0, 16, size=(N, K // G), dtype=np.uint8)
+    s = O.rne_bits(np.full((N, K // G), 0.25, np.float32), O.BF16)
+    bias = rng.integers(-5, 6, size=N).astype(np.float32)
+    out = O.gemm_kpacked(O.rne_bits(a, O.BF16), O.pack_int4_kshuffle(q), s, z, G, 8, O.BF16,
+                         bias_bits=O.rne_bits(bias, O.BF16))
+    exact = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            exact[m, n] = sum(int(a[m, k]) * (int(q[n, k]) - int(z[n, k // G])) for k in range(K)) / 4 + bias[n]
+    assert np.all(np.abs(exact) < 256)          # exactly representable in bf16
+    assert np.array_equal(O.to_f32(out, O.BF16), exact.astype(np.float32))
+    cols = [15, 0, 7]
+    sub = O.gemm_kpacked(O.rne_bits(a, O.BF16), O.pack_int4_kshuffle(q), s, z, G, 8, O.BF16,
+                         cols=cols, bias_bits=O.rne_bits(bias, O.BF16))
+    assert np.array_equal(sub, out[:, cols])
+
+
 # ---------------------------------------------------------------- bias
 @pytest.mark.parametrize("dtype", [O.F16, O.BF16])
 def test_bias_alone_when_product_is_zero(dtype):
