@@ -184,6 +184,50 @@ w4a16_status w4a16_pack_int4(const uint8_t* q, int64_t rows, int64_t cols,
 w4a16_status w4a16_unpack_int4(const int32_t* packed, int64_t rows,
                                int64_t cols, uint8_t* q);
 
+/*
+ * w4a16_gemm_kpacked - the same product for weights stored K-packed, the
+ * hybrid path's single buffer (PR #40977 "RDNA hybrid W4A16", Impl. item 4
+ * and the Code section's module docstring):
+ *   w       [N, K/8] int32: word c of row n holds K values 8c..8c+7 of
+ *           column n in ExLlama order, nibble p (bits [4p, 4p+4)) holding
+ *           K offset 0, 2, 4, 6, 1, 3, 5, 7 for p = 0..7, so that nibbles
+ *           i and i+4 are K values 2i and 2i+1
+ *           (w4a16_pack_int4_kshuffle writes it)
+ *   scales  [N, K/G] in `dtype`
+ *   zeros   [N, K/G] uint8 (values 0..15), or NULL (z = zp_bias)
+ *   bias    [N] in `dtype`, or NULL; added to the fp32 result
+ *   a [M, K] and out [M, N] as for w4a16_gemm.
+ * out[m,n] = RNE(fp32(sum_k a[m,k] (q[n,k] - z[n,k/G]) s[n,k/G]) + bias[n]).
+ * K must be a multiple of 32 (G in {32, 64, 128, K}); N is any positive
+ * size. a, w, scales, out and bias must be 16-byte aligned; zeros need no
+ * alignment. Device pointers, owned by the caller; only out is written.
+ * One launch, no scratch memory, no allocation; any M (16-row blocks).
+ * Errors: NULL, SHAPE, GROUP, DTYPE, ZP, ALIGN, DEVICE, HIP.
+ */
+w4a16_status w4a16_gemm_kpacked(const void* a, const int32_t* w,
+                                const void* scales, const uint8_t* zeros,
+                                int32_t group_size, int32_t zp_bias,
+                                const void* bias, void* out, int64_t M,
+                                int64_t K, int64_t N, int32_t dtype,
+                                void* stream);
+
+/*
+ * w4a16_pack_int4_kshuffle - host utility: q [N, K] uint8 values 0..15 ->
+ * packed [N, K/8] int32 in the K-packed ExLlama order of
+ * w4a16_gemm_kpacked (PR #40977 "RDNA hybrid W4A16", key files and symbols:
+ * the packing helper and its layout test). Host pointers.
+ * Errors: NULL, SHAPE (K % 8), VALUE.
+ */
+w4a16_status w4a16_pack_int4_kshuffle(const uint8_t* q, int64_t N, int64_t K,
+                                      int32_t* packed);
+
+/*
+ * w4a16_unpack_int4_kshuffle - host inverse of w4a16_pack_int4_kshuffle.
+ * Host pointers. Errors: NULL, SHAPE.
+ */
+w4a16_status w4a16_unpack_int4_kshuffle(const int32_t* packed, int64_t N,
+                                        int64_t K, uint8_t* q);
+
 /* Message of the calling thread's last failed call ("" if none). */
 const char* w4a16_last_error(void);
 

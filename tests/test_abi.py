@@ -20,7 +20,8 @@ def test_library_exports_every_header_symbol():
     names = W.header_functions()
     assert {"w4a16_gemm", "w4a16_gemm_bias", "w4a16_gemm_planned", "w4a16_plan", "w4a16_plan_route",
             "w4a16_dequant", "w4a16_pack_int4", "w4a16_unpack_int4", "w4a16_last_error",
-            "w4a16_version"} <= set(names)
+            "w4a16_version", "w4a16_gemm_kpacked", "w4a16_pack_int4_kshuffle",
+            "w4a16_unpack_int4_kshuffle"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert W.version().startswith("w4a16-gfx950")
@@ -54,8 +55,60 @@ def test_pack_errors():
     assert L.w4a16_pack_int4(None, 0, 8, None) == W.OK       # empty is fine
 
 
+def test_kshuffle_pack_matches_oracle_bitwise():
+    rng = np.random.default_rng(6)
+    q = rng.integers(0, 16, size=(129, 512), dtype=np.uint8)
+    assert np.array_equal(W.pack_int4_kshuffle(q), O.pack_int4_kshuffle(q))
+    assert np.array_equal(W.unpack_int4_kshuffle(W.pack_int4_kshuffle(q)), q)
+    x = rng.integers(-2**31, 2**31, size=(9, 24), dtype=np.int64).astype(np.int32)
+    assert np.array_equal(W.unpack_int4_kshuffle(x), O.unpack_int4_kshuffle(x))
+    assert W.pack_int4_kshuffle(np.arange(8, dtype=np.uint8)[None, :]).tolist() == [[0x75316420]]
+    with pytest.raises(W.W4A16Error) as e:
+        W.pack_int4_kshuffle(np.full((2, 8), 16, np.uint8))
+    assert e.value.status == W.ERR_VALUE
+    with pytest.raises(W.W4A16Error) as e:
+        W.pack_int4_kshuffle(np.zeros((2, 12), np.uint8))
+    assert e.value.status == W.ERR_SHAPE
+    assert W.lib().w4a16_pack_int4_kshuffle(None, 2, 8, None) == W.ERR_NULL
+
+
 # ------------------------------------------------------------ argument checks
 FAKE = ctypes.c_void_p(0x10000)    # aligned, never dereferenced on the host
+
+
+def _kp(M=1, K=5120, N=17408, G=128, dt=1, a=FAKE, w=FAKE, s=FAKE, z=None, zp=8, bias=None,
+        out=FAKE):
+    return W.lib().w4a16_gemm_kpacked(a, w, s, z, G, zp, bias, out, M, K, N, dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=2), W.ERR_DTYPE),
+    (dict(K=0), W.ERR_SHAPE),
+    (dict(M=-1), W.ERR_SHAPE),
+    (dict(N=0), W.ERR_SHAPE),
+    (dict(K=2120, G=2120), W.ERR_SHAPE),        # K % 32
+    (dict(G=16), W.ERR_GROUP),
+    (dict(G=96), W.ERR_GROUP),
+    (dict(K=2112, G=128), W.ERR_SHAPE),         # K % G
+    (dict(a=None), W.ERR_NULL),
+    (dict(w=None), W.ERR_NULL),
+    (dict(s=None), W.ERR_NULL),
+    (dict(out=None), W.ERR_NULL),
+    (dict(zp=16), W.ERR_ZP),
+    (dict(a=ctypes.c_void_p(0x10008)), W.ERR_ALIGN),
+    (dict(w=ctypes.c_void_p(0x10004)), W.ERR_ALIGN),
+    (dict(bias=ctypes.c_void_p(0x10002)), W.ERR_ALIGN),
+])
+def test_gemm_kpacked_rejections(kw, status):
+    assert _kp(**kw) == status
+    assert W.last_error() != ""
+
+
+def test_gemm_kpacked_accepts_odd_n_and_any_zero_alignment():
+    assert _kp(M=0, a=None, w=None, s=None, out=None) == W.OK
+    for kw in (dict(N=17), dict(z=ctypes.c_void_p(0x10003), zp=99), dict(K=2112, G=2112)):
+        st = _kp(**kw)
+        assert st == (W.ERR_DEVICE if not HAS_GPU else st), kw
 
 
 def _gemm(a=FAKE, b=FAKE, s=FAKE, z=None, G=128, zp=8, out=FAKE, M=4, K=256, N=512, dt=W.F16):

@@ -612,6 +612,99 @@ w4a16_status w4a16_unpack_int4(const int32_t* packed, int64_t rows, int64_t cols
   return W4A16_OK;
 }
 
+w4a16_status w4a16_gemm_kpacked(const void* a, const int32_t* w, const void* scales,
+                                const uint8_t* zeros, int32_t group_size, int32_t zp_bias,
+                                const void* bias, void* out, int64_t M, int64_t K, int64_t N,
+                                int32_t dtype, void* stream) {
+  if (dtype != W4A16_F16 && dtype != W4A16_BF16)
+    return fail(W4A16_ERR_DTYPE, "dtype %d: only fp16 (0) and bf16 (1) activations are supported",
+                (int)dtype);
+  if (M < 0 || K <= 0 || N <= 0)
+    return fail(W4A16_ERR_SHAPE, "need M >= 0, K > 0, N > 0 (got M=%lld K=%lld N=%lld)",
+                (long long)M, (long long)K, (long long)N);
+  if (K % 32 != 0)
+    return fail(W4A16_ERR_SHAPE, "K=%lld must be a multiple of 32 for the K-packed layout",
+                (long long)K);
+  if (!(group_size == 32 || group_size == 64 || group_size == 128 || group_size == K))
+    return fail(W4A16_ERR_GROUP, "group size %d not supported (32, 64, 128 or K=%lld)",
+                (int)group_size, (long long)K);
+  if (K % group_size != 0)
+    return fail(W4A16_ERR_SHAPE, "K=%lld is not a multiple of group size %d", (long long)K,
+                (int)group_size);
+  if (M * K >= (1ll << 31) || M * N >= (1ll << 31) || N * (K / 8) >= (1ll << 31) ||
+      M > 65535ll * w4a16::kKpRows)
+    return fail(W4A16_ERR_SHAPE, "problem too large for 32-bit row/column indexing");
+  if (M == 0) return W4A16_OK;
+  if (!a || !w || !scales || !out)
+    return fail(W4A16_ERR_NULL, "a, w, scales and out must be non-NULL");
+  if (!zeros && (zp_bias < 0 || zp_bias > 15))
+    return fail(W4A16_ERR_ZP, "zp_bias=%d must lie in 0..15", (int)zp_bias);
+  if (!aligned16(a) || !aligned16(w) || !aligned16(scales) || !aligned16(out) ||
+      (bias && !aligned16(bias)))
+    return fail(W4A16_ERR_ALIGN, "device pointers (zeros excepted) must be 16-byte aligned");
+  DeviceState* ds = nullptr;
+  w4a16_status st = device_state(&ds);
+  if (st != W4A16_OK) return st;
+  w4a16::KPackedParams p{};
+  p.dq = w4a16::dq_consts(dtype);
+  p.a = (const uint16_t*)a;
+  p.w = (const uint32_t*)w;
+  p.sc = (const uint16_t*)scales;
+  p.zp = zeros;
+  p.bias = (const uint16_t*)bias;
+  p.out = (uint16_t*)out;
+  p.M = (int32_t)M;
+  p.K = (int32_t)K;
+  p.N = (int32_t)N;
+  p.G = group_size;
+  p.zp_bias = zp_bias;
+  p.g_shift = group_size == K ? -1 : (group_size == 32 ? 0 : group_size == 64 ? 1 : 2);
+  const int64_t rounds = (K / 32 + 3) / 4;
+  p.rpw = (int32_t)ceil_div(rounds, w4a16::kKpThreads / 64);
+  // a 128-K round stays inside one group when G is a multiple of 128 or the
+  // whole of K: the scale can then multiply fp32 round sums
+  const bool fold = group_size % 128 == 0 || group_size == K;
+  hipError_t e = w4a16::launch_kpacked(p, dtype, zeros != nullptr, fold, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_pack_int4_kshuffle(const uint8_t* q, int64_t N, int64_t K, int32_t* packed) {
+  if (N < 0 || K < 0 || K % 8 != 0)
+    return fail(W4A16_ERR_SHAPE, "need N >= 0 and K a non-negative multiple of 8");
+  if (N * K == 0) return W4A16_OK;
+  if (!q || !packed) return fail(W4A16_ERR_NULL, "q and packed must be non-NULL");
+  // nibble p of a word holds K offset 2p (p < 4) or 2(p - 4) + 1 (p >= 4)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t c = 0; c < K / 8; ++c) {
+      const uint8_t* src = q + n * K + 8 * c;
+      uint32_t v = 0;
+      for (int p = 0; p < 8; ++p) {
+        const int off = p < 4 ? 2 * p : 2 * (p - 4) + 1;
+        if (src[off] > 15)
+          return fail(W4A16_ERR_VALUE, "value %u at (%lld, %lld) is outside 0..15",
+                      (unsigned)src[off], (long long)n, (long long)(8 * c + off));
+        v |= (uint32_t)src[off] << (4 * p);
+      }
+      packed[n * (K / 8) + c] = (int32_t)v;
+    }
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_unpack_int4_kshuffle(const int32_t* packed, int64_t N, int64_t K, uint8_t* q) {
+  if (N < 0 || K < 0 || K % 8 != 0)
+    return fail(W4A16_ERR_SHAPE, "need N >= 0 and K a non-negative multiple of 8");
+  if (N * K == 0) return W4A16_OK;
+  if (!q || !packed) return fail(W4A16_ERR_NULL, "q and packed must be non-NULL");
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t c = 0; c < K / 8; ++c) {
+      const uint32_t v = (uint32_t)packed[n * (K / 8) + c];
+      for (int p = 0; p < 8; ++p)
+        q[n * K + 8 * c + (p < 4 ? 2 * p : 2 * (p - 4) + 1)] = (uint8_t)((v >> (4 * p)) & 0xFu);
+    }
+  return W4A16_OK;
+}
+
 const char* w4a16_last_error(void) { return g_last_error.c_str(); }
 
 const char* w4a16_version(void) { return "w4a16-gfx950 0.1.0"; }

@@ -117,10 +117,30 @@ struct DequantParams {
   int32_t K, N, G, zp_bias;
 };
 
+// K-packed layout: weights [N, K/8] int32 in ExLlama nibble order, scales
+// and zero points [N, K/G]. One workgroup per 16 columns x 16 rows.
+struct KPackedParams {
+  DqConsts dq;
+  const uint16_t* a;
+  const uint32_t* w;
+  const uint16_t* sc;
+  const uint8_t* zp;     // nullable: zp_bias for every group
+  const uint16_t* bias;  // nullable [N]
+  uint16_t* out;
+  int32_t M, K, N, G, zp_bias;
+  int32_t g_shift;       // log2(G / 32) for G = 32, 64, 128; -1 when G == K
+  int32_t rpw;           // 128-K rounds per wavefront
+};
+constexpr int kKpThreads = 256;  // 4 wavefronts
+constexpr int kKpCols = 16;
+constexpr int kKpRows = 16;
+
 hipError_t launch_decode(const DecodeParams& p, int dtype, bool has_zp, int mode,
                          int grid, int lds_bytes, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int dtype, bool has_zp, int grid, hipStream_t stream);
 hipError_t launch_prefill_reduce(const PrefillReduceParams& p, int dtype, hipStream_t stream);
+hipError_t launch_kpacked(const KPackedParams& p, int dtype, bool has_zp, bool fold,
+                          hipStream_t stream);
 hipError_t launch_dequant(const DequantParams& p, int dtype, bool has_zp,
                           hipStream_t stream);
 

@@ -1102,6 +1102,161 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// K-packed decode (weights [N, K/8] int32, ExLlama nibble order: nibbles i and
+// i + 4 of a word hold K values 2i and 2i + 1, so (w >> 4i) & 0x000F000F is a
+// packed pair of consecutive K; scales and zero points [N, K/G]).
+//
+// A workgroup owns 16 columns x 16 activation rows and all of K, so partial
+// sums never leave it. A round is 128 K. Lane l = 16j + c loads 16 bytes of
+// column c: chunk 4r + j (32 K values) of round r. Its four words are the B
+// operands of the round's four MFMA 16x16x32 steps; step i takes word i of
+// every lane group j, and the A operand of lane l is activation row c at the
+// same 8 K values. The four wavefronts take contiguous runs of rounds and
+// add up in LDS.
+//   FOLD (G a multiple of 128, or G == K): a round lies inside one group, so
+//     the MFMAs run on unscaled operands and the scale multiplies the round's
+//     fp32 sum: fp16 operand q - z (exact); bf16 operand 128 + q, with the
+//     round's activation sums from MFMAs against ones, folded as
+//     s * (part - (128 + z) * sum).
+//   otherwise (G = 32, 64): a round spans groups; the operand is the rounded
+//     tile RNE((q - z) * s) of the lane's own chunk.
+// ---------------------------------------------------------------------------
+constexpr int kKpU = 2;  // rounds in flight per wavefront
+
+// pair i of a K-packed word as base + q: (nibble i, nibble i + 4)
+__device__ __forceinline__ u32x4 kp_magic_op(uint32_t w, const DqRegs& k) {
+  return u32x4{(w & k.m_lo) | k.mag, ((w >> 4) & k.m_lo) | k.mag, ((w >> 8) & k.m_lo) | k.mag,
+               ((w >> 12) & k.m_lo) | k.mag};
+}
+// fp16 pairs as the exact integers q - z: (1024 + q) - (1024 + z)
+__device__ __forceinline__ u32x4 kp_int_op(uint32_t w, const DqRegs& k, uint32_t z) {
+  const f16x2 bias = __builtin_bit_cast(f16x2, (0x6400u | z) * 0x10001u);
+  const u32x4 m = kp_magic_op(w, k);
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // through a scalar: hipcc folds a bit_cast of a vector element m[i] to
+    // element 0 for every i
+    const uint32_t mi = m[i];
+    r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, mi) - bias);
+  }
+  return r;
+}
+// rounded tile RNE((q - z) * s): fp16 exact integer times s in one packed
+// multiply; bf16 through the exact fp32 FMA of exact_pair
+template <typename T>
+__device__ __forceinline__ u32x4 kp_tile_op(uint32_t w, const DqRegs& k, uint32_t s_bits,
+                                            uint32_t z) {
+  if constexpr (T::kIsF16) {
+    const u32x4 q = kp_int_op(w, k, z);
+    const f16x2 sc = __builtin_bit_cast(f16x2, (s_bits & 0xFFFFu) * 0x10001u);
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t qi = q[i];  // through a scalar, as in kp_int_op
+      r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, qi) * sc);
+    }
+    return r;
+  } else {
+    return u32x4{exact_pair<0>(BF16{}, w, k, make_col<0>(BF16{}, s_bits, z)),
+                 exact_pair<1>(BF16{}, w, k, make_col<1>(BF16{}, s_bits, z)),
+                 exact_pair<2>(BF16{}, w, k, make_col<2>(BF16{}, s_bits, z)),
+                 exact_pair<3>(BF16{}, w, k, make_col<3>(BF16{}, s_bits, z))};
+  }
+}
+
+template <typename T, bool HAS_ZP, bool FOLD>
+__global__ __launch_bounds__(kKpThreads) void kpacked_kernel(KPackedParams p) {
+  __shared__ f32x4 red[kKpThreads / 64 - 1][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int j = lane >> 4;
+  const int c = lane & 15;
+  const int col = blockIdx.x * kKpCols + c;
+  const int m0 = blockIdx.y * kKpRows;
+  const bool row_ok = m0 + c < p.M;
+  const int KC = p.K >> 5;        // 32-K chunks per column
+  const int R = (KC + 3) >> 2;    // 128-K rounds
+  const int r_beg = min(R, wave * p.rpw);
+  const int r_end = min(R, r_beg + p.rpw);
+  // clamped column and row: every load below is in bounds without a branch
+  const uint32_t* wrow = p.w + (int64_t)min(col, p.N - 1) * (p.K >> 3);
+  const uint16_t* arow = p.a + (int64_t)min(m0 + c, p.M - 1) * p.K;
+  const int NG = p.K / p.G;
+  const uint16_t* srow = p.sc + (int64_t)min(col, p.N - 1) * NG;
+  const uint8_t* zrow = HAS_ZP ? p.zp + (int64_t)min(col, p.N - 1) * NG : nullptr;
+  const DqRegs mag = dq_regs(p.dq);
+  const u32x4 ones = {T::kOnePair, T::kOnePair, T::kOnePair, T::kOnePair};
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+
+  for (int r0 = r_beg; r0 < r_end; r0 += kKpU) {
+    u32x4 wv[kKpU], av[kKpU][4];
+    uint32_t sb[kKpU], zb[kKpU];
+#pragma unroll
+    for (int u = 0; u < kKpU; ++u) {
+      const int ch = (r0 + u) * 4 + j;
+      const bool live = row_ok && r0 + u < r_end && ch < KC;
+      const int cl = min(ch, KC - 1);
+      wv[u] = *(const u32x4*)(wrow + cl * 4);
+      const int g = p.g_shift < 0 ? 0 : (cl >> p.g_shift);
+      sb[u] = srow[g];
+      zb[u] = HAS_ZP ? (uint32_t)zrow[g] : (uint32_t)p.zp_bias;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 v = *(const u32x4*)(arow + cl * 32 + 8 * i);
+        av[u][i] = live ? v : zero4;  // dead K and padding rows add zero
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kKpU; ++u) {
+      if (r0 + u >= r_end) break;  // uniform over the wavefront
+      if constexpr (FOLD) {
+        f32x4 part = {0.f, 0.f, 0.f, 0.f};
+        f32x4 sa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (T::kIsF16) {
+            part = mfma<T>(av[u][i], kp_int_op(wv[u][i], mag, zb[u]), part);
+          } else {
+            part = mfma<T>(av[u][i], kp_magic_op(wv[u][i], mag), part);
+            sa = mfma<T>(av[u][i], ones, sa);
+          }
+        }
+        // lane l's outputs are column c, whose scale (and zero point) for
+        // this round's group the lane loaded itself
+        const float s = widen(T{}, sb[u]);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float d = part[v];
+          if constexpr (!T::kIsF16) d = __builtin_fmaf(-(T::kBase + (float)zb[u]), sa[v], d);
+          acc[v] = __builtin_fmaf(s, d, acc[v]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc = mfma<T>(av[u][i], kp_tile_op<T>(wv[u][i], mag, sb[u], zb[u]), acc);
+      }
+    }
+  }
+
+  // wavefronts 1..3 hand their sums to wavefront 0 through LDS
+  if (wave > 0) red[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < kKpThreads / 64 - 1; ++w) acc += red[w][lane];
+  if (col < p.N) {
+    const float bv = p.bias ? widen(T{}, p.bias[col]) : 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = m0 + 4 * j + v;  // MFMA result row 4j + v, column c
+      if (row < p.M) p.out[(int64_t)row * p.N + col] = narrow(T{}, acc[v] + bv);
+    }
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1206,6 +1361,22 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, bool has_zp, int gr
   if (dtype == W4A16_F16)
     return has_zp ? prefill_gs<F16, true>(p, grid, st) : prefill_gs<F16, false>(p, grid, st);
   return has_zp ? prefill_gs<BF16, true>(p, grid, st) : prefill_gs<BF16, false>(p, grid, st);
+}
+
+template <typename T, bool Z>
+static hipError_t kpacked_go(const KPackedParams& p, bool fold, hipStream_t st) {
+  const dim3 grid((unsigned)((p.N + kKpCols - 1) / kKpCols), (unsigned)((p.M + kKpRows - 1) / kKpRows));
+  if (fold)
+    hipLaunchKernelGGL((kpacked_kernel<T, Z, true>), grid, dim3(kKpThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((kpacked_kernel<T, Z, false>), grid, dim3(kKpThreads), 0, st, p);
+  return hipGetLastError();
+}
+hipError_t launch_kpacked(const KPackedParams& p, int dtype, bool has_zp, bool fold,
+                          hipStream_t st) {
+  if (dtype == W4A16_F16)
+    return has_zp ? kpacked_go<F16, true>(p, fold, st) : kpacked_go<F16, false>(p, fold, st);
+  return has_zp ? kpacked_go<BF16, true>(p, fold, st) : kpacked_go<BF16, false>(p, fold, st);
 }
 
 template <typename T, bool Z>

@@ -75,8 +75,12 @@ def lib() -> ctypes.CDLL:
     L.w4a16_dequant.argtypes = [vp, vp, vp, i32, i32, vp, i64, i64, i32, vp]
     L.w4a16_pack_int4.argtypes = [vp, i64, i64, vp]
     L.w4a16_unpack_int4.argtypes = [vp, i64, i64, vp]
+    L.w4a16_gemm_kpacked.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, i64, i64, i64, i32, vp]
+    L.w4a16_pack_int4_kshuffle.argtypes = [vp, i64, i64, vp]
+    L.w4a16_unpack_int4_kshuffle.argtypes = [vp, i64, i64, vp]
     for f in ("w4a16_gemm", "w4a16_gemm_bias", "w4a16_gemm_planned", "w4a16_plan", "w4a16_plan_route",
-              "w4a16_dequant", "w4a16_pack_int4", "w4a16_unpack_int4"):
+              "w4a16_dequant", "w4a16_pack_int4", "w4a16_unpack_int4", "w4a16_gemm_kpacked",
+              "w4a16_pack_int4_kshuffle", "w4a16_unpack_int4_kshuffle"):
         getattr(L, f).restype = ctypes.c_int
     L.w4a16_last_error.restype = ctypes.c_char_p
     L.w4a16_last_error.argtypes = []
@@ -194,6 +198,49 @@ def launch(args) -> None:
         raise W4A16Error(st, last_error())
 
 
+def gemm_kpacked(a: torch.Tensor, w: torch.Tensor, scales: torch.Tensor,
+                 zeros: torch.Tensor | None = None, group_size: int = 128, zp_bias: int = 8,
+                 bias: torch.Tensor | None = None,
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """``a @ dequant(w) (+ bias)`` for K-packed weights: ``w`` int32 ``[N, K/8]``
+    in ExLlama nibble order (``pack_int4_kshuffle``), ``scales`` ``[N, K/G]``
+    in ``a``'s dtype, ``zeros`` uint8 ``[N, K/G]`` or None (PR #40977 "RDNA
+    hybrid W4A16", Impl. item 4)."""
+    if a.dim() != 2 or w.dim() != 2 or scales.dim() != 2:
+        raise ValueError("a, w and scales must be 2-D")
+    if a.dtype not in _DTYPE_CODE or scales.dtype != a.dtype:
+        raise ValueError("a and scales must both be float16 or both bfloat16")
+    if w.dtype != torch.int32 or (zeros is not None and zeros.dtype != torch.uint8):
+        raise ValueError("w must be int32 and zeros uint8")
+    M, K = a.shape
+    N = w.shape[0]
+    if w.shape[1] * 8 != K:
+        raise ValueError(f"w must be [N, {K // 8}], got {list(w.shape)}")
+    if group_size <= 0 or K % group_size != 0:
+        raise ValueError(f"K={K} is not a multiple of group size {group_size}")
+    if tuple(scales.shape) != (N, K // group_size):
+        raise ValueError(f"scales must be [{N}, {K // group_size}], got {list(scales.shape)}")
+    if zeros is not None and tuple(zeros.shape) != (N, K // group_size):
+        raise ValueError(f"zeros must be [{N}, {K // group_size}], got {list(zeros.shape)}")
+    if bias is not None and (bias.dim() != 1 or bias.shape[0] != N or bias.dtype != a.dtype):
+        raise ValueError(f"bias must be [{N}] in a's dtype")
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    elif tuple(out.shape) != (M, N) or out.dtype != a.dtype:
+        raise ValueError("out must be [M, N] like a")
+    for t in (a, w, scales, zeros, bias, out):
+        if t is not None:
+            if not t.is_cuda or t.device != a.device:
+                raise ValueError("all tensors must be on the same GPU")
+            if not t.is_contiguous():
+                raise ValueError("all tensors must be contiguous")
+    with torch.cuda.device(a.device):
+        _check(lib().w4a16_gemm_kpacked(_ptr(a), _ptr(w), _ptr(scales), _ptr(zeros), group_size,
+                                        zp_bias, _ptr(bias), _ptr(out), M, K, N,
+                                        _DTYPE_CODE[a.dtype], _stream(a.device)))
+    return out
+
+
 def dequant(b_q: torch.Tensor, scales: torch.Tensor, qzeros: torch.Tensor | None = None,
             group_size: int = 128, zp_bias: int = 8,
             out: torch.Tensor | None = None) -> torch.Tensor:
@@ -251,6 +298,35 @@ def unpack_int4(packed) -> np.ndarray:
     out = np.empty((packed.shape[0], packed.shape[1] * 8), dtype=np.uint8)
     _check(lib().w4a16_unpack_int4(packed.ctypes.data_as(ctypes.c_void_p), packed.shape[0],
                                    packed.shape[1] * 8, out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def pack_int4_kshuffle(q_nk) -> np.ndarray:
+    """Host pack: uint8 ``[N, K]`` values 0..15 -> int32 ``[N, K/8]``, K-packed
+    in ExLlama nibble order."""
+    if isinstance(q_nk, torch.Tensor):
+        q_nk = q_nk.cpu().numpy()
+    q = np.asarray(q_nk)
+    if q.dtype != np.uint8 and q.size and (q.min() < 0 or q.max() > 255):
+        raise W4A16Error(ERR_VALUE, "uint4 values must lie in 0..15")
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    if q.ndim != 2:
+        raise ValueError("q must be 2-D")
+    out = np.empty((q.shape[0], q.shape[1] // 8), dtype=np.int32)
+    _check(lib().w4a16_pack_int4_kshuffle(q.ctypes.data_as(ctypes.c_void_p), q.shape[0],
+                                          q.shape[1], out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def unpack_int4_kshuffle(packed) -> np.ndarray:
+    """Host unpack: int32 ``[N, K/8]`` -> uint8 ``[N, K]``."""
+    if isinstance(packed, torch.Tensor):
+        packed = packed.cpu().numpy()
+    packed = np.ascontiguousarray(packed, dtype=np.int32)
+    out = np.empty((packed.shape[0], packed.shape[1] * 8), dtype=np.uint8)
+    _check(lib().w4a16_unpack_int4_kshuffle(packed.ctypes.data_as(ctypes.c_void_p),
+                                            packed.shape[0], packed.shape[1] * 8,
+                                            out.ctypes.data_as(ctypes.c_void_p)))
     return out
 
 
