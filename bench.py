@@ -23,6 +23,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -49,10 +51,11 @@ def parse():
     return ap.parse_args()
 
 
-def alg_bytes(w) -> int:
-    """Packed weights + scales + packed zero points + activations + output."""
+def alg_bytes(w, kpacked: bool = False) -> int:
+    """Packed weights + scales + zero points (packed 8 per int32, or one byte
+    each in the K-packed layout) + activations + output."""
     ng = w.K // w.group_size
-    zp = ng * (w.N // 8) * 4 if w.has_zp else 0
+    zp = (ng * w.N if kpacked else ng * (w.N // 8) * 4) if w.has_zp else 0
     return w.K * w.N // 2 + ng * w.N * 2 + zp + w.M * w.K * 2 + w.M * w.N * 2
 
 
@@ -67,17 +70,25 @@ class Launch:
     (``w4a16.gemm_args``), so the host enqueues faster than the GPU drains.
     """
 
-    def __init__(self, w, torch, W, synthetic, rotate: bool):
+    def __init__(self, w, torch, W, synthetic, rotate: bool, kpacked: bool = False):
         d = synthetic.draw_workload(w)
         dt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
         dev = torch.device("cuda", 0)
         self.w = w
         self.torch = torch
+        self.kpacked = kpacked
         self.a = torch.from_numpy(d["a_bits"].view("int16")).view(dt).to(dev)
-        bq = torch.from_numpy(W.pack_int4(d["q"])).to(dev)
-        s = torch.from_numpy(d["s_bits"].view("int16")).view(dt).to(dev)
-        qz = None if d["z"] is None else torch.from_numpy(W.pack_int4(d["z"])).to(dev)
-        weight_bytes = bq.numel() * 4 + s.numel() * 2 + (0 if qz is None else qz.numel() * 4)
+        if kpacked:
+            # the same weights K-packed: [N, K/8] in ExLlama order, scales and
+            # zero points [N, K/G] (zero points one byte each)
+            bq = torch.from_numpy(W.pack_int4_kshuffle(np.ascontiguousarray(d["q"].T))).to(dev)
+            s = torch.from_numpy(np.ascontiguousarray(d["s_bits"].T).view("int16")).view(dt).to(dev)
+            qz = None if d["z"] is None else torch.from_numpy(np.ascontiguousarray(d["z"].T)).to(dev)
+        else:
+            bq = torch.from_numpy(W.pack_int4(d["q"])).to(dev)
+            s = torch.from_numpy(d["s_bits"].view("int16")).view(dt).to(dev)
+            qz = None if d["z"] is None else torch.from_numpy(W.pack_int4(d["z"])).to(dev)
+        weight_bytes = bq.numel() * 4 + s.numel() * 2 + (0 if qz is None else qz.numel() * qz.element_size())
         copies = max(1, math.ceil(ROTATE_BYTES / weight_bytes)) if rotate else 1
         self.sets = [(bq, s, qz)] + [(bq.clone(), s.clone(), None if qz is None else qz.clone())
                                      for _ in range(copies - 1)]
@@ -88,11 +99,18 @@ class Launch:
 
     def bind(self):
         """Argument tuples for the current stream (call again inside a capture)."""
-        self.args = [self.W.gemm_args(self.a, bq, s, qz, self.w.group_size, 8, self.out)
-                     for bq, s, qz in self.sets]
+        if self.kpacked:
+            self.args = [self.W.gemm_kpacked_args(self.a, bq, s, qz, self.w.group_size, 8, self.out)
+                         for bq, s, qz in self.sets]
+        else:
+            self.args = [self.W.gemm_args(self.a, bq, s, qz, self.w.group_size, 8, self.out)
+                         for bq, s, qz in self.sets]
 
     def __call__(self):
-        self.W.launch(self.args[self.i % len(self.args)])
+        if self.kpacked:
+            self.W.launch_kpacked(self.args[self.i % len(self.args)])
+        else:
+            self.W.launch(self.args[self.i % len(self.args)])
         self.i += 1
 
 
@@ -203,16 +221,17 @@ def cpu_baseline(workloads, budget_s=12.0):
                       f"{len(os.sched_getaffinity(0))}"}
 
 
-def run_workload(names, steps, warmup, rotate, torch, W, synthetic, graph=True):
+def run_workload(names, steps, warmup, rotate, torch, W, synthetic, graph=True, kpacked=False):
     ws = [synthetic.WORKLOADS[n] for n in names]
-    launches = [Launch(w, torch, W, synthetic, rotate) for w in ws]
+    launches = [Launch(w, torch, W, synthetic, rotate, kpacked) for w in ws]
     total_ms, per = time_launches(launches, steps, warmup, torch)
     graph_ms = time_graph(launches, steps, torch) if graph else None
     res = []
     for w, d in zip(ws, per):
         d = sorted(d)
         res.append({"name": w.name, "median_us": 1e3 * d[len(d) // 2],
-                    "mean_us": 1e3 * sum(d) / len(d), "bytes": alg_bytes(w), "flops": flops(w),
+                    "mean_us": 1e3 * sum(d) / len(d), "bytes": alg_bytes(w, kpacked),
+                    "flops": flops(w),
                     "plan": W.plan(w.M, w.K, w.N, w.group_size, w.has_zp,
                                    torch.float16 if w.dtype == "fp16" else torch.bfloat16).as_dict()})
     return total_ms, graph_ms, res
@@ -252,14 +271,19 @@ def main():
     todo = ([["decode_m1", "decode_m5"], ["prefill"], ["k2112"], ["tiny"], ["sweep_pc16"]]
             + [[f"sweep_m{m}"] for m in (1, 2, 4, 5, 6, 16, 64, 256, 4096)]) if args.all \
         else [groups.get(args.workload, [args.workload])]
+    # --all also times the K-packed layout ([N, K/8], w4a16_gemm_kpacked) on
+    # the decode-sized workloads
+    todo = [(n, False) for n in todo] + ([(n, True) for n in (
+        ["decode_m1", "decode_m5"], ["k2112"], ["tiny"], ["sweep_pc16"], ["sweep_m1"], ["sweep_m5"],
+        ["sweep_m16"])] if args.all else [])
 
     cpu = None
-    for names in todo:
+    for names, kpacked in todo:
         wl = [synthetic.WORKLOADS[n] for n in names]
         is_prefill = any(w.M > 16 for w in wl)
         steps = args.steps if not is_prefill else max(5, min(args.steps, 50))
         eager_ms, graph_ms, res = run_workload(names, steps, args.warmup, rotate, torch, W,
-                                               synthetic)
+                                               synthetic, kpacked=kpacked)
         n_launch = len(res)
         step_bytes = sum(r["bytes"] for r in res)
         step_flops = sum(r["flops"] for r in res)
@@ -282,7 +306,8 @@ def main():
             ach = step_bytes / n_launch / (launch_us * 1e-6) / 1e9
             roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4)}
-        roof["traffic"] = load_traffic(args.traffic, "+".join(names), kernel_source_hash())
+        roof["traffic"] = None if kpacked else load_traffic(args.traffic, "+".join(names),
+                                                             kernel_source_hash())
         line = {
             "metric": metric, "value": round(value, 4), "unit": unit, "n_gpus": 1,
             "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
@@ -293,13 +318,18 @@ def main():
                                    "zero_points": w.has_zp} for w in wl],
                        "weights_rotated_over_mb": 0 if not rotate else ROTATE_BYTES >> 20,
                        "launch": "K steps captured in one HIP graph, replayed once",
+                       "layout": "[N, K/8] K-packed" if kpacked else "[K, N/8]",
                        "parallelism": "single GPU"},
             "roofline": roof,
             "eager": {"ms_per_step": round(eager_ms / steps, 5),
                       "how": "same steps launched one by one through the C ABI",
                       "launches": res},
         }
-        if names == ["decode_m1", "decode_m5"] and not args.no_prefill_extra:
+        if kpacked:
+            line["metric"] = line["metric"].replace("W4A16 GEMM", "W4A16 GEMM, K-packed weights,")
+            for r in res:
+                r["plan"] = {"kernel": "kpacked", "block": "16 columns x 16 rows, all of K"}
+        if names == ["decode_m1", "decode_m5"] and not kpacked and not args.no_prefill_extra:
             # 20 graph-replayed steps after 10 warm-up launches (the first
             # launches of a fresh process run measurably slower)
             _, pg, pres = run_workload(["prefill"], 20, 10, rotate, torch, W, synthetic)

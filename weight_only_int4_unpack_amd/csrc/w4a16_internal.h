@@ -131,7 +131,7 @@ struct KPackedParams {
   int32_t g_shift;       // log2(G / 32) for G = 32, 64, 128; -1 when G == K
   int32_t rpw;           // 128-K rounds per wavefront
 };
-constexpr int kKpThreads = 256;  // 4 wavefronts
+constexpr int kKpThreads = 512;  // 8 wavefronts
 constexpr int kKpCols = 16;
 constexpr int kKpRows = 16;
 

@@ -1112,7 +1112,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
 // column c: chunk 4r + j (32 K values) of round r. Its four words are the B
 // operands of the round's four MFMA 16x16x32 steps; step i takes word i of
 // every lane group j, and the A operand of lane l is activation row c at the
-// same 8 K values. The four wavefronts take contiguous runs of rounds and
+// same 8 K values. The eight wavefronts take contiguous runs of rounds and
 // add up in LDS.
 //   FOLD (G a multiple of 128, or G == K): a round lies inside one group, so
 //     the MFMAs run on unscaled operands and the scale multiplies the round's
@@ -1241,7 +1241,7 @@ __global__ __launch_bounds__(kKpThreads) void kpacked_kernel(KPackedParams p) {
     }
   }
 
-  // wavefronts 1..3 hand their sums to wavefront 0 through LDS
+  // wavefronts 1..7 hand their sums to wavefront 0 through LDS
   if (wave > 0) red[wave - 1][lane] = acc;
   __syncthreads();
   if (wave != 0) return;

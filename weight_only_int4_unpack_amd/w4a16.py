@@ -241,6 +241,19 @@ def gemm_kpacked(a: torch.Tensor, w: torch.Tensor, scales: torch.Tensor,
     return out
 
 
+def gemm_kpacked_args(a, w, scales, zeros, group_size, zp_bias, out, bias=None):
+    """The C-ABI argument tuple of one K-packed GEMM, for repeated launches
+    without re-checking shapes; pass it to ``launch_kpacked``."""
+    M, K = a.shape
+    return (_ptr(a), _ptr(w), _ptr(scales), _ptr(zeros), group_size, zp_bias, _ptr(bias),
+            _ptr(out), M, K, w.shape[0], _DTYPE_CODE[a.dtype], _stream(a.device))
+
+
+def launch_kpacked(args) -> None:
+    """Run a tuple made by ``gemm_kpacked_args`` (on the stream it names)."""
+    _check(lib().w4a16_gemm_kpacked(*args))
+
+
 def dequant(b_q: torch.Tensor, scales: torch.Tensor, qzeros: torch.Tensor | None = None,
             group_size: int = 128, zp_bias: int = 8,
             out: torch.Tensor | None = None) -> torch.Tensor:
