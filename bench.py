@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--warm", action="store_true", help="no weight rotation (cache-warm)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters")
+    ap.add_argument("--kpacked", action="store_true",
+                    help="time the workload with the weights K-packed ([N, K/8], w4a16_gemm_kpacked)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -273,7 +275,7 @@ def main():
         else [groups.get(args.workload, [args.workload])]
     # --all also times the K-packed layout ([N, K/8], w4a16_gemm_kpacked) on
     # the decode-sized workloads
-    todo = [(n, False) for n in todo] + ([(n, True) for n in (
+    todo = [(n, args.kpacked) for n in todo] + ([(n, True) for n in (
         ["decode_m1", "decode_m5"], ["k2112"], ["tiny"], ["sweep_pc16"], ["sweep_m1"], ["sweep_m5"],
         ["sweep_m16"])] if args.all else [])
 
