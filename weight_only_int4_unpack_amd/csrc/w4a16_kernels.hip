@@ -1114,6 +1114,10 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
 // every lane group j, and the A operand of lane l is activation row c at the
 // same 8 K values. The eight wavefronts take contiguous runs of rounds and
 // add up in LDS.
+//   LDSA: when the block's activation rows fit (at most 60 KB, rows padded by
+//     16 bytes so that the 16 rows of one read fall in different banks), they
+//     are copied to LDS once per workgroup and the A operands are read there;
+//     otherwise each lane loads them from global memory per round.
 //   FOLD (G a multiple of 128, or G == K): a round lies inside one group, so
 //     the MFMAs run on unscaled operands and the scale multiplies the round's
 //     fp32 sum: fp16 operand q - z (exact); bf16 operand 128 + q, with the
@@ -1166,9 +1170,10 @@ __device__ __forceinline__ u32x4 kp_tile_op(uint32_t w, const DqRegs& k, uint32_
   }
 }
 
-template <typename T, bool HAS_ZP, bool FOLD>
+template <typename T, bool HAS_ZP, bool FOLD, bool LDSA>
 __global__ __launch_bounds__(kKpThreads) void kpacked_kernel(KPackedParams p) {
   __shared__ f32x4 red[kKpThreads / 64 - 1][64];
+  extern __shared__ __attribute__((aligned(16))) uint16_t a_lds[];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int j = lane >> 4;
@@ -1190,6 +1195,18 @@ __global__ __launch_bounds__(kKpThreads) void kpacked_kernel(KPackedParams p) {
   const u32x4 ones = {T::kOnePair, T::kOnePair, T::kOnePair, T::kOnePair};
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int mb = min(kKpRows, p.M - m0);
+  const int astride = p.K + 8;  // elements: 16 bytes of padding per row
+  if constexpr (LDSA) {
+    // the block's activation rows, once per workgroup
+    const int per_row = p.K >> 3;  // 16-byte pieces
+    for (int idx = threadIdx.x; idx < mb * per_row; idx += kKpThreads) {
+      const int rr = idx / per_row, q = idx - rr * per_row;
+      *(u32x4*)(a_lds + rr * astride + 8 * q) = *(const u32x4*)(p.a + (int64_t)(m0 + rr) * p.K + 8 * q);
+    }
+    __syncthreads();
+  }
+  const uint16_t* alds = a_lds + min(c, mb - 1) * astride;
 
   for (int r0 = r_beg; r0 < r_end; r0 += kKpU) {
     u32x4 wv[kKpU], av[kKpU][4];
@@ -1205,7 +1222,8 @@ __global__ __launch_bounds__(kKpThreads) void kpacked_kernel(KPackedParams p) {
       zb[u] = HAS_ZP ? (uint32_t)zrow[g] : (uint32_t)p.zp_bias;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const u32x4 v = *(const u32x4*)(arow + cl * 32 + 8 * i);
+        const u32x4 v = LDSA ? *(const u32x4*)(alds + cl * 32 + 8 * i)
+                             : *(const u32x4*)(arow + cl * 32 + 8 * i);
         av[u][i] = live ? v : zero4;  // dead K and padding rows add zero
       }
     }
@@ -1366,10 +1384,19 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, bool has_zp, int gr
 template <typename T, bool Z>
 static hipError_t kpacked_go(const KPackedParams& p, bool fold, hipStream_t st) {
   const dim3 grid((unsigned)((p.N + kKpCols - 1) / kKpCols), (unsigned)((p.M + kKpRows - 1) / kKpRows));
-  if (fold)
-    hipLaunchKernelGGL((kpacked_kernel<T, Z, true>), grid, dim3(kKpThreads), 0, st, p);
-  else
-    hipLaunchKernelGGL((kpacked_kernel<T, Z, false>), grid, dim3(kKpThreads), 0, st, p);
+  const int mb = p.M < kKpRows ? p.M : kKpRows;
+  const size_t lds = (size_t)mb * (p.K + 8) * 2;  // activation rows, padded
+  if (lds <= 60 * 1024) {
+    if (fold)
+      hipLaunchKernelGGL((kpacked_kernel<T, Z, true, true>), grid, dim3(kKpThreads), lds, st, p);
+    else
+      hipLaunchKernelGGL((kpacked_kernel<T, Z, false, true>), grid, dim3(kKpThreads), lds, st, p);
+  } else {
+    if (fold)
+      hipLaunchKernelGGL((kpacked_kernel<T, Z, true, false>), grid, dim3(kKpThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL((kpacked_kernel<T, Z, false, false>), grid, dim3(kKpThreads), 0, st, p);
+  }
   return hipGetLastError();
 }
 hipError_t launch_kpacked(const KPackedParams& p, int dtype, bool has_zp, bool fold,
