@@ -6,7 +6,9 @@ The kernel takes one of two numerics paths: G a multiple of 128 (or G == K)
 folds the scale into fp32 round sums; G = 32, 64 multiplies rounded tiles.
 Cases cover both paths in both dtypes, ragged K rounds (K % 128 != 0), ragged
 N (N % 16 != 0), several 16-row blocks, per-channel groups and the full-size
-decode shape on sampled columns.
+decode shape on sampled columns. The activation rows of a 16-row block are
+staged in LDS when they fit in 60 KB (M = 6 at K = 5120 does not; 16 rows at
+K = 1856 do), so both operand paths are covered.
 """
 import numpy as np
 import pytest
@@ -31,6 +33,8 @@ CASES = [
     (33, 2112, 72, 2112, "bf16", False),    # per-channel, partial last round, three row blocks
     (2, 96, 24, 32, "fp16", True),          # one partial round (three chunks)
     (5, 512, 1000, 128, "bf16", False),     # fold, N % 16 = 8
+    (6, 5120, 1040, 128, "bf16", False),    # rows just over the LDS staging limit: global loads
+    (16, 1856, 48, 64, "fp16", True),       # 16 staged rows just under the limit
 ]
 IDS = [f"M{c[0]}_K{c[1]}_N{c[2]}_G{c[3]}_{c[4]}_{'zp' if c[5] else 'sym'}" for c in CASES]
 
