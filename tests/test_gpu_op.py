@@ -51,3 +51,21 @@ def test_compiled_call_routes_on_runtime_m():
         assert np.array_equal(got, dev_to_bits(p.gpu_gemm())), M
     routes = {W.plan(M, K, N, G, True, TORCH_DT["bf16"]).route for M in (1, 5, 64, 700)}
     assert routes == {W.ROUTE_DECODE, W.ROUTE_PREFILL}
+
+
+def test_kpacked_op_equals_binding_and_oracle():
+    M, K, N, G, dtype = 5, 1024, 520, 128, "bf16"
+    p = random_problem(M, K, N, G, dtype, True, seed=130)
+    d_q = O.unpack_int4(p.b_q).T                      # [N, K] uint4 of the same weights
+    w = torch.from_numpy(O.pack_int4_kshuffle(np.ascontiguousarray(d_q))).cuda()
+    s_nk = np.ascontiguousarray(p.s_bits.T)
+    z_nk = np.ascontiguousarray(O.unpack_int4(p.qz).T)
+    s_d = bits_to_dev(s_nk, dtype)
+    z_d = torch.from_numpy(z_nk).cuda()
+    got = dev_to_bits(op.gemm_kpacked(p.a, w, s_d, z_d, G))
+    assert np.array_equal(got, dev_to_bits(W.gemm_kpacked(p.a, w, s_d, z_d, G)))
+    want = O.gemm_kpacked(p.a_bits, O.pack_int4_kshuffle(np.ascontiguousarray(d_q)), s_nk, z_nk,
+                          G, 8, dtype)
+    assert_within_tolerance(got, want, dtype, "kpacked op")
+    torch.library.opcheck(torch.ops.w4a16.gemm_kpacked.default, (p.a, w, s_d, z_d, G, 8, None),
+                          test_utils=("test_schema", "test_faketensor"))

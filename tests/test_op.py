@@ -68,3 +68,41 @@ def test_fake_rejects_malformed_calls(bad):
             b = torch.empty((511,), device="cuda", dtype=torch.float16)
         with pytest.raises(ValueError):
             op.gemm(a, b_q, s, z, G, 8, b)
+
+
+# ------------------------------------------------------------ K-packed operator
+def _fake_kp(M=4, K=256, N=512, G=128, dtype=torch.float16, zp=False):
+    a = torch.empty((M, K), device="cuda", dtype=dtype)
+    w = torch.empty((N, K // 8), device="cuda", dtype=torch.int32)
+    s = torch.empty((N, K // G), device="cuda", dtype=dtype)
+    z = torch.empty((N, K // G), device="cuda", dtype=torch.uint8) if zp else None
+    return a, w, s, z
+
+
+def test_kpacked_fake_shape_and_one_call_node():
+    with FakeTensorMode():
+        a, w, s, z = _fake_kp(M=7, K=2112, N=5120, G=64, dtype=torch.bfloat16, zp=True)
+        out = op.gemm_kpacked(a, w, s, z, 64)
+        assert tuple(out.shape) == (7, 5120) and out.dtype == torch.bfloat16
+        a, w, s, z = _fake_kp()
+        gm = make_fx(lambda a, w, s: op.gemm_kpacked(a, w, s, None, 128))(a, w, s)
+    calls = [n for n in gm.graph.nodes if n.op == "call_function"]
+    assert [n.target for n in calls] == [torch.ops.w4a16.gemm_kpacked.default]
+    assert not torch.ops.w4a16.gemm_kpacked.default._schema.is_mutable
+
+
+@pytest.mark.parametrize("bad", ["w_cols", "scales", "zeros_dtype", "group"])
+def test_kpacked_fake_rejects_malformed_calls(bad):
+    with FakeTensorMode():
+        a, w, s, z = _fake_kp(zp=True)
+        G = 128
+        if bad == "w_cols":
+            w = torch.empty((512, 31), device="cuda", dtype=torch.int32)
+        elif bad == "scales":
+            s = torch.empty((2, 512), device="cuda", dtype=torch.float16)
+        elif bad == "zeros_dtype":
+            z = torch.empty((512, 2), device="cuda", dtype=torch.int32)
+        else:
+            G = 96
+        with pytest.raises(ValueError):
+            op.gemm_kpacked(a, w, s, z, G)

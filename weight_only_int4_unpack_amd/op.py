@@ -19,6 +19,11 @@ The page's fake checks nothing and its Risks section names that as a gap
 (the output shape is taken on trust). The fake here applies the same shape
 and dtype checks as the real call, so a malformed call fails while tracing.
 
+``torch.ops.w4a16.gemm_kpacked`` does the same for weights K-packed
+(``[N, K/8]`` in ExLlama order, scales and uint8 zero points ``[N, K/G]``;
+PR #40977 "RDNA hybrid W4A16", Impl. items 2 and 4: the hybrid path's skinny
+kernel is registered with a fake implementation for the same reason).
+
 The real implementation is the ctypes binding (argument marshalling only);
 every step of the computation runs in the library's gfx950 kernels.
 """
@@ -75,3 +80,49 @@ def gemm(a: torch.Tensor, b_q: torch.Tensor, scales: torch.Tensor,
     """Facade: ``a @ dequant(b_q, scales, qzeros) (+ bias)`` through the
     opaque operator ``torch.ops.w4a16.gemm``."""
     return torch.ops.w4a16.gemm(a, b_q, scales, qzeros, group_size, zp_bias, bias)
+
+
+def _check_meta_kpacked(a, w, scales, zeros, group_size, bias):
+    """Shape/dtype contract of the K-packed operator (real and fake)."""
+    if a.dim() != 2 or w.dim() != 2 or scales.dim() != 2:
+        raise ValueError("a, w and scales must be 2-D")
+    if a.dtype not in _FLOATS or scales.dtype != a.dtype:
+        raise ValueError("a and scales must both be float16 or both bfloat16")
+    if w.dtype != torch.int32 or (zeros is not None and zeros.dtype != torch.uint8):
+        raise ValueError("w must be int32 and zeros uint8")
+    K = a.size(1)
+    N = w.size(0)
+    if w.size(1) * 8 != K:
+        raise ValueError(f"w must be [N, {K // 8}]")
+    if group_size <= 0 or K % group_size != 0:
+        raise ValueError(f"K={K} is not a multiple of group size {group_size}")
+    if tuple(scales.shape) != (N, K // group_size):
+        raise ValueError(f"scales must be [{N}, {K // group_size}]")
+    if zeros is not None and tuple(zeros.shape) != (N, K // group_size):
+        raise ValueError(f"zeros must be [{N}, {K // group_size}]")
+    if bias is not None and (bias.dim() != 1 or bias.size(0) != N or bias.dtype != a.dtype):
+        raise ValueError(f"bias must be [{N}] in a's dtype")
+
+
+@torch.library.custom_op("w4a16::gemm_kpacked", mutates_args=())
+def _gemm_kpacked_op(a: torch.Tensor, w: torch.Tensor, scales: torch.Tensor,
+                     zeros: torch.Tensor | None, group_size: int, zp_bias: int = 8,
+                     bias: torch.Tensor | None = None) -> torch.Tensor:
+    _check_meta_kpacked(a, w, scales, zeros, group_size, bias)
+    return _W.gemm_kpacked(a.contiguous(), w.contiguous(), scales.contiguous(),
+                           None if zeros is None else zeros.contiguous(), group_size, zp_bias,
+                           bias=None if bias is None else bias.contiguous())
+
+
+@_gemm_kpacked_op.register_fake
+def _gemm_kpacked_fake(a, w, scales, zeros, group_size, zp_bias=8, bias=None):
+    _check_meta_kpacked(a, w, scales, zeros, group_size, bias)
+    return torch.empty((a.size(0), w.size(0)), dtype=a.dtype, device=a.device)
+
+
+def gemm_kpacked(a: torch.Tensor, w: torch.Tensor, scales: torch.Tensor,
+                 zeros: torch.Tensor | None, group_size: int, zp_bias: int = 8,
+                 bias: torch.Tensor | None = None) -> torch.Tensor:
+    """Facade: ``a @ dequant(w) (+ bias)`` for K-packed weights through the
+    opaque operator ``torch.ops.w4a16.gemm_kpacked``."""
+    return torch.ops.w4a16.gemm_kpacked(a, w, scales, zeros, group_size, zp_bias, bias)
