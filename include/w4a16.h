@@ -33,9 +33,21 @@
  *   - All argument checks run before anything is launched.
  *   - Device pointers must be 16-byte aligned; the caller owns every buffer.
  *   - GPU calls are enqueued on `stream` (a hipStream_t; NULL = the null
- *     stream) and never synchronise.
+ *     stream) and never synchronise the device or the stream.
  *   - G (group_size) is 32, 64, 128 or K (one group per column), and K is a
  *     multiple of G. N is a multiple of 8. M = 0 is a no-op that succeeds.
+ *     K is at most 2^24 (the kernels address a row block with 32-bit byte
+ *     offsets).
+ *
+ * Scratch ("workspace"). Some launches split K across workgroups and meet in
+ * fp32 partial sums in device memory (the page of PR #51453, Review section,
+ * asks for split-K because small problems leave most of the GPU idle). A
+ * workspace starts with W4A16_WORKSPACE_COUNTER_BYTES of arrival counters,
+ * followed by the partials. The counter region must hold zeros before the
+ * workspace is first used; every launch that completes leaves it zero, and
+ * nothing else is ever written there, so one zeroed workspace serves any
+ * sequence of calls on one stream. Two launches that run at the same time
+ * (different streams) must not share a workspace.
  */
 #ifndef W4A16_H
 #define W4A16_H
@@ -58,8 +70,13 @@ typedef enum {
   W4A16_ERR_DEVICE = 7,     /* no device, or the current device is not gfx950 */
   W4A16_ERR_HIP = 8,        /* a HIP runtime call or launch failed */
   W4A16_ERR_VALUE = 9,      /* pack: a value outside 0..15 */
-  W4A16_ERR_PLAN = 10       /* a caller-supplied plan does not fit the problem */
+  W4A16_ERR_PLAN = 10,      /* a caller-supplied plan does not fit the problem */
+  W4A16_ERR_WORKSPACE = 11  /* workspace too small, or scratch that would have to be
+                               allocated while the stream is being captured */
 } w4a16_status;
+
+/* Bytes of arrival counters at the start of every workspace (see above). */
+#define W4A16_WORKSPACE_COUNTER_BYTES 65536
 
 typedef enum { W4A16_F16 = 0, W4A16_BF16 = 1 } w4a16_dtype;
 
@@ -85,18 +102,24 @@ typedef struct {
   int32_t grid;             /* workgroups launched */
   int32_t threads;          /* threads per workgroup */
   int32_t lds_bytes;        /* LDS per workgroup */
-  int64_t workspace_bytes;  /* device scratch the launch needs (0 = none) */
+  int64_t workspace_bytes;  /* device scratch the launch needs: 0, or the
+                               counter region plus the fp32 partials */
 } w4a16_plan_t;
 
 /*
  * w4a16_gemm - out = a . dequant(b_q, scales, qzeros) on the GPU.
  * Route and tiles are chosen from the runtime M, K, N, G on every call
  * (PR #51453 Motivation: a tile choice frozen at trace time slowed decode).
- * Uses a per-device scratch buffer for split-K partials that the library
- * allocates on first need and keeps; that first call is therefore not
- * capturable into a HIP graph. Concurrent calls on one device that both
- * need the scratch buffer must be ordered (same stream).
- * Errors: NULL, SHAPE, GROUP, DTYPE, ZP, ALIGN, DEVICE, HIP.
+ * Scratch: the library keeps one workspace per (device, stream). When a
+ * launch needs more than that stream's workspace holds, it allocates a
+ * larger one (hipMalloc), zeroes its counter region on `stream`, and keeps
+ * the old one allocated until the process ends (a captured graph or a
+ * queued launch may still use it); it never synchronises. While `stream`
+ * is being captured into a graph no allocation is made: a launch that would
+ * need one fails with WORKSPACE (make one uncaptured call of the largest
+ * problem first, or use w4a16_gemm_ws). Calls on different streams never
+ * share scratch.
+ * Errors: NULL, SHAPE, GROUP, DTYPE, ZP, ALIGN, DEVICE, HIP, WORKSPACE.
  */
 w4a16_status w4a16_gemm(const void* a, const int32_t* b_q, const void* scales,
                         const int32_t* qzeros, int32_t group_size,
@@ -134,7 +157,43 @@ w4a16_status w4a16_gemm_planned(const void* a, const int32_t* b_q,
                                 const w4a16_plan_t* plan, void* stream);
 
 /*
- * w4a16_plan - the launch w4a16_gemm would make (host only, no GPU call).
+ * w4a16_workspace_bytes - the workspace w4a16_gemm_ws needs for one problem
+ * (host only, no GPU call): 0 when the launch splits no K across
+ * workgroups, else W4A16_WORKSPACE_COUNTER_BYTES plus the fp32 partials.
+ * num_cus: compute units of the device the call will run on (256 on
+ * MI355X; <= 0 means 256); w4a16_gemm_ws plans with the current device's
+ * count. Written to *bytes. The split-K request this serves is PR #51453's
+ * Review section; keeping scratch in caller memory keeps the call free of
+ * allocation, as its Code section's non-mutating, graph-capture-friendly
+ * operator needs.
+ * Errors: SHAPE, GROUP, DTYPE, NULL (bytes).
+ */
+w4a16_status w4a16_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t group_size,
+                                   int32_t dtype, int32_t num_cus, int64_t* bytes);
+
+/*
+ * w4a16_gemm_ws - as w4a16_gemm_bias (bias may be NULL), with the scratch
+ * in caller memory: `workspace` (device, 16-byte aligned, owned by the
+ * caller) of `ws_bytes` bytes, laid out and kept as described at the top.
+ * NULL with ws_bytes 0 is accepted when the problem needs no scratch. No
+ * allocation, no synchronisation: the call can be captured into a HIP graph
+ * on its first use (PR #51453 Code section: mutates_args=[], so that the
+ * operator is safe under CUDA-graph capture; Risks section: compile mode 3
+ * with FULL_AND_PIECEWISE graphs).
+ * Errors: those of w4a16_gemm_bias, and WORKSPACE (ws_bytes below
+ * w4a16_workspace_bytes for the current device), NULL (workspace needed).
+ */
+w4a16_status w4a16_gemm_ws(const void* a, const int32_t* b_q, const void* scales,
+                           const int32_t* qzeros, int32_t group_size, int32_t zp_bias,
+                           const void* bias, void* out, int64_t M, int64_t K, int64_t N,
+                           int32_t dtype, void* workspace, int64_t ws_bytes, void* stream);
+
+/*
+ * w4a16_plan - the launch w4a16_gemm would make (host only, no GPU call):
+ * route by the real M (PR #40977 "RDNA hybrid W4A16", Impl. item 5: the
+ * skinny kernel for small batches, the tiled kernel above) and tiles from
+ * the runtime shape (PR #51453 Motivation and Impl. item 1: BLOCK_M/N/K
+ * picked per call, never frozen at trace time).
  * num_cus: compute units of the target (256 on MI355X); <= 0 means 256.
  * Errors: SHAPE, GROUP, DTYPE, NULL (plan).
  */
@@ -147,9 +206,13 @@ w4a16_status w4a16_plan(int64_t M, int64_t K, int64_t N, int32_t group_size,
  * (W4A16_ROUTE_DECODE needs 1 <= M <= 16) and, for decode, the steps per
  * wavefront (1, 2, 4 or 8; 0 = selector's choice) and the decode mode
  * (0, 1, 2; -1 = selector's choice; mode 1 needs every wavefront's steps
- * inside one group) forced; for prefill, steps_per_wave forces the 64-row
- * K stages per workgroup (0 = selector's choice; a multiple of 2 when
- * G = 128 < K; at most 16 K splits result) and decode_mode is ignored.
+ * inside one group; mode 0, the rounded-weight operand, is fp16 only)
+ * forced; for prefill, steps_per_wave forces the 64-row K stages per
+ * workgroup (0 = selector's choice; a multiple of 2 when G = 128 < K; at
+ * most 32 K splits result) and decode_mode is ignored. Same passages as
+ * w4a16_plan; forcing a route exists to test every kernel against the
+ * reference on the same shapes (PR #40977 Code section: the reference test
+ * is run across the skinny-batch boundary).
  * Errors: those of w4a16_plan, and PLAN.
  */
 w4a16_status w4a16_plan_route(int64_t M, int64_t K, int64_t N,
@@ -160,8 +223,11 @@ w4a16_status w4a16_plan_route(int64_t M, int64_t K, int64_t N,
 
 /*
  * w4a16_dequant - w_out[k,n] = RNE_dtype((q - z) * s), the dequantised
- * weight as the prefill kernel stages it, written as a dense [K, N] array
- * (test probe; same device routine as the GEMM's weight tiles).
+ * weight in the activation dtype, written as a dense [K, N] array (test
+ * probe of the magic-number unpack of PR #40977 "RDNA hybrid W4A16",
+ * Impl. item 3, with the reference's (raw - zero) * scale of its Code
+ * section; the fp16 kernels that feed rounded weights to the MFMA use the
+ * same device routine).
  * Errors: NULL, SHAPE, GROUP, DTYPE, ZP, ALIGN, DEVICE, HIP.
  */
 w4a16_status w4a16_dequant(const int32_t* b_q, const void* scales,
@@ -172,14 +238,18 @@ w4a16_status w4a16_dequant(const int32_t* b_q, const void* scales,
 /*
  * w4a16_pack_int4 - host utility: q [rows, cols] uint8 values 0..15 ->
  * packed [rows, cols/8] int32 in the layout above (used for b_q and
- * qzeros). Host pointers. Errors: NULL, SHAPE (cols % 8), VALUE.
+ * qzeros; PR #51453 Impl. item 1: eight uint4 per int32 along N, so
+ * N = 8 * packed columns). Host pointers.
+ * Errors: NULL, SHAPE (cols % 8), VALUE.
  */
 w4a16_status w4a16_pack_int4(const uint8_t* q, int64_t rows, int64_t cols,
                              int32_t* packed);
 
 /*
- * w4a16_unpack_int4 - host inverse of w4a16_pack_int4 (diagnostics).
- * Host pointers; `cols` counts unpacked columns. Errors: NULL, SHAPE.
+ * w4a16_unpack_int4 - host inverse of w4a16_pack_int4 (diagnostics; the
+ * nibbles come out by logical shifts, as PR #40977's Impl. item 4 extracts
+ * them). Host pointers; `cols` counts unpacked columns.
+ * Errors: NULL, SHAPE.
  */
 w4a16_status w4a16_unpack_int4(const int32_t* packed, int64_t rows,
                                int64_t cols, uint8_t* q);
@@ -222,16 +292,27 @@ w4a16_status w4a16_pack_int4_kshuffle(const uint8_t* q, int64_t N, int64_t K,
                                       int32_t* packed);
 
 /*
- * w4a16_unpack_int4_kshuffle - host inverse of w4a16_pack_int4_kshuffle.
- * Host pointers. Errors: NULL, SHAPE.
+ * w4a16_unpack_int4_kshuffle - host inverse of w4a16_pack_int4_kshuffle
+ * (PR #40977 "RDNA hybrid W4A16", Impl. item 4: the shuffle is undone when
+ * the nibbles are unpacked). Host pointers. Errors: NULL, SHAPE.
  */
 w4a16_status w4a16_unpack_int4_kshuffle(const int32_t* packed, int64_t N,
                                         int64_t K, uint8_t* q);
 
-/* Message of the calling thread's last failed call ("" if none). */
+/*
+ * Message of the calling thread's last failed call ("" if none): why the
+ * problem was refused, as PR #43731's can_implement (Code section) returns
+ * a reason with every refusal and its Motivation treats "no kernel" as an
+ * error, never a silent substitute. Owned by the library, valid until the
+ * thread's next failing call.
+ */
 const char* w4a16_last_error(void);
 
-/* Library version string. */
+/*
+ * Library version string (static storage), so a caller can record which
+ * build of the kernels ran (PR #40977 Impl. item 6: benchmark runs name the
+ * kernel they time).
+ */
 const char* w4a16_version(void);
 
 #ifdef __cplusplus

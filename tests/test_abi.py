@@ -18,7 +18,8 @@ HAS_GPU = torch.cuda.is_available()
 def test_library_exports_every_header_symbol():
     L = W.lib()
     names = W.header_functions()
-    assert {"w4a16_gemm", "w4a16_gemm_bias", "w4a16_gemm_planned", "w4a16_plan", "w4a16_plan_route",
+    assert {"w4a16_gemm", "w4a16_gemm_bias", "w4a16_gemm_planned", "w4a16_gemm_ws",
+            "w4a16_workspace_bytes", "w4a16_plan", "w4a16_plan_route",
             "w4a16_dequant", "w4a16_pack_int4", "w4a16_unpack_int4", "w4a16_last_error",
             "w4a16_version", "w4a16_gemm_kpacked", "w4a16_pack_int4_kshuffle",
             "w4a16_unpack_int4_kshuffle"} <= set(names)
@@ -264,7 +265,8 @@ def test_selector_prefill_splits(M, K, N, G):
         assert ks % 2 == 0                               # whole groups of 128 rows
     if S > 1:
         assert tiles < 256 and ks >= 2
-        assert p.workspace_bytes == S * M * N * 4          # partials of the real rows only
+        # counter region, then the partials of the real rows only
+        assert p.workspace_bytes == W.WORKSPACE_COUNTER_BYTES + S * M * N * 4
     # a forced split reproduces exactly; invalid ones are rejected
     f = W.plan(M, K, N, G, True, torch.bfloat16, route=W.ROUTE_PREFILL, steps_per_wave=ks)
     assert (f.splits, f.steps_per_wave, f.grid) == (S, ks, p.grid)
@@ -307,3 +309,84 @@ def test_planned_call_rejects_mismatched_plan():
     st = W.lib().w4a16_gemm_planned(FAKE, FAKE, FAKE, FAKE, 32, 8, FAKE, 4, 4096, 4096, W.F16,
                                     ctypes.byref(p), None)
     assert st == W.ERR_PLAN
+
+
+# ------------------------------------------------------------ workspace
+def test_workspace_bytes_follow_the_plan():
+    # decode at the 5120 x 17408 shape: 10 splits of fp32 partials after the
+    # counter region; M = 5 has five rows of them
+    for M in (1, 5):
+        p = W.plan(M, 5120, 17408, 128, False, torch.bfloat16)
+        assert p.splits == 10
+        n = W.workspace_bytes(M, 5120, 17408, 128, torch.bfloat16)
+        assert n == p.workspace_bytes == W.WORKSPACE_COUNTER_BYTES + 10 * M * 17408 * 4
+    # unsplit launches need none: the 256 x 512 tiny problem and the prefill
+    assert W.workspace_bytes(4, 256, 512, 128, torch.float16) == 0
+    assert W.workspace_bytes(2048, 5120, 17408, 128, torch.bfloat16) == 0
+    assert W.workspace_bytes(0, 5120, 17408, 128, torch.bfloat16) == 0
+    # fewer CUs, fewer splits wanted: never more scratch than for 256
+    assert W.workspace_bytes(64, 4096, 4096, 32, torch.float16, num_cus=32) <= \
+        W.workspace_bytes(64, 4096, 4096, 32, torch.float16)
+
+
+def test_workspace_bytes_errors():
+    L = W.lib()
+    n = ctypes.c_int64(-1)
+    assert L.w4a16_workspace_bytes(1, 256, 512, 128, W.F16, 256, None) == W.ERR_NULL
+    assert L.w4a16_workspace_bytes(1, 256, 512, 128, 7, 256, ctypes.byref(n)) == W.ERR_DTYPE
+    assert L.w4a16_workspace_bytes(1, 256, 516, 128, W.F16, 256, ctypes.byref(n)) == W.ERR_SHAPE
+    assert L.w4a16_workspace_bytes(1, 256, 512, 96, W.F16, 256, ctypes.byref(n)) == W.ERR_GROUP
+    assert L.w4a16_workspace_bytes(1, 2112, 512, 128, W.F16, 256, ctypes.byref(n)) == W.ERR_SHAPE
+    assert n.value == -1     # untouched on error
+
+
+def _gemm_ws(ws=FAKE, nbytes=1 << 30, M=5, K=4096, N=4096, G=128, dt=W.F16, bias=None, a=FAKE):
+    return W.lib().w4a16_gemm_ws(a, FAKE, FAKE, None, G, 8, bias, FAKE, M, K, N, dt, ws, nbytes,
+                                 None)
+
+
+def test_gemm_ws_rejections():
+    need = W.workspace_bytes(5, 4096, 4096, 128, torch.float16)
+    assert need > 0
+    assert _gemm_ws(nbytes=need - 1) == W.ERR_WORKSPACE
+    assert "workspace" in W.last_error()
+    assert _gemm_ws(ws=None, nbytes=0) == W.ERR_NULL
+    assert _gemm_ws(nbytes=-1) == W.ERR_WORKSPACE
+    assert _gemm_ws(ws=ctypes.c_void_p(0x10008)) == W.ERR_ALIGN
+    assert _gemm_ws(bias=ctypes.c_void_p(0x10002)) == W.ERR_ALIGN
+    assert _gemm_ws(a=None) == W.ERR_NULL
+    assert _gemm_ws(G=96) == W.ERR_GROUP
+    assert _gemm_ws(M=0, ws=None, nbytes=0, a=None) == W.OK
+    if not HAS_GPU:   # valid arguments reach the device check
+        assert _gemm_ws(nbytes=need) == W.ERR_DEVICE
+        # a problem without split needs no workspace at all
+        assert _gemm_ws(ws=None, nbytes=0, M=4, K=256, N=512) == W.ERR_DEVICE
+
+
+def test_bf16_decode_mode_0_rejected():
+    # the rounded-weight operand of decode mode 0 is fp16 only: bf16 rounding
+    # (2^-8 per weight) over a long K leaves the tolerance
+    with pytest.raises(W.W4A16Error) as e:
+        W.plan(4, 4096, 4096, 32, True, torch.bfloat16, route=W.ROUTE_DECODE, decode_mode=0)
+    assert e.value.status == W.ERR_PLAN and "fp16" in W.last_error()
+    assert W.plan(4, 4096, 4096, 32, True, torch.float16, route=W.ROUTE_DECODE,
+                  decode_mode=0).decode_mode == 0
+    # the selector never picks it for bf16
+    for G in (32, 64, 128, 4096):
+        for M in range(1, 9):
+            assert W.plan(M, 4096, 4096, G, True, torch.bfloat16).decode_mode != 0
+
+
+def test_k_limit_and_counter_limit():
+    # K above 2^24 would overflow the 32-bit byte offsets of a row block
+    assert _gemm(M=1, K=1 << 25, N=8, G=1 << 25) == W.ERR_SHAPE
+    assert "2^24" in W.last_error()
+    assert _kp(M=1, K=1 << 25, N=8, G=1 << 25) == W.ERR_SHAPE
+    # more column blocks than the counter region serves: the selector takes
+    # the prefill route, and a forced split decode is refused
+    N = 4097 * 256
+    assert W.plan(1, 4096, N, 128, False, torch.bfloat16).route == W.ROUTE_PREFILL
+    with pytest.raises(W.W4A16Error) as e:
+        W.plan(1, 4096, N, 128, False, torch.bfloat16, route=W.ROUTE_DECODE)
+    assert e.value.status == W.ERR_PLAN
+    assert W.plan(1, 4096, 4096 * 256, 128, False, torch.bfloat16).route == W.ROUTE_DECODE

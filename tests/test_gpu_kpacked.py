@@ -2,8 +2,11 @@
 
 Weights are int32 ``[N, K/8]`` in ExLlama nibble order, scales and zero points
 ``[N, K/G]`` (PR #40977 "RDNA hybrid W4A16", Impl. item 4 and Code section).
-The kernel takes one of two numerics paths: G a multiple of 128 (or G == K)
-folds the scale into fp32 round sums; G = 32, 64 multiplies rounded tiles.
+The kernel takes one of three numerics paths: G a multiple of 128 (or G == K)
+folds the scale into fp32 round sums; fp16 with G = 32, 64 multiplies
+rounded tiles (2^-11 relative per weight); bf16 with G = 32, 64 keeps the
+exact operand and folds per 32-K chunk, since rounded bf16 tiles leave the
+tolerance over a long K (pinned on the CPU in test_oracle.py).
 Cases cover both paths in both dtypes, ragged K rounds (K % 128 != 0), ragged
 N (N % 16 != 0), several 16-row blocks, per-channel groups and the full-size
 decode shape on sampled columns. The activation rows of a 16-row block are
@@ -95,6 +98,21 @@ def test_kpacked_bias(M, K, N, G, dtype, zp):
     assert_within_tolerance(got, want, dtype, "kpacked bias")
     alone = _run(d, w, s_nk, z_nk, G, dtype, bias=bias, a_bits=np.zeros_like(d["a_bits"]))
     assert np.array_equal(alone, np.broadcast_to(bias, (M, N)))
+
+
+# Long K with small groups and zero points: where rounded bf16 tiles fail
+# (K = 5120, 8192, 16384 at G = 32 and 64), in both dtypes, on every column.
+LONG_K = [(M, K, N, G, dt) for (M, K, N) in ((8, 5120, 1024), (16, 8192, 512), (16, 16384, 256))
+          for G in (32, 64) for dt in ("bf16", "fp16")]
+
+
+@pytest.mark.parametrize("M,K,N,G,dtype", LONG_K,
+                         ids=[f"M{c[0]}_K{c[1]}_N{c[2]}_G{c[3]}_{c[4]}" for c in LONG_K])
+def test_kpacked_small_groups_long_k(M, K, N, G, dtype):
+    d, w, s_nk, z_nk = _problem(M, K, N, G, dtype, True, 30 + K // 1024 + G)
+    got = _run(d, w, s_nk, z_nk, G, dtype)
+    want = O.gemm_kpacked(d["a_bits"], w, s_nk, z_nk, G, 8, dtype)
+    assert_within_tolerance(got, want, dtype, f"kpacked K={K} G={G}")
 
 
 @pytest.mark.parametrize("M", [1, 5])

@@ -37,7 +37,10 @@ def _routes(M):
     if 1 <= M <= 16:
         def big(p):   # the fast layout takes 1, 2 or 4 steps per wavefront
             return 4 if (p.N % 16 == 0 and p.K % 8 == 0) else 1
-        out += [("decode_sit", lambda p: _plan(p, W.ROUTE_DECODE, L=big(p), mode=0)),
+
+        def sit(p):   # the rounded-weight operand (mode 0) is fp16 only
+            return _plan(p, W.ROUTE_DECODE, L=big(p), mode=0 if p.dtype == "fp16" else 2)
+        out += [("decode_sit", sit),
                 ("decode_multi", lambda p: _plan(p, W.ROUTE_DECODE, L=big(p), mode=2)),
                 ("decode_onegroup", lambda p: _plan(p, W.ROUTE_DECODE, L=1, mode=1)),
                 ("decode_L2", lambda p: _plan(p, W.ROUTE_DECODE, L=min(2, big(p))))]
@@ -70,8 +73,12 @@ def test_dequant_probe_zp_bias_values():
 
 
 # ---------------------------------------------------------------- parity grid
-GRID = [(M, dtype, G, zp) for M in (1, 5, 6, 64) for dtype in ("fp16", "bf16")
+# The M grid is the page's reference test grid (PR #40977, Code section:
+# 1, the skinny-batch limit 5, one past it, and 64), from the golden file.
+_PAGE_GRID = json.load(open(os.path.join(GOLDEN, "pages_parity_grid.json")))
+GRID = [(M, dtype, G, zp) for M in _PAGE_GRID["m_grid"] for dtype in ("fp16", "bf16")
         for G in (32, 64, 128, 512) for zp in (False, True)]
+assert _PAGE_GRID["group_size_reported_broken"] in (32, 64, 128, 512)
 
 
 @pytest.mark.parametrize("M,dtype,G,zp", GRID)
@@ -244,27 +251,65 @@ def test_q_equals_z_gives_zero(dtype, zp):
          "s_bits": O.rne_bits(rng.uniform(1e-3, 1e-2, (K // G, N)).astype(np.float32), dtype),
          "z": z}
     p = make_problem(d, M, K, N, G, dtype)
+    bound = _factored_zero_bound(p, zp)
     for label, mk in _routes(M):
         pl = mk(p)
         got = O.to_f32(dev_to_bits(p.gpu_gemm(plan=pl)), dtype)
         eff = pl if pl is not None else W.plan(M, K, N, G, zp, TORCH_DT[dtype])
-        if eff.route == W.ROUTE_PREFILL or eff.decode_mode != 0:
-            # s * (sum a (base + q) - (base + z) sum a): the two fp32 sums
-            # cancel up to their rounding, not to an exact zero (prefill and
-            # the grouped decode modes; decode mode 0 feeds the exact tile)
-            assert np.all(np.abs(got) <= 2.0 ** -12), label
+        if eff.route == W.ROUTE_DECODE and eff.decode_mode != 0 or \
+                eff.route == W.ROUTE_PREFILL and dtype == "bf16":
+            # factored form s (sum a (base + q) - (base + z) sum a): the two
+            # fp32 sums cancel up to their rounding, within the bound below
+            assert np.all(np.abs(got) <= bound), (label, float(np.abs(got).max()))
         else:
+            # exact operand q - z = 0 (fp16 prefill) or the exact tile (mode 0)
             assert np.all(got == 0.0), label
 
 
+def _factored_zero_bound(p, zp):
+    """Bound on |out| when q == z in the factored form. For output (m, n),
+    each group's fold computes s (P - b S) with P = sum a (b + q) and S = sum a
+    accumulated in fp32 over at most G terms (one group: the route's fold
+    never spans two), b + q <= B (bf16: 128 + 15; fp16: 1024 + 15, the even
+    nibble positions being the larger). Standard summation error bounds give
+    |P^ - P| <= g_G sum |a|(b + q) and |S^ - S| <= g_G sum |a|, g_G = G u / (1 - G u),
+    u = 2^-24, so |fold| <= 2 g_G B s sum |a| per group; the fold's own FMA,
+    the sums over groups, wavefronts and splits add roundings relative to
+    these already tiny terms (factor 1.01), and the cast to the output type
+    one ulp of the result (at least the smallest subnormal)."""
+    a = np.abs(O.to_f32(p.a_bits, p.dtype).astype(np.float64))             # [M, K]
+    s = np.abs(O.to_f32(p.s_bits, p.dtype).astype(np.float64))             # [K/G, N]
+    s_k = np.repeat(s, p.G, axis=0)                                        # [K, N]
+    u = 2.0 ** -24
+    g = p.G * u / (1 - p.G * u)
+    B = 143.0 if p.dtype == "bf16" else 1039.0
+    bound = 2 * g * B * (a @ s_k) * 1.01                                   # [M, N]
+    tiny = 2.0 ** -24 if p.dtype == "fp16" else 2.0 ** -133
+    return bound * (1 + 2.0 ** -7) + tiny
+
+
+# Linearity, bit for bit on every route: scaling S or a by 2 scales every
+# product and every partial sum by 2 with no change in rounding (no overflow
+# or underflow at these magnitudes), and negating a negates every sum (IEEE
+# rounding is symmetric); the reductions are deterministic, so the outputs
+# must be exactly 2C and -C.
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("M", [5, 100])
-def test_scale_linearity_bitwise(M):
-    p = random_problem(M, 1024, 512, 64, "bf16", True, seed=77)
-    base = {label: dev_to_bits(p.gpu_gemm(plan=mk(p))) for label, mk in _routes(M)}
-    p.s = p.s * 2
-    for label, mk in _routes(M):
-        got = O.to_f32(dev_to_bits(p.gpu_gemm(plan=mk(p))), "bf16")
-        assert np.array_equal(got, 2 * O.to_f32(base[label], "bf16")), label
+def test_linearity_bitwise(M, dtype):
+    p = random_problem(M, 1024, 512, 64, dtype, True, seed=77)
+    routes = _routes(M)
+    base = {label: O.to_f32(dev_to_bits(p.gpu_gemm(plan=mk(p))), dtype) for label, mk in routes}
+    a0, s0 = p.a, p.s
+    for what, factor in (("s*2", 2.0), ("a*2", 2.0), ("-a", -1.0)):
+        p.a, p.s = a0, s0
+        if what == "s*2":
+            p.s = s0 * 2
+        else:
+            p.a = a0 * factor
+        for label, mk in routes:
+            got = O.to_f32(dev_to_bits(p.gpu_gemm(plan=mk(p))), dtype)
+            assert np.array_equal(got, factor * base[label]), (what, label)
+    p.a, p.s = a0, s0
 
 
 # ---------------------------------------------------------------- robustness

@@ -449,3 +449,25 @@ def test_tolerance_helper():
     assert O.within_tolerance(g, w, O.F16).all()
     g = O.rne_bits(np.array([0.53, 10.0, -300.0], np.float32), O.F16)
     assert not O.within_tolerance(g, w, O.F16)[0]
+
+
+# ---------------------------------------------------------------- why bf16 operands stay exact
+@pytest.mark.parametrize("M,K,N,G", [(16, 16384, 2048, 32), (8, 8192, 4096, 64)])
+def test_rounded_bf16_tiles_leave_the_tolerance_at_long_k(M, K, N, G):
+    # A kernel that feeds the rounded tile RNE_bf16((q - z) s) to the matrix
+    # core (bf16 keeps 8 significant bits, so each weight is off by up to
+    # 2^-9 relative) drifts out of the 2e-2 tolerance over a long K with zero
+    # points, even with the product taken exactly (fp64) and rounded once:
+    # this is why every bf16 kernel path keeps an exact operand and applies
+    # the scale to fp32 sums. The same product of the exact fp32 weights stays
+    # inside. (Inputs: the synthetic recipe, family 777.)
+    d = synthetic.draw(M, K, N, G, "bf16", True, family=777)
+    b_q, qz = O.pack_int4(d["q"]), O.pack_int4(d["z"])
+    want = O.gemm(d["a_bits"], b_q, d["s_bits"], qz, G, 8, "bf16")
+    a64 = O.to_f32(d["a_bits"], "bf16").astype(np.float64)
+    tile = O.to_f32(O.dequant_tile(b_q, d["s_bits"], qz, G, 8, "bf16"), "bf16").astype(np.float64)
+    rounded = O.rne_bits((a64 @ tile).astype(np.float32), "bf16")
+    assert not O.within_tolerance(rounded, want, "bf16").all()
+    exact = O.dequant_fp32(b_q, d["s_bits"], qz, G, 8, "bf16").astype(np.float64)
+    assert O.within_tolerance(O.rne_bits((a64 @ exact).astype(np.float32), "bf16"), want,
+                              "bf16").all()

@@ -17,6 +17,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -56,10 +57,14 @@ w4a16_status check_shape(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dty
   if (K % G != 0)
     return fail(W4A16_ERR_SHAPE, "K=%lld is not a multiple of group size %d", (long long)K,
                 (int)G);
-  // 32-bit index limits of the kernels (rows, columns, and per-row offsets)
+  // 32-bit index limits of the kernels: rows, columns, per-row offsets, and
+  // the byte offsets of one prefill row block ((64 - 1) * K * 2 < 2^32 needs
+  // K < 2^25; K <= 2^24 leaves a margin)
   const int64_t lim = (int64_t)1 << 31;
-  if (K >= lim || N >= lim || M >= lim || (K / G) * N >= lim || M * K >= lim * 64 ||
-      K * (N / 8) >= lim * 64)
+  if (K > ((int64_t)1 << 24))
+    return fail(W4A16_ERR_SHAPE, "K=%lld exceeds 2^24 (32-bit byte offsets of a row block)",
+                (long long)K);
+  if (N >= lim || M >= lim || (K / G) * N >= lim || M * K >= lim * 64 || K * (N / 8) >= lim * 64)
     return fail(W4A16_ERR_SHAPE, "problem too large for 32-bit row/column indexing");
   return W4A16_OK;
 }
@@ -164,11 +169,20 @@ w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dty
   if (mode == 1 && !fits_one)
     return fail(W4A16_ERR_PLAN, "decode mode 1 needs the %lld steps of a wavefront inside one group",
                 (long long)L);
+  // Mode 0 feeds RNE_dtype((q - z) s) to the MFMA. In fp16 that is 2^-11
+  // relative per weight; in bf16 (2^-8) the sum over a long K leaves the
+  // 2e-2 tolerance (K = 5120, G = 32 with zero points already does), so
+  // bf16 always takes the exact operand of modes 1 and 2.
+  if (mode == 0 && dtype != W4A16_F16)
+    return fail(W4A16_ERR_PLAN, "decode mode 0 (rounded weights) is fp16 only");
   const int64_t S = ceil_div(KS, kDecodeWaves * L);
   // the kernel addresses the split-K partials with 32-bit byte offsets
   if (S > 1 && S * M * N * 4 >= (int64_t(1) << 32))
     return fail(W4A16_ERR_PLAN, "decode split-K partials (%lld splits x %lld x %lld fp32) exceed 4 GiB",
                 (long long)S, (long long)M, (long long)N);
+  if (S > 1 && NB > kMaxCounterBlocks)
+    return fail(W4A16_ERR_PLAN, "decode split-K needs %lld column blocks of counters (at most %lld)",
+                (long long)NB, (long long)kMaxCounterBlocks);
   pl->route = W4A16_ROUTE_DECODE;
   pl->block_m = kDecodeMaxM;
   pl->block_n = kDecodeCols;
@@ -179,7 +193,7 @@ w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dty
   pl->grid = (int32_t)(NB * S);
   pl->threads = kDecodeThreads;
   pl->lds_bytes = decode_lds_bytes((int)M, decode_ng_max(K, G, L));
-  pl->workspace_bytes = S > 1 ? (int64_t)(S * M * N * 4 + NB * kDecodeWaves * 4) : 0;
+  pl->workspace_bytes = S > 1 ? (int64_t)(kCounterBytes + S * M * N * 4) : 0;
   return W4A16_OK;
 }
 
@@ -229,7 +243,7 @@ w4a16_status plan_prefill(int64_t M, int64_t K, int64_t N, int32_t G, int num_cu
   pl->grid = (int32_t)(per_xcd * kXcds);
   pl->threads = kPrefillThreads;
   pl->lds_bytes = prefill_lds_bytes();
-  pl->workspace_bytes = S > 1 ? (int64_t)(S * M * N * 4) : 0;
+  pl->workspace_bytes = S > 1 ? (int64_t)(kCounterBytes + S * M * N * 4) : 0;
   return W4A16_OK;
 }
 
@@ -248,8 +262,11 @@ w4a16_status make_plan(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype
   // where the decode kernel's single in-place fold beat the prefill's K-split
   // route (K = N = 4096, M = 16: 12.0 vs 12.9 us; M = 12: 11.4 vs 12.5 us).
   // With groups of 32 the prefill route stays faster at M = 12 and 16.
+  // (N beyond what the counter region serves, 2^20 columns, has column
+  // blocks enough to fill the GPU on the prefill route's tiles)
   if (route == 0)
-    route = (M <= w4a16::kAutoDecodeMaxM || (M <= w4a16::kDecodeMaxM && (int64_t)G == K))
+    route = ((M <= w4a16::kAutoDecodeMaxM || (M <= w4a16::kDecodeMaxM && (int64_t)G == K)) &&
+             ceil_div(N, w4a16::kDecodeCols) <= w4a16::kMaxCounterBlocks)
                 ? W4A16_ROUTE_DECODE
                 : W4A16_ROUTE_PREFILL;
   if (route == W4A16_ROUTE_DECODE) {
@@ -280,18 +297,20 @@ w4a16_status check_plan(const w4a16_plan_t* pl, int64_t M, int64_t K, int64_t N,
 }
 
 // ---------------------------------------------------------------------------
-// per-device state: architecture check, CU count, split-K scratch
+// per-device state: architecture check, CU count, LDS limit, and the
+// library's own per-stream workspaces (for the calls without one)
 // ---------------------------------------------------------------------------
+struct StreamWs {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
 struct DeviceState {
   bool probed = false;
   bool ok = false;
   int num_cus = 0;
-  float* partials = nullptr;      // decode split-K fp32 partials, [S, M, N]
-  size_t partial_bytes = 0;
-  float* prefill_ws = nullptr;    // prefill K-split fp32 partials, [S, M, N]
-  size_t prefill_bytes = 0;
-  int32_t* counters = nullptr;    // arrival counters, one per (column block, wavefront)
-  size_t counter_n = 0;
+  size_t lds_per_block = 0;
+  std::map<hipStream_t, StreamWs> ws;  // one workspace per stream
+  std::vector<void*> retired;          // outgrown workspaces, kept until exit
 };
 std::mutex g_mu;
 std::vector<DeviceState> g_dev;
@@ -314,93 +333,63 @@ w4a16_status device_state(DeviceState** out) {
     ds.probed = true;
     ds.ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
     ds.num_cus = prop.multiProcessorCount;
+    ds.lds_per_block = prop.sharedMemPerBlock;
   }
   if (!ds.ok) return fail(W4A16_ERR_DEVICE, "device %d is not a gfx950 (MI355X) GPU", dev);
   *out = &ds;
   return W4A16_OK;
 }
 
-// Grows the device's split-K scratch. The partials need no initial value;
-// the arrival counters live in a buffer of their own that is zeroed when it
-// is allocated and that every launch leaves at zero (the last arrival on a
-// counter resets it), so shapes of different size never
-// see each other's data in a counter slot.
-w4a16_status ensure_workspace(DeviceState* ds, size_t partial_bytes, size_t counter_n) {
+// The library's workspace of `stream`, grown to at least `bytes`. Growing
+// allocates a new buffer and clears its counter region on `stream` (ordered
+// before the launch that needs it); the old buffer stays allocated, because
+// a graph captured earlier or a launch still queued may use it. Nothing
+// here synchronises. While the stream is being captured, growing would put
+// an allocation and a memset node into the graph: refused instead.
+w4a16_status stream_workspace(DeviceState* ds, hipStream_t stream, size_t bytes, void** ptr) {
   std::lock_guard<std::mutex> lk(g_mu);
-  if (ds->partial_bytes >= partial_bytes && ds->counter_n >= counter_n) return W4A16_OK;
-  // other streams may still use the old buffers
-  if (hipDeviceSynchronize() != hipSuccess) {
+  StreamWs& w = ds->ws[stream];
+  if (w.bytes >= bytes) {
+    *ptr = w.ptr;
+    return W4A16_OK;
+  }
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
     (void)hipGetLastError();
-    return fail(W4A16_ERR_HIP, "device synchronisation before growing the scratch failed");
+    cs = hipStreamCaptureStatusActive;  // e.g. the null stream while another captures
   }
-  if (ds->partial_bytes < partial_bytes) {
-    if (ds->partials && hipFree(ds->partials) != hipSuccess) {
-      (void)hipGetLastError();
-      return fail(W4A16_ERR_HIP, "freeing the old split-K partials failed");
-    }
-    ds->partials = nullptr;
-    ds->partial_bytes = 0;
-    const size_t sz = std::max<size_t>(partial_bytes, (size_t)8 << 20);
-    if (hipMalloc((void**)&ds->partials, sz) != hipSuccess) {
-      (void)hipGetLastError();
-      ds->partials = nullptr;
-      return fail(W4A16_ERR_HIP, "hipMalloc of %zu bytes of split-K partials failed", sz);
-    }
-    ds->partial_bytes = sz;
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(W4A16_ERR_WORKSPACE,
+                "the launch needs %zu bytes of scratch and the stream's workspace holds %zu; it "
+                "cannot grow while the stream is captured (run the problem once uncaptured, or "
+                "pass a workspace to w4a16_gemm_ws)",
+                bytes, w.bytes);
+  const size_t sz = std::max<size_t>({bytes, 2 * w.bytes, (size_t)8 << 20});
+  void* p = nullptr;
+  if (hipMalloc(&p, sz) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(W4A16_ERR_HIP, "hipMalloc of %zu bytes of split-K scratch failed", sz);
   }
-  if (ds->counter_n < counter_n) {
-    if (ds->counters && hipFree(ds->counters) != hipSuccess) {
-      (void)hipGetLastError();
-      return fail(W4A16_ERR_HIP, "freeing the old arrival counters failed");
-    }
-    ds->counters = nullptr;
-    ds->counter_n = 0;
-    const size_t n = std::max<size_t>(counter_n, 4096);
-    if (hipMalloc((void**)&ds->counters, n * sizeof(int32_t)) != hipSuccess) {
-      (void)hipGetLastError();
-      ds->counters = nullptr;
-      return fail(W4A16_ERR_HIP, "hipMalloc of the arrival counters failed");
-    }
-    if (hipMemset(ds->counters, 0, n * sizeof(int32_t)) != hipSuccess ||
-        hipDeviceSynchronize() != hipSuccess) {
-      (void)hipGetLastError();
-      return fail(W4A16_ERR_HIP, "clearing the arrival counters failed");
-    }
-    ds->counter_n = n;
+  if (hipMemsetAsync(p, 0, (size_t)w4a16::kCounterBytes, stream) != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(p);
+    return fail(W4A16_ERR_HIP, "clearing the arrival counters failed");
   }
+  if (w.ptr) ds->retired.push_back(w.ptr);
+  w.ptr = p;
+  w.bytes = sz;
+  *ptr = p;
   return W4A16_OK;
 }
 
-// Scratch for the prefill K-split partials, kept apart from the decode
-// split-K scratch so that growing one never waits on the other's users.
-w4a16_status ensure_prefill_ws(DeviceState* ds, size_t bytes) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  if (ds->prefill_bytes >= bytes) return W4A16_OK;
-  if (hipDeviceSynchronize() != hipSuccess) {  // other streams may still use the old buffer
-    (void)hipGetLastError();
-    return fail(W4A16_ERR_HIP, "device synchronisation before growing the scratch failed");
-  }
-  if (ds->prefill_ws && hipFree(ds->prefill_ws) != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(W4A16_ERR_HIP, "freeing the old prefill partials failed");
-  }
-  ds->prefill_ws = nullptr;
-  ds->prefill_bytes = 0;
-  const size_t sz = std::max<size_t>(bytes, (size_t)8 << 20);
-  if (hipMalloc((void**)&ds->prefill_ws, sz) != hipSuccess) {
-    (void)hipGetLastError();
-    ds->prefill_ws = nullptr;
-    return fail(W4A16_ERR_HIP, "hipMalloc of %zu bytes of prefill partials failed", sz);
-  }
-  ds->prefill_bytes = sz;
-  return W4A16_OK;
-}
-
-w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, DeviceState* ds,
-                 hipStream_t stream) {
+// One launch of `pl` with its scratch at `ws` (at least pl.workspace_bytes,
+// counter region zero; unused when the plan needs none).
+w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, void* ws, hipStream_t stream) {
   using namespace w4a16;
   hipError_t e = hipSuccess;
   if (pl.route == W4A16_ROUTE_NONE) return W4A16_OK;
+  int32_t* counters = (int32_t*)ws;
+  float* partials = ws ? (float*)((char*)ws + kCounterBytes) : nullptr;
   if (pl.route == W4A16_ROUTE_DECODE) {
     DecodeParams p{};
     p.dq = dq_consts(g.dtype);
@@ -423,11 +412,8 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, DeviceState* 
     p.S = pl.splits;
     p.NB = (int32_t)ceil_div(g.N, kDecodeCols);
     if (pl.splits > 1) {
-      const size_t part = (size_t)pl.splits * g.M * g.N * sizeof(float);
-      w4a16_status st = ensure_workspace(ds, part, (size_t)p.NB * kDecodeWaves);
-      if (st != W4A16_OK) return st;
-      p.ws = ds->partials;
-      p.counters = ds->counters;
+      p.ws = partials;
+      p.counters = counters;
     }
     e = launch_decode(p, g.dtype, g.qzeros != nullptr, pl.decode_mode, pl.grid, pl.lds_bytes,
                       stream);
@@ -453,16 +439,11 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, DeviceState* 
     p.band = (int32_t)std::min<int64_t>(kPrefillBand, p.tiles_m);
     p.S = pl.splits;
     p.kt_split = pl.steps_per_wave;
-    if (pl.splits > 1) {
-      const size_t part = (size_t)pl.splits * g.M * g.N * sizeof(float);
-      w4a16_status st = ensure_prefill_ws(ds, part);
-      if (st != W4A16_OK) return st;
-      p.ws = ds->prefill_ws;
-    }
+    if (pl.splits > 1) p.ws = partials;
     e = launch_prefill(p, g.dtype, g.qzeros != nullptr, pl.grid, stream);
     if (e == hipSuccess && pl.splits > 1) {
       PrefillReduceParams r{};
-      r.ws = ds->prefill_ws;
+      r.ws = partials;
       r.bias = (const uint16_t*)g.bias;
       r.out = (uint16_t*)g.out;
       r.M = (int32_t)g.M;
@@ -475,18 +456,50 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, DeviceState* 
   return W4A16_OK;
 }
 
+// Where a call's scratch comes from.
+enum class WsMode { Library, Caller };
+
 w4a16_status gemm_common(const void* a, const int32_t* b_q, const void* scales,
                          const int32_t* qzeros, int32_t G, int32_t zp_bias, const void* bias,
                          void* out, int64_t M, int64_t K, int64_t N, int32_t dtype,
-                         const w4a16_plan_t* forced, void* stream) {
+                         const w4a16_plan_t* forced, void* stream, WsMode wsm = WsMode::Library,
+                         void* ws = nullptr, int64_t ws_bytes = 0) {
   w4a16_status st = check_shape(M, K, N, G, dtype);
   if (st != W4A16_OK) return st;
   if (M == 0) return W4A16_OK;
   st = check_ptrs(a, b_q, scales, qzeros, out, zp_bias);
   if (st != W4A16_OK) return st;
   if (bias && !aligned16(bias)) return fail(W4A16_ERR_ALIGN, "bias must be 16-byte aligned");
+  if (wsm == WsMode::Caller) {
+    if (ws_bytes < 0) return fail(W4A16_ERR_WORKSPACE, "ws_bytes must be >= 0");
+    if (ws && !aligned16(ws)) return fail(W4A16_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
   if (forced) {
     st = check_plan(forced, M, K, N, G, dtype);
+    if (st != W4A16_OK) return st;
+  }
+  // a caller's workspace is checked against the plan for 256 CUs before
+  // any device call (so the check runs without a GPU), and again below
+  // against the plan for the current device's CU count
+  auto check_ws = [&](const w4a16_plan_t& q) -> w4a16_status {
+    if (wsm != WsMode::Caller || q.workspace_bytes == 0) return W4A16_OK;
+    if (!ws)
+      return fail(W4A16_ERR_NULL, "the launch needs %lld bytes of workspace and none was given",
+                  (long long)q.workspace_bytes);
+    if (ws_bytes < q.workspace_bytes)
+      return fail(W4A16_ERR_WORKSPACE, "the launch needs %lld bytes of workspace, %lld given",
+                  (long long)q.workspace_bytes, (long long)ws_bytes);
+    return W4A16_OK;
+  };
+  if (wsm == WsMode::Caller) {
+    w4a16_plan_t pre;
+    if (forced) {
+      pre = *forced;
+    } else {
+      st = make_plan(M, K, N, G, dtype, 256, 0, 0, -1, &pre);
+      if (st != W4A16_OK) return st;
+    }
+    st = check_ws(pre);
     if (st != W4A16_OK) return st;
   }
   DeviceState* ds = nullptr;
@@ -506,8 +519,19 @@ w4a16_status gemm_common(const void* a, const int32_t* b_q, const void* scales,
                    (long long)M, (long long)K, (long long)N, (int)G, pl.route, pl.block_m, pl.splits,
                    pl.steps_per_wave, pl.decode_mode, pl.grid);
   }
+  void* scratch = nullptr;
+  if (pl.workspace_bytes > 0) {
+    if (wsm == WsMode::Caller) {
+      st = check_ws(pl);
+      if (st != W4A16_OK) return st;
+      scratch = ws;
+    } else {
+      st = stream_workspace(ds, (hipStream_t)stream, (size_t)pl.workspace_bytes, &scratch);
+      if (st != W4A16_OK) return st;
+    }
+  }
   w4a16::GemmArgs g{a, b_q, scales, qzeros, bias, out, M, K, N, G, zp_bias, dtype};
-  return run(g, pl, ds, (hipStream_t)stream);
+  return run(g, pl, scratch, (hipStream_t)stream);
 }
 
 }  // namespace
@@ -536,6 +560,24 @@ w4a16_status w4a16_gemm_planned(const void* a, const int32_t* b_q, const void* s
   if (!plan) return fail(W4A16_ERR_NULL, "plan must be non-NULL");
   return gemm_common(a, b_q, scales, qzeros, group_size, zp_bias, nullptr, out, M, K, N, dtype,
                      plan, stream);
+}
+
+w4a16_status w4a16_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t group_size,
+                                   int32_t dtype, int32_t num_cus, int64_t* bytes) {
+  if (!bytes) return fail(W4A16_ERR_NULL, "bytes must be non-NULL");
+  w4a16_plan_t pl;
+  w4a16_status st = make_plan(M, K, N, group_size, dtype, num_cus, 0, 0, -1, &pl);
+  if (st != W4A16_OK) return st;
+  *bytes = pl.workspace_bytes;
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_gemm_ws(const void* a, const int32_t* b_q, const void* scales,
+                           const int32_t* qzeros, int32_t group_size, int32_t zp_bias,
+                           const void* bias, void* out, int64_t M, int64_t K, int64_t N,
+                           int32_t dtype, void* workspace, int64_t ws_bytes, void* stream) {
+  return gemm_common(a, b_q, scales, qzeros, group_size, zp_bias, bias, out, M, K, N, dtype,
+                     nullptr, stream, WsMode::Caller, workspace, ws_bytes);
 }
 
 w4a16_status w4a16_plan(int64_t M, int64_t K, int64_t N, int32_t group_size, int32_t has_zp,
@@ -631,8 +673,8 @@ w4a16_status w4a16_gemm_kpacked(const void* a, const int32_t* w, const void* sca
   if (K % group_size != 0)
     return fail(W4A16_ERR_SHAPE, "K=%lld is not a multiple of group size %d", (long long)K,
                 (int)group_size);
-  if (M * K >= (1ll << 31) || M * N >= (1ll << 31) || N * (K / 8) >= (1ll << 31) ||
-      M > 65535ll * w4a16::kKpRows)
+  if (K > (1ll << 24) || M * K >= (1ll << 31) || M * N >= (1ll << 31) ||
+      N * (K / 8) >= (1ll << 31) || M > 65535ll * w4a16::kKpRows)
     return fail(W4A16_ERR_SHAPE, "problem too large for 32-bit row/column indexing");
   if (M == 0) return W4A16_OK;
   if (!a || !w || !scales || !out)
@@ -645,6 +687,11 @@ w4a16_status w4a16_gemm_kpacked(const void* a, const int32_t* w, const void* sca
   DeviceState* ds = nullptr;
   w4a16_status st = device_state(&ds);
   if (st != W4A16_OK) return st;
+  // activation rows go to LDS when they fit the staging limit and, with the
+  // kernel's static reduction array, the device's LDS per workgroup
+  const size_t stage_lds = w4a16::kpacked_lds_bytes(M, K);
+  const bool stage = stage_lds <= (size_t)w4a16::kKpLdsStageMax &&
+                     stage_lds + w4a16::kKpRedBytes <= ds->lds_per_block;
   w4a16::KPackedParams p{};
   p.dq = w4a16::dq_consts(dtype);
   p.a = (const uint16_t*)a;
@@ -664,7 +711,8 @@ w4a16_status w4a16_gemm_kpacked(const void* a, const int32_t* w, const void* sca
   // a 128-K round stays inside one group when G is a multiple of 128 or the
   // whole of K: the scale can then multiply fp32 round sums
   const bool fold = group_size % 128 == 0 || group_size == K;
-  hipError_t e = w4a16::launch_kpacked(p, dtype, zeros != nullptr, fold, (hipStream_t)stream);
+  hipError_t e =
+      w4a16::launch_kpacked(p, dtype, zeros != nullptr, fold, stage, (hipStream_t)stream);
   if (e != hipSuccess) return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return W4A16_OK;
 }

@@ -32,6 +32,18 @@ constexpr int kPrefillMaxSplits = 32;   // most K splits of one prefill tile
 constexpr int kXcds = 8;                // MI355X: workgroups round-robin over 8 XCDs
 constexpr int64_t kLdsPerCu = 160 * 1024;  // gfx950 LDS per CU
 
+// ---- scratch memory of the split-K routes. Every workspace (the caller's,
+// the library's per-stream one, the fixed device array) starts with a region
+// of arrival counters that must be zero before first use and that every
+// completed launch leaves zero; the fp32 partials follow it, so that no
+// launch ever writes partials where another expects zeroed counters.
+constexpr int64_t kCounterBytes = W4A16_WORKSPACE_COUNTER_BYTES;
+// decode column blocks the region serves: one int32 counter per wavefront each
+constexpr int64_t kMaxCounterBlocks = kCounterBytes / (kDecodeWaves * (int64_t)sizeof(int32_t));
+// the fixed device array of the entry point that allocates nothing
+constexpr int64_t kStaticPartialBytes = 32ll << 20;
+constexpr int64_t kStaticScratchBytes = kCounterBytes + kStaticPartialBytes;
+
 // partial sums of the 4 wavefronts, then the staged scales (halves) and
 // packed zero points (words) of at most ng_max groups
 inline int decode_lds_bytes(int M, int ng_max) {
@@ -134,13 +146,30 @@ struct KPackedParams {
 constexpr int kKpThreads = 512;  // 8 wavefronts
 constexpr int kKpCols = 16;
 constexpr int kKpRows = 16;
+// LDS of the K-packed kernel: a static array through which wavefronts 1..7
+// hand their 16x16 sums to wavefront 0, plus (when it fits) the block's
+// activation rows, each padded by 16 bytes, as dynamic LDS. The rows are
+// staged only up to kKpLdsStageMax bytes (more costs occupancy and measured
+// no faster) and never beyond what the device gives one workgroup.
+constexpr int kKpRedBytes = (kKpThreads / 64 - 1) * 64 * 16;
+constexpr int kKpLdsStageMax = 60 * 1024;
+inline size_t kpacked_lds_bytes(int64_t M, int64_t K) {
+  const int64_t mb = M < kKpRows ? M : kKpRows;
+  return (size_t)(mb * (K + 8) * 2);
+}
 
 hipError_t launch_decode(const DecodeParams& p, int dtype, bool has_zp, int mode,
                          int grid, int lds_bytes, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int dtype, bool has_zp, int grid, hipStream_t stream);
 hipError_t launch_prefill_reduce(const PrefillReduceParams& p, int dtype, hipStream_t stream);
-hipError_t launch_kpacked(const KPackedParams& p, int dtype, bool has_zp, bool fold,
+// stage: the activation rows go to LDS (the host checked that
+// kpacked_lds_bytes + kKpRedBytes fits the device's per-workgroup LDS)
+hipError_t launch_kpacked(const KPackedParams& p, int dtype, bool has_zp, bool fold, bool stage,
                           hipStream_t stream);
+// Entry point without allocation: the device address of this device's copy
+// of the fixed scratch array (kStaticScratchBytes, counter region zeroed on
+// first use on the device, on `stream`).
+hipError_t static_scratch(hipStream_t stream, void** ptr);
 hipError_t launch_dequant(const DequantParams& p, int dtype, bool has_zp,
                           hipStream_t stream);
 

@@ -599,14 +599,17 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
       if (wv + 4 * r < M)
         store_wt4(wsr, (uint32_t)(s * M + wv + 4 * r) * row_bytes + lane_off, part[r]);
   }
-  // vmcnt counts the whole wavefront's stores: once it reads zero, every
-  // lane's partials have completed, so the counter cannot run ahead of them
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // Release: the partials (stored with the device-scope cache policy) are
+  // complete and visible to every XCD before the counter moves; acquire
+  // (below, last arrival only): no partial load is issued before the counter
+  // said all S splits have published theirs.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   int32_t* counter = p.counters + b * kDecodeWaves + wv;
   int prev = 0;
   if (lane == 0)
     prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (__builtin_amdgcn_readfirstlane(prev) != p.S - 1) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   // last arrival: add the S partials of each row in split order, up to QB
   // splits' loads of all the wavefront's rows in flight at once
   if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1114,7 +1117,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
 // every lane group j, and the A operand of lane l is activation row c at the
 // same 8 K values. The eight wavefronts take contiguous runs of rounds and
 // add up in LDS.
-//   LDSA: when the block's activation rows fit (at most 60 KB, rows padded by
+//   LDSA: when the block's activation rows fit (kKpLdsStageMax, rows padded by
 //     16 bytes so that the 16 rows of one read fall in different banks), they
 //     are copied to LDS once per workgroup and the A operands are read there;
 //     otherwise each lane loads them from global memory per round.
@@ -1123,8 +1126,16 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
 //     fp32 sum: fp16 operand q - z (exact); bf16 operand 128 + q, with the
 //     round's activation sums from MFMAs against ones, folded as
 //     s * (part - (128 + z) * sum).
-//   otherwise (G = 32, 64): a round spans groups; the operand is the rounded
-//     tile RNE((q - z) * s) of the lane's own chunk.
+//   TILE (fp16, G = 32, 64): a round spans groups; the operand is the
+//     rounded tile RNE_fp16((q - z) * s) of the lane's own chunk (relative
+//     error 2^-11 per weight).
+//   CHUNK (bf16, G = 32, 64): rounding a weight to bf16 costs 2^-8 relative,
+//     which over a long K leaves the 2e-2 tolerance, so the operand stays
+//     exact (128 + q) and the scale folds per group as in FOLD. For that an
+//     MFMA step must lie in one group: lane l = 16j + c loads word j of each
+//     of the round's four chunks (four 4-byte loads instead of one 16-byte
+//     load), so step i covers chunk 4r + i alone, whose group's scale folds
+//     into the step's sum (G = 64: every two steps).
 // ---------------------------------------------------------------------------
 constexpr int kKpU = 2;  // rounds in flight per wavefront
 
@@ -1147,32 +1158,31 @@ __device__ __forceinline__ u32x4 kp_int_op(uint32_t w, const DqRegs& k, uint32_t
   }
   return r;
 }
-// rounded tile RNE((q - z) * s): fp16 exact integer times s in one packed
-// multiply; bf16 through the exact fp32 FMA of exact_pair
+// fp16 rounded tile RNE((q - z) * s): the exact integer times s in one
+// packed multiply, which rounds once (fp16 only: a bf16 tile rounds too
+// coarsely for long K, see CHUNK below)
 template <typename T>
 __device__ __forceinline__ u32x4 kp_tile_op(uint32_t w, const DqRegs& k, uint32_t s_bits,
                                             uint32_t z) {
-  if constexpr (T::kIsF16) {
-    const u32x4 q = kp_int_op(w, k, z);
-    const f16x2 sc = __builtin_bit_cast(f16x2, (s_bits & 0xFFFFu) * 0x10001u);
-    u32x4 r;
+  static_assert(T::kIsF16, "rounded K-packed tiles are fp16 only");
+  const u32x4 q = kp_int_op(w, k, z);
+  const f16x2 sc = __builtin_bit_cast(f16x2, (s_bits & 0xFFFFu) * 0x10001u);
+  u32x4 r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t qi = q[i];  // through a scalar, as in kp_int_op
-      r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, qi) * sc);
-    }
-    return r;
-  } else {
-    return u32x4{exact_pair<0>(BF16{}, w, k, make_col<0>(BF16{}, s_bits, z)),
-                 exact_pair<1>(BF16{}, w, k, make_col<1>(BF16{}, s_bits, z)),
-                 exact_pair<2>(BF16{}, w, k, make_col<2>(BF16{}, s_bits, z)),
-                 exact_pair<3>(BF16{}, w, k, make_col<3>(BF16{}, s_bits, z))};
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t qi = q[i];  // through a scalar, as in kp_int_op
+    r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, qi) * sc);
   }
+  return r;
 }
 
-template <typename T, bool HAS_ZP, bool FOLD, bool LDSA>
+enum { kKpFold = 0, kKpTile = 1, kKpChunk32 = 2, kKpChunk64 = 3 };
+
+template <typename T, bool HAS_ZP, int NUM, bool LDSA>
 __global__ __launch_bounds__(kKpThreads) void kpacked_kernel(KPackedParams p) {
+  constexpr bool FOLD = NUM == kKpFold;
   __shared__ f32x4 red[kKpThreads / 64 - 1][64];
+  static_assert(sizeof(red) == kKpRedBytes, "host LDS accounting");
   extern __shared__ __attribute__((aligned(16))) uint16_t a_lds[];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -1208,6 +1218,48 @@ __global__ __launch_bounds__(kKpThreads) void kpacked_kernel(KPackedParams p) {
   }
   const uint16_t* alds = a_lds + min(c, mb - 1) * astride;
 
+  if constexpr (NUM == kKpChunk32 || NUM == kKpChunk64) {
+    constexpr int SPG = NUM == kKpChunk32 ? 1 : 2;  // MFMA steps per group
+    for (int r0 = r_beg; r0 < r_end; r0 += kKpU) {
+      uint32_t wv[kKpU][4], sb[kKpU][4], zb[kKpU][4];
+      u32x4 av[kKpU][4];
+#pragma unroll
+      for (int u = 0; u < kKpU; ++u) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ch = (r0 + u) * 4 + i;  // step i covers chunk ch alone
+          const bool live = row_ok && r0 + u < r_end && ch < KC;
+          const int cl = min(ch, KC - 1);
+          wv[u][i] = wrow[cl * 4 + j];
+          const int g = cl >> p.g_shift;
+          sb[u][i] = srow[g];
+          zb[u][i] = HAS_ZP ? (uint32_t)zrow[g] : (uint32_t)p.zp_bias;
+          const u32x4 v = LDSA ? *(const u32x4*)(alds + cl * 32 + 8 * j)
+                               : *(const u32x4*)(arow + cl * 32 + 8 * j);
+          av[u][i] = live ? v : zero4;  // dead K and padding rows add zero
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kKpU; ++u) {
+        if (r0 + u >= r_end) break;  // uniform over the wavefront
+#pragma unroll
+        for (int i0 = 0; i0 < 4; i0 += SPG) {
+          f32x4 part = {0.f, 0.f, 0.f, 0.f};
+          f32x4 sa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = i0; i < i0 + SPG; ++i) {
+            part = mfma<T>(av[u][i], kp_magic_op(wv[u][i], mag), part);
+            sa = mfma<T>(av[u][i], ones, sa);
+          }
+          // column c's scale and zero point of this group, loaded by the lane
+          const float s = widen(T{}, sb[u][i0]);
+          const float base = T::kBase + (float)zb[u][i0];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(s, __builtin_fmaf(-base, sa[v], part[v]), acc[v]);
+        }
+      }
+    }
+  } else
   for (int r0 = r_beg; r0 < r_end; r0 += kKpU) {
     u32x4 wv[kKpU], av[kKpU][4];
     uint32_t sb[kKpU], zb[kKpU];
@@ -1381,29 +1433,37 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, bool has_zp, int gr
   return has_zp ? prefill_gs<BF16, true>(p, grid, st) : prefill_gs<BF16, false>(p, grid, st);
 }
 
-template <typename T, bool Z>
-static hipError_t kpacked_go(const KPackedParams& p, bool fold, hipStream_t st) {
+template <typename T, bool Z, int NUM>
+static hipError_t kpacked_num(const KPackedParams& p, bool stage, hipStream_t st) {
   const dim3 grid((unsigned)((p.N + kKpCols - 1) / kKpCols), (unsigned)((p.M + kKpRows - 1) / kKpRows));
-  const int mb = p.M < kKpRows ? p.M : kKpRows;
-  const size_t lds = (size_t)mb * (p.K + 8) * 2;  // activation rows, padded
-  if (lds <= 60 * 1024) {
-    if (fold)
-      hipLaunchKernelGGL((kpacked_kernel<T, Z, true, true>), grid, dim3(kKpThreads), lds, st, p);
-    else
-      hipLaunchKernelGGL((kpacked_kernel<T, Z, false, true>), grid, dim3(kKpThreads), lds, st, p);
+  if (stage) {
+    hipLaunchKernelGGL((kpacked_kernel<T, Z, NUM, true>), grid, dim3(kKpThreads),
+                       kpacked_lds_bytes(p.M, p.K), st, p);
   } else {
-    if (fold)
-      hipLaunchKernelGGL((kpacked_kernel<T, Z, true, false>), grid, dim3(kKpThreads), 0, st, p);
-    else
-      hipLaunchKernelGGL((kpacked_kernel<T, Z, false, false>), grid, dim3(kKpThreads), 0, st, p);
+    hipLaunchKernelGGL((kpacked_kernel<T, Z, NUM, false>), grid, dim3(kKpThreads), 0, st, p);
   }
   return hipGetLastError();
 }
-hipError_t launch_kpacked(const KPackedParams& p, int dtype, bool has_zp, bool fold,
+// numerics: FOLD when a 128-K round lies in one group (G a multiple of 128,
+// or G == K); otherwise TILE for fp16 and CHUNK for bf16
+template <typename T, bool Z>
+static hipError_t kpacked_go(const KPackedParams& p, bool fold, bool stage, hipStream_t st) {
+  if (fold) return kpacked_num<T, Z, kKpFold>(p, stage, st);
+  if constexpr (T::kIsF16) {
+    return kpacked_num<T, Z, kKpTile>(p, stage, st);
+  } else {
+    if (p.g_shift == 0) return kpacked_num<T, Z, kKpChunk32>(p, stage, st);
+    if (p.g_shift == 1) return kpacked_num<T, Z, kKpChunk64>(p, stage, st);
+    return hipErrorInvalidValue;
+  }
+}
+hipError_t launch_kpacked(const KPackedParams& p, int dtype, bool has_zp, bool fold, bool stage,
                           hipStream_t st) {
   if (dtype == W4A16_F16)
-    return has_zp ? kpacked_go<F16, true>(p, fold, st) : kpacked_go<F16, false>(p, fold, st);
-  return has_zp ? kpacked_go<BF16, true>(p, fold, st) : kpacked_go<BF16, false>(p, fold, st);
+    return has_zp ? kpacked_go<F16, true>(p, fold, stage, st)
+                  : kpacked_go<F16, false>(p, fold, stage, st);
+  return has_zp ? kpacked_go<BF16, true>(p, fold, stage, st)
+                : kpacked_go<BF16, false>(p, fold, stage, st);
 }
 
 template <typename T, bool Z>

@@ -23,9 +23,10 @@ LIB_PATH = os.path.join(_PKG, "libw4a16.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "w4a16.h")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_GROUP, ERR_DTYPE, ERR_ZP, ERR_ALIGN, ERR_DEVICE, \
-    ERR_HIP, ERR_VALUE, ERR_PLAN = range(11)
+    ERR_HIP, ERR_VALUE, ERR_PLAN, ERR_WORKSPACE = range(12)
 STATUS_NAMES = ["OK", "NULL", "SHAPE", "GROUP", "DTYPE", "ZP", "ALIGN", "DEVICE",
-                "HIP", "VALUE", "PLAN"]
+                "HIP", "VALUE", "PLAN", "WORKSPACE"]
+WORKSPACE_COUNTER_BYTES = 65536   # W4A16_WORKSPACE_COUNTER_BYTES
 F16, BF16 = 0, 1
 ROUTE_NONE, ROUTE_DECODE, ROUTE_PREFILL = 0, 1, 2
 
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
     L.w4a16_gemm_bias.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, i64, i64, i64, i32, vp]
     L.w4a16_gemm_planned.argtypes = [vp, vp, vp, vp, i32, i32, vp, i64, i64, i64, i32,
                                      ctypes.POINTER(Plan), vp]
+    L.w4a16_gemm_ws.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, i64, i64, i64, i32, vp, i64, vp]
+    L.w4a16_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(i64)]
     L.w4a16_plan.argtypes = [i64, i64, i64, i32, i32, i32, i32, ctypes.POINTER(Plan)]
     L.w4a16_plan_route.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, i32, i32,
                                    ctypes.POINTER(Plan)]
@@ -78,7 +81,8 @@ def lib() -> ctypes.CDLL:
     L.w4a16_gemm_kpacked.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, i64, i64, i64, i32, vp]
     L.w4a16_pack_int4_kshuffle.argtypes = [vp, i64, i64, vp]
     L.w4a16_unpack_int4_kshuffle.argtypes = [vp, i64, i64, vp]
-    for f in ("w4a16_gemm", "w4a16_gemm_bias", "w4a16_gemm_planned", "w4a16_plan", "w4a16_plan_route",
+    for f in ("w4a16_gemm", "w4a16_gemm_bias", "w4a16_gemm_planned", "w4a16_gemm_ws",
+              "w4a16_workspace_bytes", "w4a16_plan", "w4a16_plan_route",
               "w4a16_dequant", "w4a16_pack_int4", "w4a16_unpack_int4", "w4a16_gemm_kpacked",
               "w4a16_pack_int4_kshuffle", "w4a16_unpack_int4_kshuffle"):
         getattr(L, f).restype = ctypes.c_int
@@ -142,6 +146,47 @@ def _shapes(a, b_q, scales, qzeros, group_size):
     return M, K, N
 
 
+_NUM_CUS: dict[int, int] = {}
+_WS: dict[tuple[int, int], torch.Tensor] = {}
+
+
+def workspace_bytes(M: int, K: int, N: int, group_size: int, dtype, num_cus: int = 256) -> int:
+    """Scratch bytes ``gemm_ws`` needs for one problem (0 if none; host only)."""
+    n = ctypes.c_int64(0)
+    _check(lib().w4a16_workspace_bytes(M, K, N, group_size, _DTYPE_CODE.get(dtype, dtype),
+                                       num_cus, ctypes.byref(n)))
+    return n.value
+
+
+def _num_cus(dev: torch.device) -> int:
+    i = dev.index if dev.index is not None else torch.cuda.current_device()
+    if i not in _NUM_CUS:
+        _NUM_CUS[i] = torch.cuda.get_device_properties(i).multi_processor_count
+    return _NUM_CUS[i]
+
+
+def stream_workspace(dev: torch.device, nbytes: int) -> torch.Tensor | None:
+    """A workspace of at least ``nbytes`` from torch's allocator for the
+    current stream of ``dev``, its counter region zero (``torch.zeros``, a
+    fill kernel on that stream). Outside graph capture one workspace per
+    (device, stream) is kept and reused: every completed launch leaves its
+    counters zero. During capture each call gets a fresh one from the
+    graph's pool (its fill is recorded in the graph), so no memory of the
+    graph is ever handed to eager work."""
+    if nbytes <= 0:
+        return None
+    stream = torch.cuda.current_stream(dev)
+    key = (dev.index, stream.cuda_stream)
+    if torch.cuda.is_current_stream_capturing():
+        return torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        size = max(nbytes, 2 * (0 if ws is None else ws.numel()))
+        ws = torch.zeros(size, dtype=torch.uint8, device=dev)
+        _WS[key] = ws
+    return ws
+
+
 def gemm(a: torch.Tensor, b_q: torch.Tensor, scales: torch.Tensor,
          qzeros: torch.Tensor | None = None, group_size: int = 128, zp_bias: int = 8,
          out: torch.Tensor | None = None, plan: Plan | None = None,
@@ -149,7 +194,11 @@ def gemm(a: torch.Tensor, b_q: torch.Tensor, scales: torch.Tensor,
     """``a @ dequant(b_q, scales, qzeros) (+ bias)`` on the GPU, in ``a``'s dtype.
 
     ``bias`` (optional, ``[N]`` in ``a``'s dtype) is added to the fp32 result
-    before the cast (PR #40977 "RDNA hybrid W4A16", Code section)."""
+    before the cast (PR #40977 "RDNA hybrid W4A16", Code section). Without a
+    forced ``plan`` the call goes through ``w4a16_gemm_ws`` with a workspace
+    from torch's allocator (``stream_workspace``), so it can be captured into
+    a graph on first use; with one, through ``w4a16_gemm_planned`` and the
+    library's per-stream workspace."""
     M, K, N = _shapes(a, b_q, scales, qzeros, group_size)
     if bias is not None:
         if plan is not None:
@@ -162,12 +211,36 @@ def gemm(a: torch.Tensor, b_q: torch.Tensor, scales: torch.Tensor,
     elif (tuple(out.shape) != (M, N) or out.dtype != a.dtype or out.device != a.device
           or not out.is_contiguous()):
         raise ValueError("out must be a contiguous [M, N] tensor like a")
-    args = gemm_args(a, b_q, scales, qzeros, group_size, zp_bias, out)
     if a.device.index == torch.cuda.current_device():
-        _run_gemm(args, plan, bias)
+        _gemm_on_device(a, b_q, scales, qzeros, group_size, zp_bias, out, plan, bias)
     else:
         with torch.cuda.device(a.device):
-            _run_gemm(args, plan, bias)
+            _gemm_on_device(a, b_q, scales, qzeros, group_size, zp_bias, out, plan, bias)
+    return out
+
+
+def _gemm_on_device(a, b_q, scales, qzeros, group_size, zp_bias, out, plan, bias):
+    args = gemm_args(a, b_q, scales, qzeros, group_size, zp_bias, out)
+    if plan is not None:
+        _run_gemm(args, plan, bias)
+        return
+    M, K = a.shape
+    nb = workspace_bytes(M, K, args[9], group_size, a.dtype, _num_cus(a.device))
+    ws = stream_workspace(a.device, nb)
+    _check(lib().w4a16_gemm_ws(*args[:6], _ptr(bias), *args[6:11], _ptr(ws), nb, args[11]))
+
+
+def gemm_ws(a, b_q, scales, qzeros, group_size, zp_bias, out, workspace, ws_bytes=None,
+            bias=None) -> torch.Tensor:
+    """``w4a16_gemm_ws`` with a caller-owned ``workspace`` (a device tensor,
+    or None when the problem needs none); shapes checked as in ``gemm``."""
+    _shapes(a, b_q, scales, qzeros, group_size)
+    args = gemm_args(a, b_q, scales, qzeros, group_size, zp_bias, out)
+    nb = (0 if workspace is None else workspace.numel() * workspace.element_size()) \
+        if ws_bytes is None else ws_bytes
+    with torch.cuda.device(a.device):
+        _check(lib().w4a16_gemm_ws(*args[:6], _ptr(bias), *args[6:11], _ptr(workspace), nb,
+                                   args[11]))
     return out
 
 
