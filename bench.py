@@ -50,6 +50,8 @@ def parse():
                     help="time the workload with the weights K-packed ([N, K/8], w4a16_gemm_kpacked)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the context ceilings (plain streaming read, dense bf16 matmul)")
     return ap.parse_args()
 
 
@@ -68,8 +70,9 @@ def flops(w) -> int:
 class Launch:
     """Device-resident inputs of one workload with rotated weight copies.
 
-    Calls go straight to the C ABI with argument tuples built once per copy
-    (``w4a16.gemm_args``), so the host enqueues faster than the GPU drains.
+    Calls go straight to the C ABI (``w4a16_gemm_ws`` with one caller-owned
+    workspace, or ``w4a16_gemm_kpacked``) with argument tuples built once per
+    copy, so the host enqueues faster than the GPU drains.
     """
 
     def __init__(self, w, torch, W, synthetic, rotate: bool, kpacked: bool = False):
@@ -95,6 +98,11 @@ class Launch:
         self.sets = [(bq, s, qz)] + [(bq.clone(), s.clone(), None if qz is None else qz.clone())
                                      for _ in range(copies - 1)]
         self.out = torch.empty((w.M, w.N), dtype=dt, device=dev)
+        # caller-owned scratch (counter region zeroed once), shared by the
+        # rotated copies: the launches run one after another on one stream
+        nb = 0 if kpacked else W.workspace_bytes(w.M, w.K, w.N, w.group_size, dt,
+                                                 torch.cuda.get_device_properties(0).multi_processor_count)
+        self.ws = torch.zeros(nb, dtype=torch.uint8, device=dev) if nb else None
         self.W = W
         self.args = None
         self.i = 0
@@ -105,14 +113,14 @@ class Launch:
             self.args = [self.W.gemm_kpacked_args(self.a, bq, s, qz, self.w.group_size, 8, self.out)
                          for bq, s, qz in self.sets]
         else:
-            self.args = [self.W.gemm_args(self.a, bq, s, qz, self.w.group_size, 8, self.out)
-                         for bq, s, qz in self.sets]
+            self.args = [self.W.gemm_ws_args(self.a, bq, s, qz, self.w.group_size, 8, self.out,
+                                             self.ws) for bq, s, qz in self.sets]
 
     def __call__(self):
         if self.kpacked:
             self.W.launch_kpacked(self.args[self.i % len(self.args)])
         else:
-            self.W.launch(self.args[self.i % len(self.args)])
+            self.W.launch_ws(self.args[self.i % len(self.args)])
         self.i += 1
 
 
@@ -172,6 +180,84 @@ def time_graph(launches, steps, torch):
     for L in launches:              # back to the eager stream
         L.bind()
     return t0.elapsed_time(t1)
+
+
+def _graph_time(fn_list, torch):
+    """Capture one call of each fn into a HIP graph, replay it three times
+    untimed, then once timed with HIP events on the replaying stream;
+    returns ms per call."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for f in fn_list:
+                f()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    t0.record(stream)
+    g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / len(fn_list)
+
+
+def context_read(torch, nbytes, launches=60):
+    """Achievable HBM read rate of one launch of ``nbytes``: a plain
+    streaming-read kernel (``libw4a16_probe.so``) over copies rotated across
+    >= 512 MB, graph-replayed; the best of a few grid sizes."""
+    import ctypes
+    probe = ctypes.CDLL(os.path.join(ROOT, "weight_only_int4_unpack_amd", "libw4a16_probe.so"))
+    probe.w4a16_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = (nbytes + 15) // 16 * 16
+    copies = max(2, math.ceil(ROTATE_BYTES / nbytes))
+    bufs = [torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda")
+            for _ in range(copies)]
+    best = None
+    for blocks in (1024, 2048, 4096, 8192):
+        out = torch.empty(blocks, dtype=torch.int32, device="cuda")
+
+        def mk(b, blocks=blocks, out=out):
+            def f():
+                st = probe.w4a16_probe_read(b.data_ptr(), nbytes, blocks, 0x9E3779B9,
+                                            out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+                assert st == 0, st
+            return f
+        ms = _graph_time([mk(bufs[i % copies]) for i in range(launches)], torch)
+        if best is None or ms < best[0]:
+            best = (ms, blocks)
+    ms, blocks = best
+    del bufs
+    return {"bytes": nbytes, "us_per_launch": round(ms * 1e3, 2),
+            "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "workgroups": blocks,
+            "how": f"plain 16-byte streaming read, {copies} copies rotated, {launches} launches "
+                   "graph-replayed, best grid of 1024/2048/4096/8192 x 256 threads"}
+
+
+def context_matmul(torch, M=2048, K=5120, N=17408, launches=20):
+    """Dense bf16 torch.matmul (hipBLASLt) at the prefill shape, the weights
+    as a plain [K, N] bf16 matrix rotated over >= 512 MB, graph-replayed."""
+    a = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+    copies = max(2, math.ceil(ROTATE_BYTES / (K * N * 2)))
+    ws = [torch.randn(K, N, device="cuda").to(torch.bfloat16) for _ in range(copies)]
+    out = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    for w in ws:                                     # warm up the library's choice
+        torch.matmul(a, w, out=out)
+    torch.cuda.synchronize()
+    fns = [(lambda w=ws[i % copies]: torch.matmul(a, w, out=out)) for i in range(launches)]
+    ms = _graph_time(fns, torch)
+    del ws
+    tf = 2 * M * N * K / (ms * 1e-3) / 1e12
+    return {"shape": [M, K, N], "us_per_launch": round(ms * 1e3, 2), "tflops": round(tf, 1),
+            "frac_of_mfma_peak": round(tf / MFMA_PEAK_TFLOPS, 4),
+            "how": f"torch.matmul bf16 [M,K] x [K,N], {copies} weight copies rotated, "
+                   f"{launches} launches graph-replayed"}
 
 
 def load_traffic(path, name, src_hash):
@@ -342,6 +428,13 @@ def main():
                                          "frac_of_mfma_peak": round(tf / MFMA_PEAK_TFLOPS, 4),
                                          "us_per_launch": round(pus, 2),
                                          "plan": pf["plan"]}}
+        if names == ["decode_m1", "decode_m5"] and not kpacked and not args.no_context:
+            # achievable ceilings on this GPU, for reading value and the
+            # prefill figure against (context, not the specification peaks)
+            ctx = {"read_46mb": context_read(torch, res[0]["bytes"])}
+            if not args.no_prefill_extra:
+                ctx["dense_bf16_matmul_prefill_shape"] = context_matmul(torch)
+            line.setdefault("extra", {})["context"] = ctx
         if not args.no_cpu and cpu is None and not args.all:
             cpu = cpu_baseline(wl)
             if is_prefill:

@@ -288,17 +288,24 @@ def _factored_zero_bound(p, zp):
     return bound * (1 + 2.0 ** -7) + tiny
 
 
-# Linearity, bit for bit on every route: scaling S or a by 2 scales every
-# product and every partial sum by 2 with no change in rounding (no overflow
-# or underflow at these magnitudes), and negating a negates every sum (IEEE
-# rounding is symmetric); the reductions are deterministic, so the outputs
-# must be exactly 2C and -C.
+# Linearity. Scaling S or a by 2 scales every product and every partial sum
+# by 2 with no change in rounding (no overflow or underflow at these
+# magnitudes), on any hardware summation that aligns in binary; the
+# reductions are deterministic, so the outputs must be exactly 2C, bit for
+# bit, on every route. Negating a negates every product; with IEEE rounding
+# to nearest every sum would negate exactly too, and on the bf16 routes and
+# the fp16 prefill (integer operand) the output is exactly -C. The fp16
+# matrix-core dot product is not sign-symmetric in its internal rounding
+# (measured on MI355X: a few outputs in a thousand off by 1-2 ulp on the fp16
+# decode routes, including the one fed plain rounded weights), so there the
+# pin is -C within 2 ulp of the output on every element, and at most 1 % of
+# the outputs differing at all.
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("M", [5, 100])
 def test_linearity_bitwise(M, dtype):
     p = random_problem(M, 1024, 512, 64, dtype, True, seed=77)
     routes = _routes(M)
-    base = {label: O.to_f32(dev_to_bits(p.gpu_gemm(plan=mk(p))), dtype) for label, mk in routes}
+    base = {label: dev_to_bits(p.gpu_gemm(plan=mk(p))) for label, mk in routes}
     a0, s0 = p.a, p.s
     for what, factor in (("s*2", 2.0), ("a*2", 2.0), ("-a", -1.0)):
         p.a, p.s = a0, s0
@@ -307,8 +314,19 @@ def test_linearity_bitwise(M, dtype):
         else:
             p.a = a0 * factor
         for label, mk in routes:
-            got = O.to_f32(dev_to_bits(p.gpu_gemm(plan=mk(p))), dtype)
-            assert np.array_equal(got, factor * base[label]), (what, label)
+            pl = mk(p)
+            bits = dev_to_bits(p.gpu_gemm(plan=pl))
+            got, want = O.to_f32(bits, dtype), factor * O.to_f32(base[label], dtype)
+            eff = pl if pl is not None else W.plan(M, p.K, p.N, p.G, True, TORCH_DT[dtype])
+            if what == "-a" and dtype == "fp16" and eff.route == W.ROUTE_DECODE:
+                # magnitudes within 2 ulp, signs opposite to the base result
+                ulps = np.abs((bits & 0x7FFF).astype(np.int32) -
+                              (base[label] & 0x7FFF).astype(np.int32))
+                flipped = (bits >> 15) != (base[label] >> 15)
+                assert np.all(flipped | (got == want)), (what, label)
+                assert int(ulps.max()) <= 2 and np.mean(got != want) <= 0.01, (what, label)
+            else:
+                assert np.array_equal(got, want), (what, label)
     p.a, p.s = a0, s0
 
 

@@ -13,6 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libw4a16.so")
+# measurement probe for bench.py (a plain streaming read), its own library
+PROBE_LIB = os.path.join(PKG, "libw4a16_probe.so")
 
 ARCH = "gfx950"
 # Packed fp32 ops stay off: hipcc still emits v_pk_* f16 ops, which are
@@ -46,6 +48,10 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     for o in objs:
         os.remove(o)
+    tmp = PROBE_LIB + ".tmp"
+    _run([cc, *HIP_FLAGS, "-x", "hip", "-shared", os.path.join(CSRC, "probe_read.hip"),
+          "-o", tmp], verbose)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

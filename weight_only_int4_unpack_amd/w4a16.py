@@ -264,6 +264,22 @@ def _run_gemm(args, plan, bias=None):
         _check(L.w4a16_gemm_planned(*args[:-1], ctypes.byref(plan), args[-1]))
 
 
+def gemm_ws_args(a, b_q, scales, qzeros, group_size, zp_bias, out, workspace, bias=None):
+    """The ``w4a16_gemm_ws`` argument tuple of one GEMM with a caller-owned
+    ``workspace`` tensor (or None), for repeated launches without re-checking
+    shapes; pass it to ``launch_ws``."""
+    M, K = a.shape
+    N = b_q.shape[1] * 8
+    nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return (_ptr(a), _ptr(b_q), _ptr(scales), _ptr(qzeros), group_size, zp_bias, _ptr(bias),
+            _ptr(out), M, K, N, _DTYPE_CODE[a.dtype], _ptr(workspace), nb, _stream(a.device))
+
+
+def launch_ws(args) -> None:
+    """Run a tuple made by ``gemm_ws_args`` (on the stream it names)."""
+    _check(lib().w4a16_gemm_ws(*args))
+
+
 def launch(args) -> None:
     """Run a tuple made by ``gemm_args`` (on the stream it names)."""
     st = lib().w4a16_gemm(*args)
