@@ -189,6 +189,27 @@ w4a16_status w4a16_gemm_ws(const void* a, const int32_t* b_q, const void* scales
                            int32_t dtype, void* workspace, int64_t ws_bytes, void* stream);
 
 /*
+ * w4a16_gemm_noalloc - as w4a16_gemm_bias (bias may be NULL), for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). Its scratch is a fixed
+ * device array inside the library, one copy per GPU, held until the process
+ * ends: W4A16_NOALLOC_SCRATCH_BYTES, i.e. the counter region plus 32 MiB of
+ * fp32 partials; a problem whose split-K partials need more is refused with
+ * WORKSPACE before anything runs (w4a16_workspace_bytes gives the need). The
+ * call allocates nothing; its first call on a device looks up the array's
+ * address and clears its counter region with a kernel on `stream`. Every
+ * call on one GPU shares that GPU's array: calls that may overlap in time
+ * (different streams, or several threads) race on it and must be ordered by
+ * the caller, e.g. issued to one stream.
+ * Errors: those of w4a16_gemm_bias, and WORKSPACE.
+ */
+#define W4A16_NOALLOC_SCRATCH_BYTES (W4A16_WORKSPACE_COUNTER_BYTES + (32ll << 20))
+w4a16_status w4a16_gemm_noalloc(const void* a, const int32_t* b_q, const void* scales,
+                                const int32_t* qzeros, int32_t group_size, int32_t zp_bias,
+                                const void* bias, void* out, int64_t M, int64_t K, int64_t N,
+                                int32_t dtype, void* stream);
+
+/*
  * w4a16_plan - the launch w4a16_gemm would make (host only, no GPU call):
  * route by the real M (PR #40977 "RDNA hybrid W4A16", Impl. item 5: the
  * skinny kernel for small batches, the tiled kernel above) and tiles from

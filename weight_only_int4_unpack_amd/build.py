@@ -22,7 +22,7 @@ ARCH = "gfx950"
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wall", "-Wno-unused-function"]
-SOURCES = ["w4a16_host.cpp", "w4a16_kernels.hip"]
+SOURCES = ["w4a16_host.cpp", "w4a16_kernels.hip", "w4a16_noalloc.hip"]
 
 
 def hipcc() -> str:

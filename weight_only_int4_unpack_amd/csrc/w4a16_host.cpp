@@ -457,7 +457,7 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, void* ws, hip
 }
 
 // Where a call's scratch comes from.
-enum class WsMode { Library, Caller };
+enum class WsMode { Library, Caller, Static };
 
 w4a16_status gemm_common(const void* a, const int32_t* b_q, const void* scales,
                          const int32_t* qzeros, int32_t G, int32_t zp_bias, const void* bias,
@@ -491,6 +491,15 @@ w4a16_status gemm_common(const void* a, const int32_t* b_q, const void* scales,
                   (long long)q.workspace_bytes, (long long)ws_bytes);
     return W4A16_OK;
   };
+  if (wsm == WsMode::Static) {  // the fixed array's size, checked without a device
+    w4a16_plan_t pre;
+    st = make_plan(M, K, N, G, dtype, 256, 0, 0, -1, &pre);
+    if (st != W4A16_OK) return st;
+    if (pre.workspace_bytes > w4a16::kStaticScratchBytes)
+      return fail(W4A16_ERR_WORKSPACE,
+                  "the launch needs %lld bytes of scratch; the fixed array holds %lld",
+                  (long long)pre.workspace_bytes, (long long)w4a16::kStaticScratchBytes);
+  }
   if (wsm == WsMode::Caller) {
     w4a16_plan_t pre;
     if (forced) {
@@ -525,6 +534,14 @@ w4a16_status gemm_common(const void* a, const int32_t* b_q, const void* scales,
       st = check_ws(pl);
       if (st != W4A16_OK) return st;
       scratch = ws;
+    } else if (wsm == WsMode::Static) {
+      if (pl.workspace_bytes > w4a16::kStaticScratchBytes)
+        return fail(W4A16_ERR_WORKSPACE,
+                    "the launch needs %lld bytes of scratch; the fixed array holds %lld",
+                    (long long)pl.workspace_bytes, (long long)w4a16::kStaticScratchBytes);
+      const hipError_t e = w4a16::static_scratch((hipStream_t)stream, &scratch);
+      if (e != hipSuccess)
+        return fail(W4A16_ERR_HIP, "fixed scratch array: %s", hipGetErrorString(e));
     } else {
       st = stream_workspace(ds, (hipStream_t)stream, (size_t)pl.workspace_bytes, &scratch);
       if (st != W4A16_OK) return st;
@@ -578,6 +595,14 @@ w4a16_status w4a16_gemm_ws(const void* a, const int32_t* b_q, const void* scales
                            int32_t dtype, void* workspace, int64_t ws_bytes, void* stream) {
   return gemm_common(a, b_q, scales, qzeros, group_size, zp_bias, bias, out, M, K, N, dtype,
                      nullptr, stream, WsMode::Caller, workspace, ws_bytes);
+}
+
+w4a16_status w4a16_gemm_noalloc(const void* a, const int32_t* b_q, const void* scales,
+                                const int32_t* qzeros, int32_t group_size, int32_t zp_bias,
+                                const void* bias, void* out, int64_t M, int64_t K, int64_t N,
+                                int32_t dtype, void* stream) {
+  return gemm_common(a, b_q, scales, qzeros, group_size, zp_bias, bias, out, M, K, N, dtype,
+                     nullptr, stream, WsMode::Static);
 }
 
 w4a16_status w4a16_plan(int64_t M, int64_t K, int64_t N, int32_t group_size, int32_t has_zp,

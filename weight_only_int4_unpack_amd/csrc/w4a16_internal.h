@@ -43,6 +43,7 @@ constexpr int64_t kMaxCounterBlocks = kCounterBytes / (kDecodeWaves * (int64_t)s
 // the fixed device array of the entry point that allocates nothing
 constexpr int64_t kStaticPartialBytes = 32ll << 20;
 constexpr int64_t kStaticScratchBytes = kCounterBytes + kStaticPartialBytes;
+static_assert(kStaticScratchBytes == W4A16_NOALLOC_SCRATCH_BYTES, "header and library agree");
 
 // partial sums of the 4 wavefronts, then the staged scales (halves) and
 // packed zero points (words) of at most ng_max groups

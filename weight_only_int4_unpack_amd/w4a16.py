@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
                                      ctypes.POINTER(Plan), vp]
     L.w4a16_gemm_ws.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, i64, i64, i64, i32, vp, i64, vp]
     L.w4a16_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(i64)]
+    L.w4a16_gemm_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, i64, i64, i64, i32, vp]
     L.w4a16_plan.argtypes = [i64, i64, i64, i32, i32, i32, i32, ctypes.POINTER(Plan)]
     L.w4a16_plan_route.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, i32, i32,
                                    ctypes.POINTER(Plan)]
@@ -82,7 +83,7 @@ def lib() -> ctypes.CDLL:
     L.w4a16_pack_int4_kshuffle.argtypes = [vp, i64, i64, vp]
     L.w4a16_unpack_int4_kshuffle.argtypes = [vp, i64, i64, vp]
     for f in ("w4a16_gemm", "w4a16_gemm_bias", "w4a16_gemm_planned", "w4a16_gemm_ws",
-              "w4a16_workspace_bytes", "w4a16_plan", "w4a16_plan_route",
+              "w4a16_workspace_bytes", "w4a16_gemm_noalloc", "w4a16_plan", "w4a16_plan_route",
               "w4a16_dequant", "w4a16_pack_int4", "w4a16_unpack_int4", "w4a16_gemm_kpacked",
               "w4a16_pack_int4_kshuffle", "w4a16_unpack_int4_kshuffle"):
         getattr(L, f).restype = ctypes.c_int
@@ -228,6 +229,19 @@ def _gemm_on_device(a, b_q, scales, qzeros, group_size, zp_bias, out, plan, bias
     nb = workspace_bytes(M, K, args[9], group_size, a.dtype, _num_cus(a.device))
     ws = stream_workspace(a.device, nb)
     _check(lib().w4a16_gemm_ws(*args[:6], _ptr(bias), *args[6:11], _ptr(ws), nb, args[11]))
+
+
+NOALLOC_SCRATCH_BYTES = WORKSPACE_COUNTER_BYTES + (32 << 20)   # W4A16_NOALLOC_SCRATCH_BYTES
+
+
+def gemm_noalloc(a, b_q, scales, qzeros, group_size, zp_bias, out, bias=None) -> torch.Tensor:
+    """``w4a16_gemm_noalloc``: scratch from the library's fixed device array
+    (no allocation); shapes checked as in ``gemm``."""
+    _shapes(a, b_q, scales, qzeros, group_size)
+    args = gemm_args(a, b_q, scales, qzeros, group_size, zp_bias, out)
+    with torch.cuda.device(a.device):
+        _check(lib().w4a16_gemm_noalloc(*args[:6], _ptr(bias), *args[6:]))
+    return out
 
 
 def gemm_ws(a, b_q, scales, qzeros, group_size, zp_bias, out, workspace, ws_bytes=None,
