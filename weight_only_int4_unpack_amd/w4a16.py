@@ -19,7 +19,9 @@ import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libw4a16.so")
+# W4A16_LIB names another build of the same ABI (the host-side sanitizer
+# build used by ``sanitize.py``); by default the in-tree gfx950 library
+LIB_PATH = os.environ.get("W4A16_LIB") or os.path.join(_PKG, "libw4a16.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "w4a16.h")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_GROUP, ERR_DTYPE, ERR_ZP, ERR_ALIGN, ERR_DEVICE, \
