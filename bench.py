@@ -52,6 +52,8 @@ def parse():
                     help="also run a plain device copy of known size (counter calibration)")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the context ceilings (plain streaming read, dense bf16 matmul)")
+    ap.add_argument("--read-probe", type=int, default=0, metavar="BYTES",
+                    help="only time the plain streaming read of BYTES (context ceiling) and exit")
     return ap.parse_args()
 
 
@@ -346,6 +348,9 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     rotate = not args.warm
+    if args.read_probe:
+        print(json.dumps({"read_probe": context_read(torch, args.read_probe)}), flush=True)
+        return
 
     if args.copy_probe:
         x = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
