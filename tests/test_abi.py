@@ -256,7 +256,10 @@ def test_selector_prefill_tiles():
                                      (16, 4096, 4096, 4096), (300, 2112, 5120, 64)])
 def test_selector_prefill_splits(M, K, N, G):
     p = W.plan(M, K, N, G, True, torch.bfloat16, route=W.ROUTE_PREFILL)
-    tiles = -(-M // 64) * -(-N // 256)
+    # tile rows: 64, or 16 / 32 for M <= 16 / 64 when K % 64 == 0 and K splits
+    assert p.block_m == (64 if K % 64 or M > 64 or p.splits == 1 else (16 if M <= 16 else 32))
+    assert p.lds_bytes == 2 * p.block_m * 80 * 2
+    tiles = -(-M // p.block_m) * -(-N // 256)
     KT = -(-K // 64)
     S, ks = p.splits, p.steps_per_wave
     assert 1 <= S <= 32
@@ -300,7 +303,7 @@ def test_prefill_forced_split_errors():
     with pytest.raises(W.W4A16Error):     # 64 stages, 1 per split: 64 > 32 splits
         W.plan(64, 4096, 4096, 32, False, torch.bfloat16, route=W.ROUTE_PREFILL, steps_per_wave=1)
     p = W.plan(64, 4096, 4096, 32, False, torch.bfloat16, route=W.ROUTE_PREFILL, steps_per_wave=16)
-    assert p.splits == 4 and p.grid == 64
+    assert p.splits == 4 and p.block_m == 32 and p.grid == (64 // 32) * 16 * 4
 
 
 def test_planned_call_rejects_mismatched_plan():

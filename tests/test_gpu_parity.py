@@ -111,6 +111,34 @@ def test_prefill_tiles_parity(K, G, dtype, zp):
     assert_within_tolerance(got, p.oracle_gemm(), dtype, f"K={K} G={G} {dtype} zp={zp}")
 
 
+# Tiles of 16 and 32 rows (few rows, K splits): several tiles with a ragged
+# last one (M = 40 over 32-row tiles, M = 12 and 16 in one 16-row tile), every
+# group span, both dtypes, zero points, ragged N; and bit for bit on exact
+# inputs, through the selector's own plan.
+SMALL_TILES = [(M, G, dtype, zp) for M in (12, 16, 40, 64) for G in (32, 64, 128, 1024)
+               for dtype in ("fp16", "bf16") for zp in (False, True) if (G + M) % 3 != 1]
+
+
+@pytest.mark.parametrize("M,G,dtype,zp", SMALL_TILES)
+def test_small_prefill_tiles_parity(M, G, dtype, zp):
+    K, N = 1024, 776
+    p = random_problem(M, K, N, G, dtype, zp, seed=M * 3 + G)
+    plan = _plan(p, W.ROUTE_PREFILL)
+    assert plan.block_m == (16 if M <= 16 else 32) and plan.splits > 1
+    assert_within_tolerance(dev_to_bits(p.gpu_gemm(plan=plan)), p.oracle_gemm(), dtype,
+                            f"M={M} G={G} {dtype} zp={zp} bm={plan.block_m}")
+
+
+@pytest.mark.parametrize("M,dtype", [(16, "bf16"), (40, "fp16"), (9, "fp16"), (64, "bf16")])
+def test_small_prefill_tiles_exact_bitwise(M, dtype):
+    q = _exact_problem(M, 2048, 520, 128, dtype, True, seed=90 + M)
+    plan = _plan(q, W.ROUTE_PREFILL)
+    assert plan.block_m in (16, 32)
+    got = dev_to_bits(q.gpu_gemm(plan=plan))
+    want = q.oracle_gemm()
+    assert np.array_equal(got, want), f"M={M}: {int((got != want).sum())} differ"
+
+
 # bf16 prefill with groups of 128 over a long K (8576 = 67 groups), unsplit
 # and with forced K splits of 35 and 3 groups, so that splits start at group
 # offsets other than 0; tolerance against the oracle and the exact-arithmetic
