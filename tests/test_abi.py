@@ -256,8 +256,8 @@ def test_selector_prefill_tiles():
                                      (16, 4096, 4096, 4096), (300, 2112, 5120, 64)])
 def test_selector_prefill_splits(M, K, N, G):
     p = W.plan(M, K, N, G, True, torch.bfloat16, route=W.ROUTE_PREFILL)
-    # tile rows: 64, or 16 / 32 for M <= 16 / 64 when K % 64 == 0 and K splits
-    assert p.block_m == (64 if K % 64 or M > 64 or p.splits == 1 else (16 if M <= 16 else 32))
+    # tile rows: 64, or 32 for M <= 64 when K % 64 == 0 and K splits
+    assert p.block_m == (64 if K % 64 or M > 64 or p.splits == 1 else 32)
     assert p.lds_bytes == 2 * p.block_m * 80 * 2
     tiles = -(-M // p.block_m) * -(-N // 256)
     KT = -(-K // 64)

@@ -111,10 +111,10 @@ def test_prefill_tiles_parity(K, G, dtype, zp):
     assert_within_tolerance(got, p.oracle_gemm(), dtype, f"K={K} G={G} {dtype} zp={zp}")
 
 
-# Tiles of 16 and 32 rows (few rows, K splits): several tiles with a ragged
-# last one (M = 40 over 32-row tiles, M = 12 and 16 in one 16-row tile), every
-# group span, both dtypes, zero points, ragged N; and bit for bit on exact
-# inputs, through the selector's own plan.
+# Tiles of 32 rows (few rows, K splits): several tiles with a ragged last one
+# (M = 40 and 64 over 32-row tiles, M = 12 and 16 in one), every group span,
+# both dtypes, zero points, ragged N; and bit for bit on exact inputs,
+# through the selector's own plan.
 SMALL_TILES = [(M, G, dtype, zp) for M in (12, 16, 40, 64) for G in (32, 64, 128, 1024)
                for dtype in ("fp16", "bf16") for zp in (False, True) if (G + M) % 3 != 1]
 
@@ -124,7 +124,7 @@ def test_small_prefill_tiles_parity(M, G, dtype, zp):
     K, N = 1024, 776
     p = random_problem(M, K, N, G, dtype, zp, seed=M * 3 + G)
     plan = _plan(p, W.ROUTE_PREFILL)
-    assert plan.block_m == (16 if M <= 16 else 32) and plan.splits > 1
+    assert plan.block_m == 32 and plan.splits > 1
     assert_within_tolerance(dev_to_bits(p.gpu_gemm(plan=plan)), p.oracle_gemm(), dtype,
                             f"M={M} G={G} {dtype} zp={zp} bm={plan.block_m}")
 
@@ -133,7 +133,7 @@ def test_small_prefill_tiles_parity(M, G, dtype, zp):
 def test_small_prefill_tiles_exact_bitwise(M, dtype):
     q = _exact_problem(M, 2048, 520, 128, dtype, True, seed=90 + M)
     plan = _plan(q, W.ROUTE_PREFILL)
-    assert plan.block_m in (16, 32)
+    assert plan.block_m == 32
     got = dev_to_bits(q.gpu_gemm(plan=plan))
     want = q.oracle_gemm()
     assert np.array_equal(got, want), f"M={M}: {int((got != want).sum())} differ"

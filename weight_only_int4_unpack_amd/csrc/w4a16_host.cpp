@@ -205,17 +205,17 @@ w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dty
 // M = 16 and 256, since every split adds M x N x 8 bytes of partial traffic;
 // 13.4 vs 14.8 us at M = 16, 32.7 vs 34.0 us at M = 256.)
 //
-// Tile rows: 64, or for few rows (M <= 16: 16, M <= 64: 32) when K % 64 == 0
-// and the launch splits K, so that fewer MFMA rows are padding and more
-// workgroups fit a CU (K = N = 4096: M = 16 12.2 vs 13.1 us, M = 64 17.7 vs
-// 20.0 us with 32-row tiles; a 2048-row prefill is faster with 64).
+// Tile rows: 64, or 32 for M <= 64 when K % 64 == 0 and the launch splits
+// K, so that fewer MFMA rows are padding and more workgroups fit a CU
+// (K = N = 4096: M = 16 12.2 vs 13.1 us, M = 64 17.7 vs 20.0 us with 32-row
+// tiles; a 2048-row prefill is faster with 64).
 w4a16_status plan_prefill_bm(int64_t M, int64_t K, int64_t N, int32_t G, int num_cus,
                              int32_t ks_forced, int64_t BM, w4a16_plan_t* pl);
 
 w4a16_status plan_prefill(int64_t M, int64_t K, int64_t N, int32_t G, int num_cus,
                           int32_t ks_forced, w4a16_plan_t* pl) {
   using namespace w4a16;
-  const int64_t small = M <= 16 ? 16 : (M <= 64 ? 32 : kPrefillBM);
+  const int64_t small = M <= 64 ? 32 : kPrefillBM;
   if (small < kPrefillBM && K % kPrefillBK == 0) {
     w4a16_plan_t q{};
     w4a16_status st = plan_prefill_bm(M, K, N, G, num_cus, ks_forced, small, &q);

@@ -21,7 +21,7 @@ constexpr int kDecodeMaxSteps = 8;     // most 32-row steps one wavefront stream
 constexpr int kAutoDecodeMaxM = 8;     // selector: decode for 1 <= M <= this (prefill with K splits wins above)
 
 // ---- prefill route (tiled MFMA)
-constexpr int kPrefillBM = 64;         // rows per workgroup tile (16 or 32 for few rows, with K splits)
+constexpr int kPrefillBM = 64;         // rows per workgroup tile (32 for few rows, with K splits)
 constexpr int kPrefillBN = 256;        // output columns per workgroup (4 waves x 64)
 constexpr int kPrefillBK = 64;         // K rows per pipeline stage
 constexpr int kPrefillThreads = 256;
@@ -107,7 +107,7 @@ struct PrefillParams {
   const uint16_t* bias;  // nullable [N] (unused when S > 1: the reduction adds it)
   uint16_t* out;
   int32_t M, K, N, G, zp_bias;
-  int32_t bm;         // rows per workgroup tile: 64, or 32 / 16 (K splits only)
+  int32_t bm;         // rows per workgroup tile: 64, or 32 (K splits only)
   int32_t g_shift;    // log2(G) when G is 32, 64 or 128 (unused when G == K)
   int32_t tiles_m, tiles_n, tiles, per_xcd;
   int32_t band;       // tile rows per band of the workgroup -> tile order

@@ -723,18 +723,19 @@ __device__ __forceinline__ V ldg(const char* base, uint32_t off) {
 // K; activations load in 16-byte pieces (KM = 1, K % 8 == 0) or one at a time.
 // ---------------------------------------------------------------------------
 // BM: rows per workgroup tile, 64 (two workgroups per CU, 252 VGPRs) or, for
-// few rows, 32 or 16 (fewer padding rows in the MFMAs, fewer registers, three
-// or four workgroups per CU; measured at K = N = 4096: M = 64 in 17.7 us with
-// 32-row tiles against 20.0 us with 64-row tiles, while the 2048-row prefill
-// takes 506 us with 32-row tiles against 426 us, each weight being
-// dequantised twice as often).
+// few rows, 32 (fewer padding rows in the MFMAs, fewer registers, three
+// workgroups per CU; measured at K = N = 4096: M = 64 in 17.7 us with 32-row
+// tiles against 20.0 us with 64-row tiles, M = 16 12.2 against 13.1 us, while
+// the 2048-row prefill takes 506 us with 32-row tiles against 426 us, each
+// weight being dequantised twice as often). 16-row tiles were slower than 32
+// at M = 16 (14.3 us; with four workgroups per CU they spilled to scratch).
 template <typename T, bool HAS_ZP, int GS, int KM, bool SPLIT, int BM>
-__global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : (BM == 32 ? 3 : 4)) void prefill_kernel(
+__global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_kernel(
     PrefillParams p) {
-  static_assert(BM == 16 || BM == 32 || BM == 64, "tile rows");
+  static_assert(BM == 32 || BM == 64, "tile rows");
   constexpr int RH = kPrefillLdsRowHalves;
   constexpr int MB = BM / 16;
-  constexpr int AP = (BM + 31) / 32;  // 16-byte A pieces per thread per stage (BM = 16: half the threads)
+  constexpr int AP = BM / 32;  // 16-byte A pieces per thread per stage
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * RH];
 
   const int tid = threadIdx.x;
@@ -824,7 +825,7 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : (BM == 32 ? 3 : 4))
 #pragma unroll
     for (int j = 0; j < AP; ++j) {
       const int row = j * 32 + (tid >> 3);
-      if (BM >= 32 || row < BM) *(u32x4*)&As[buf][row * RH + (tid & 7) * 8] = ar[j];
+      *(u32x4*)&As[buf][row * RH + (tid & 7) * 8] = ar[j];
     }
   };
   // One slab's weights (rows 8g..8g+7, two rows per register) and, for a
@@ -1407,17 +1408,13 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, bool has_zp, int mode
                 : decode_mode<BF16, false>(p, mode, grid, lds, st);
 }
 
-// 64-row tiles in every variant; 32- and 16-row tiles only with K splits and
+// 64-row tiles in every variant; 32-row tiles only with K splits and
 // K % 64 == 0 (the host's planner never asks for others)
 template <typename T, bool Z, int GS, int KM>
 static hipError_t prefill_go(const PrefillParams& p, int grid, hipStream_t st) {
   const dim3 g(grid), b(kPrefillThreads);
   if (p.S > 1) {
     if constexpr (KM == 0) {
-      if (p.bm == 16) {
-        hipLaunchKernelGGL((prefill_kernel<T, Z, GS, KM, true, 16>), g, b, 0, st, p);
-        return hipGetLastError();
-      }
       if (p.bm == 32) {
         hipLaunchKernelGGL((prefill_kernel<T, Z, GS, KM, true, 32>), g, b, 0, st, p);
         return hipGetLastError();
