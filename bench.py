@@ -54,6 +54,12 @@ def parse():
                     help="skip the context ceilings (plain streaming read, dense bf16 matmul)")
     ap.add_argument("--read-probe", type=int, default=0, metavar="BYTES",
                     help="only time the plain streaming read of BYTES (context ceiling) and exit")
+    ap.add_argument("--issue-probe", action="store_true",
+                    help="only run the instruction-issue probe (cycles per instruction of one "
+                         "wavefront, MFMA with 0-32 FMAs each, 1 and 2 wavefronts per SIMD) and exit")
+    ap.add_argument("--prefill-stages", default="",
+                    help="comma-separated 64-row K stages per split (0 = selector's) to force on "
+                         "the prefill route for --workload; one line per value (split-count sweep)")
     return ap.parse_args()
 
 
@@ -262,6 +268,67 @@ def context_matmul(torch, M=2048, K=5120, N=17408, launches=20):
                    f"{launches} launches graph-replayed"}
 
 
+def forced_prefill(name, stages, torch, W, synthetic, launches=40):
+    """Graph-replayed per-launch time of one workload on the prefill route
+    with the K stages per split forced (w4a16_gemm_planned; the library's
+    workspace of the capturing stream is made by one uncaptured call first)."""
+    w = synthetic.WORKLOADS[name]
+    L = Launch(w, torch, W, synthetic, rotate=True)
+    dt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
+    pl = W.plan(w.M, w.K, w.N, w.group_size, w.has_zp, dt, route=W.ROUTE_PREFILL,
+                steps_per_wave=stages)
+    run = lambda i: W.gemm(L.a, *L.sets[i % len(L.sets)][:2], L.sets[i % len(L.sets)][2],
+                           w.group_size, 8, out=L.out, plan=pl)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(launches):
+                run(i)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return {"workload": name, "stages_per_split": pl.steps_per_wave, "splits": pl.splits,
+            "workgroups": pl.grid, "us_per_launch": round(t0.elapsed_time(t1) * 1e3 / launches, 2)}
+
+
+def issue_probe(torch, iters=4000):
+    """Shader-clock cycles per loop trip of probe_issue_kernel: eight MFMA
+    chains with NV FMAs after each MFMA, or 64 FMAs alone; 256 workgroups
+    with 100 KB of LDS (one per CU: one wavefront per SIMD) or 512 with 60 KB
+    (two per SIMD). Reports cycles per issued instruction of one wavefront
+    (the loop's instruction count is read from the build's own assembly and
+    given in the output's note)."""
+    import ctypes
+    probe = ctypes.CDLL(os.path.join(ROOT, "weight_only_int4_unpack_amd", "libw4a16_probe.so"))
+    probe.w4a16_probe_issue.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 3
+    out = torch.empty(512 * 256, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(1, dtype=torch.int64, device="cuda")
+    res = []
+    for per_simd, blocks, lds in ((1, 256, 100 * 1024), (2, 512, 60 * 1024)):
+        for nv in (0, 8, 16, 32, -1):
+            for _ in range(5):
+                st = probe.w4a16_probe_issue(nv, blocks, lds, iters, out.data_ptr(), clk.data_ptr(),
+                                             torch.cuda.current_stream().cuda_stream)
+                assert st == 0, st
+            torch.cuda.synchronize()
+            cyc = clk.item() / iters
+            res.append({"wavefronts_per_simd": per_simd,
+                        "loop": "64 FMAs" if nv < 0 else f"8 MFMAs + {nv} FMAs each",
+                        "cycles_per_trip": round(cyc, 1)})
+    return res
+
+
 def load_traffic(path, name, src_hash):
     """HBM bytes per launch of this workload, from rocprofv3 FETCH_SIZE and
     WRITE_SIZE passes (scaled by a plain-copy calibration), or None when the
@@ -350,6 +417,15 @@ def main():
     rotate = not args.warm
     if args.read_probe:
         print(json.dumps({"read_probe": context_read(torch, args.read_probe)}), flush=True)
+        return
+    if args.issue_probe:
+        for r in issue_probe(torch):
+            print(json.dumps({"issue_probe": r}), flush=True)
+        return
+    if args.prefill_stages:
+        for st in (int(x) for x in args.prefill_stages.split(",")):
+            print(json.dumps({"forced_prefill": forced_prefill(args.workload, st, torch, W,
+                                                               synthetic)}), flush=True)
         return
 
     if args.copy_probe:
