@@ -18,6 +18,7 @@ hipError_t launch_prefill(const PrefillParams&, int, bool, int, hipStream_t) {
 hipError_t launch_prefill_reduce(const PrefillReduceParams&, int, hipStream_t) {
   return hipErrorNoDevice;
 }
+hipError_t launch_asum(const AsumParams&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_kpacked(const KPackedParams&, int, bool, bool, bool, hipStream_t) {
   return hipErrorNoDevice;
 }

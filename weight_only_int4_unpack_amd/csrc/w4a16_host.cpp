@@ -209,26 +209,26 @@ w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dty
 // K, so that fewer MFMA rows are padding and more workgroups fit a CU
 // (K = N = 4096: M = 16 12.2 vs 13.1 us, M = 64 17.7 vs 20.0 us with 32-row
 // tiles; a 2048-row prefill is faster with 64).
-w4a16_status plan_prefill_bm(int64_t M, int64_t K, int64_t N, int32_t G, int num_cus,
+w4a16_status plan_prefill_bm(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype, int num_cus,
                              int32_t ks_forced, int64_t BM, w4a16_plan_t* pl);
 
-w4a16_status plan_prefill(int64_t M, int64_t K, int64_t N, int32_t G, int num_cus,
+w4a16_status plan_prefill(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype, int num_cus,
                           int32_t ks_forced, w4a16_plan_t* pl) {
   using namespace w4a16;
   const int64_t small = M <= 64 ? 32 : kPrefillBM;
   if (small < kPrefillBM && K % kPrefillBK == 0) {
     w4a16_plan_t q{};
-    w4a16_status st = plan_prefill_bm(M, K, N, G, num_cus, ks_forced, small, &q);
+    w4a16_status st = plan_prefill_bm(M, K, N, G, dtype, num_cus, ks_forced, small, &q);
     if (st != W4A16_OK) return st;
     if (q.splits > 1) {
       *pl = q;
       return W4A16_OK;
     }
   }
-  return plan_prefill_bm(M, K, N, G, num_cus, ks_forced, kPrefillBM, pl);
+  return plan_prefill_bm(M, K, N, G, dtype, num_cus, ks_forced, kPrefillBM, pl);
 }
 
-w4a16_status plan_prefill_bm(int64_t M, int64_t K, int64_t N, int32_t G, int num_cus,
+w4a16_status plan_prefill_bm(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype, int num_cus,
                              int32_t ks_forced, int64_t BM, w4a16_plan_t* pl) {
   using namespace w4a16;
   const int64_t tm = ceil_div(M, BM), tn = ceil_div(N, kPrefillBN);
@@ -266,8 +266,13 @@ w4a16_status plan_prefill_bm(int64_t M, int64_t K, int64_t N, int32_t G, int num
   pl->steps_per_wave = (int32_t)ks;
   pl->grid = (int32_t)(per_xcd * kXcds);
   pl->threads = kPrefillThreads;
-  pl->lds_bytes = prefill_lds_bytes((int)BM);
-  pl->workspace_bytes = S > 1 ? (int64_t)(kCounterBytes + S * M * N * 4) : 0;
+  pl->lds_bytes = prefill_ring_ok(K, N, G, BM) ? kRingBytes : prefill_lds_bytes((int)BM);
+  // K splits: counter region, then the fp32 partials; bf16 through the ring
+  // without splits: counter region, then the precomputed activation sums
+  pl->workspace_bytes = S > 1 ? (int64_t)(kCounterBytes + S * M * N * 4)
+                        : prefill_asum_pre(K, N, G, dtype, BM, S)
+                            ? (int64_t)(kCounterBytes + prefill_asum_bytes(M, K, G))
+                            : 0;
   return W4A16_OK;
 }
 
@@ -300,7 +305,7 @@ w4a16_status make_plan(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype
     st = plan_decode(M, K, N, G, dtype, num_cus, L, mode, pl);
     if (st != W4A16_OK) return st;
   } else if (route == W4A16_ROUTE_PREFILL) {
-    st = plan_prefill(M, K, N, G, num_cus, L, pl);
+    st = plan_prefill(M, K, N, G, dtype, num_cus, L, pl);
     if (st != W4A16_OK) return st;
   } else {
     return fail(W4A16_ERR_PLAN, "unknown route %d", (int)route);
@@ -457,6 +462,21 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, void* ws, hip
     p.zp_bias = g.zp_bias;
     p.g_shift = g.G == 32 ? 5 : g.G == 64 ? 6 : g.G == 128 ? 7 : 0;
     p.bm = pl.block_m;
+    p.ring = prefill_ring_ok(g.K, g.N, g.G, pl.block_m) ? 1 : 0;
+    if (prefill_asum_pre(g.K, g.N, g.G, g.dtype, pl.block_m, pl.splits)) {
+      AsumParams ap{};
+      ap.a = (const uint16_t*)g.a;
+      ap.out = (float*)((char*)ws + kCounterBytes);
+      ap.M = (int32_t)g.M;
+      ap.K = (int32_t)g.K;
+      ap.G = g.G;
+      ap.rows = (int32_t)prefill_asum_rows(g.M);
+      e = launch_asum(ap, stream);
+      if (e != hipSuccess)
+        return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+      p.asum = ap.out;
+      p.asum_rows = ap.rows;
+    }
     p.tiles_m = (int32_t)ceil_div(g.M, pl.block_m);
     p.tiles_n = (int32_t)ceil_div(g.N, kPrefillBN);
     p.tiles = p.tiles_m * p.tiles_n;

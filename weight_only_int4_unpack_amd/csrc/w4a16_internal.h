@@ -54,6 +54,40 @@ inline int decode_lds_bytes(int M, int ng_max) {
 inline int prefill_lds_bytes(int bm) {
   return 2 * bm * kPrefillLdsRowHalves * 2;
 }
+// Prefill through an LDS ring: every operand of a 64-row K stage (activation
+// tile, packed weight tile, the group's scales and zero points) is copied by
+// the load units straight into one of kRingSlots LDS slots, kRingSlots - 1
+// stages ahead of the stage being multiplied, without passing through
+// registers. Taken for 64-row tiles when K % 64 == 0, G != 32 and N % 32 == 0
+// (every 16-byte weight piece of a tile row then lies inside the row).
+constexpr int kRingSlots = 4;
+constexpr int kRingTileBytes = 64 * kPrefillBK * 2;  // 64 rows x 64 halves; also 64 K rows x 256 nibbles
+// per wavefront, its 64 columns' scales (128 B) and zero-point words (32 B),
+// in a 256-byte block
+constexpr int kRingAuxOff = 2 * kRingTileBytes;
+constexpr int kRingAuxBytes = 256;
+constexpr int kRingSumOff = 160;  // within a block: 16 precomputed activation sums (bf16, no K split)
+constexpr int kRingSlotBytes = kRingAuxOff + 4 * kRingAuxBytes;
+constexpr int kRingBytes = kRingSlots * kRingSlotBytes;
+static_assert(kRingSlotBytes % 16 == 0, "16-byte aligned slots");
+static_assert(2 * kRingBytes <= kLdsPerCu, "two ring workgroups per CU");
+inline bool prefill_ring_ok(int64_t K, int64_t N, int32_t G, int64_t bm) {
+  return bm == kPrefillBM && K % kPrefillBK == 0 && G != 32 && N % 32 == 0 && N <= (1 << 26);
+}
+// bf16 through the ring without K splits: the activation sums of every
+// (group, row), which the factored numerics need at each group's fold, come
+// from a pass over A before the GEMM (asum_kernel: the same MFMA chain
+// against a ones operand that the GEMM would run per wavefront, so the
+// values are bit-identical) instead of four times per tile inside the GEMM.
+// They sit in the workspace after the counter region, [K/G][rows padded to
+// 64] fp32, and reach the GEMM through the ring's per-wavefront blocks.
+inline int64_t prefill_asum_rows(int64_t M) { return (M + kPrefillBM - 1) / kPrefillBM * kPrefillBM; }
+inline bool prefill_asum_pre(int64_t K, int64_t N, int32_t G, int32_t dtype, int64_t bm, int64_t S) {
+  return dtype == W4A16_BF16 && S == 1 && prefill_ring_ok(K, N, G, bm);
+}
+inline int64_t prefill_asum_bytes(int64_t M, int64_t K, int32_t G) {
+  return (K / G) * prefill_asum_rows(M) * (int64_t)sizeof(float);
+}
 
 // Constants of the nibble-to-float step, passed as kernel arguments so that
 // the compiler keeps them in registers (see the kernels' dequantisation).
@@ -108,6 +142,9 @@ struct PrefillParams {
   uint16_t* out;
   int32_t M, K, N, G, zp_bias;
   int32_t bm;         // rows per workgroup tile: 64, or 32 (K splits only)
+  int32_t ring;       // 1: operands staged through the LDS ring (prefill_ring_ok holds)
+  const float* asum;  // precomputed activation sums [K/G][asum_rows] (prefill_asum_pre), else null
+  int32_t asum_rows;
   int32_t g_shift;    // log2(G) when G is 32, 64 or 128 (unused when G == K)
   int32_t tiles_m, tiles_n, tiles, per_xcd;
   int32_t band;       // tile rows per band of the workgroup -> tile order
@@ -120,6 +157,12 @@ struct PrefillReduceParams {
   const uint16_t* bias;  // nullable [N]
   uint16_t* out;      // [M][N]
   int32_t M, N, S;
+};
+
+struct AsumParams {
+  const uint16_t* a;  // [M, K] bf16
+  float* out;         // [K/G][rows] fp32, rows = prefill_asum_rows(M)
+  int32_t M, K, G, rows;
 };
 
 struct DequantParams {
@@ -164,6 +207,7 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, bool has_zp, int mode
                          int grid, int lds_bytes, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int dtype, bool has_zp, int grid, hipStream_t stream);
 hipError_t launch_prefill_reduce(const PrefillReduceParams& p, int dtype, hipStream_t stream);
+hipError_t launch_asum(const AsumParams& p, hipStream_t stream);
 // stage: the activation rows go to LDS (the host checked that
 // kpacked_lds_bytes + kKpRedBytes fits the device's per-workgroup LDS)
 hipError_t launch_kpacked(const KPackedParams& p, int dtype, bool has_zp, bool fold, bool stage,

@@ -693,6 +693,48 @@ __device__ __forceinline__ V ldg(const char* base, uint32_t off) {
   return *(const V*)(base + off);
 }
 
+// Global -> LDS copies of the prefill ring (gfx950 global_load_lds): lane i
+// reads `size` bytes at sbase + voff and the load unit writes them to LDS
+// byte address lds + i * size; no register receives data. They are issued
+// here rather than through the compiler's builtin because the compiler,
+// seeing the ring's slots as one array, would wait for every copy in flight
+// (vmcnt(0)) before each read of any slot, and the ring exists to keep the
+// copies of later stages in flight meanwhile. The kernel therefore waits for
+// them itself (ring_wait) and contains no other vector-memory loads while a
+// copy can be in flight. m0 is set inside the statement (the one nop covers
+// the m0 write -> LDS-copy hazard).
+typedef __attribute__((address_space(3))) unsigned char lds_byte;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_byte*)p;
+}
+// The base address in scalar registers (its value is wave-uniform).
+__device__ __forceinline__ const void* scalar_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(scalar_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+// 4 bytes per lane from the lane's own address
+__device__ __forceinline__ void copy4_to_lds_lane(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+// Wait until at most N of this wavefront's vector-memory operations are in
+// flight (they complete in issue order); also a compiler barrier for memory.
+template <int N>
+__device__ __forceinline__ void ring_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Prefill: workgroup tile 64 x 256, K staged 64 rows (two 32-row slabs) at a
 // time. The A tile goes through LDS (double-buffered) and is read by all 4
@@ -729,14 +771,17 @@ __device__ __forceinline__ V ldg(const char* base, uint32_t off) {
 // the 2048-row prefill takes 506 us with 32-row tiles against 426 us, each
 // weight being dequantised twice as often). 16-row tiles were slower than 32
 // at M = 16 (14.3 us; with four workgroups per CU they spilled to scratch).
-template <typename T, bool HAS_ZP, int GS, int KM, bool SPLIT, int BM>
+template <typename T, bool HAS_ZP, int GS, int KM, bool SPLIT, int BM, bool RING>
 __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_kernel(
     PrefillParams p) {
   static_assert(BM == 32 || BM == 64, "tile rows");
+  static_assert(!RING || (BM == 64 && KM == 0 && GS != 1), "ring: 64-row tiles, full stages, G != 32");
   constexpr int RH = kPrefillLdsRowHalves;
   constexpr int MB = BM / 16;
   constexpr int AP = BM / 32;  // 16-byte A pieces per thread per stage
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * RH];
+  constexpr int kLds = RING ? kRingBytes : 2 * BM * RH * 2;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
+  auto As = reinterpret_cast<uint16_t(*)[BM * RH]>(smem);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -770,6 +815,8 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
   // base + q.
   constexpr bool kTile = T::kIsF16 && (GS == 1 || GS == 2) && !SPLIT;
   constexpr bool kIntOp = T::kIsF16 && !kTile;
+  // bf16 ring without K splits: activation sums precomputed (p.asum)
+  constexpr bool kPreSum = RING && !SPLIT && !T::kIsF16;
 
   f32x4 acc[MB][4];   // output accumulator
   f32x4 part[MB][4];  // current group's sum of a (base + q)   (GS > 0)
@@ -794,6 +841,68 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
   const uint32_t s_off = (uint32_t)(ncolc * 2);
   const uint32_t z_off = (uint32_t)((ncolc >> 2) * 2);
   const int KF = p.K / kPrefillBK;  // full stages
+
+  // ---- LDS ring (RING). A slot holds one stage: the activation tile (64
+  // rows x 128 B), the weight tile (64 K rows x 128 B: 256 columns of
+  // nibbles), and per wavefront a 256-byte block with the scales (128 B)
+  // and packed zero-point words (32 B) of its 64 columns in the stage's
+  // group. Tiles are stored in 1 KB blocks of 8 rows; within a row the
+  // 16-byte pieces are permuted (XOR) so that the operand reads meet
+  // distinct LDS banks: activation row r keeps piece j at j ^ (r & 7) (the
+  // 16 rows one MFMA operand read spans hit 8 distinct pieces per 8 lanes);
+  // weight row k keeps piece j at j ^ 2((k >> 3) & 3) (the 4 rows one
+  // 16-bit read spans, 8 apart, hit 4 distinct piece pairs). Each wavefront
+  // copies blocks 2w and 2w + 1 of both tiles and its own scale/zero block:
+  // five copies per stage.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t a_dma[2] = {0u, 0u}, b_dma[2] = {0u, 0u};
+  uint32_t a_rd[2] = {0u, 0u}, b_rd = 0u, s_rd = 0u, z_rd = 0u, ring_lds = 0u;
+  const char* aux_src = nullptr;  // per lane: the scale pair / zero word of group 0
+  uint32_t aux_step = 0u;         // bytes between groups
+  if constexpr (RING) {
+    ring_lds = lds_addr(smem);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int blk = 2 * wv + j;
+      const int row = 8 * blk + (lane >> 3);
+      const int ap = (lane & 7) ^ (row & 7);
+      a_dma[j] = (uint32_t)((min(m0 + row, p.M - 1) - m0) * p.K * 2 + ap * 16);
+      const int bp = (lane & 7) ^ (2 * (blk & 3));
+      const int cc = min(tn * 8 + bp, p.N / 32 - 1) - tn * 8;  // pieces past N: clamped, never stored
+      b_dma[j] = (uint32_t)(row * (p.N / 2) + cc * 16);
+    }
+    // lanes 0..31: scale pairs of the wavefront's 64 columns; 32..39: their
+    // 8 zero-point words; 40..55 (kPreSum): the activation sums of tile rows
+    // 16w .. 16w + 15; the rest repeat lane 0's pair into the block's pad
+    const int col0 = tn * kPrefillBN + wv * 64;
+    if (HAS_ZP && lane >= 32 && lane < 40) {
+      aux_src = (const char*)p.qz + (int64_t)min(col0 / 8 + lane - 32, p.N / 8 - 1) * 4;
+      aux_step = (uint32_t)(p.N / 2);
+    } else if (kPreSum && lane >= 40 && lane < 56) {
+      aux_src = (const char*)(p.asum + m0 + 16 * wv + (lane - 40));
+      aux_step = (uint32_t)(p.asum_rows * 4);
+    } else {
+      aux_src = (const char*)p.sc + (int64_t)min(col0 + 2 * (lane < 32 ? lane : 0), p.N - 2) * 2;
+      aux_step = (uint32_t)(p.N * 2);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) a_rd[ks] = (uint32_t)(c * 128 + (((ks * 4 + g) ^ (c & 7)) * 16));
+    b_rd = (uint32_t)(kRingTileBytes + 8 * g * 128 + (((2 * wave + (c >> 3)) ^ (2 * g)) * 16) + (c & 7) * 2);
+    s_rd = (uint32_t)(kRingAuxOff + wave * kRingAuxBytes + 8 * c);
+    z_rd = (uint32_t)(kRingAuxOff + wave * kRingAuxBytes + 128 + 2 * c);
+  }
+  // the five copies of stage kt into slot kt % kRingSlots
+  auto ring_issue = [&](int kt) {
+    const uint32_t slot = ring_lds + (uint32_t)((kt & (kRingSlots - 1)) * kRingSlotBytes);
+    const char* ab = (const char*)p.a + ((int64_t)m0 * p.K + (int64_t)kt * kPrefillBK) * 2;
+    copy16_to_lds(ab, a_dma[0], slot + 2 * wv * 1024);
+    copy16_to_lds(ab, a_dma[1], slot + (2 * wv + 1) * 1024);
+    const char* bb = (const char*)p.bq + (int64_t)kt * kPrefillBK * (p.N / 2) + tn * (kPrefillBN / 2);
+    copy16_to_lds(bb, b_dma[0], slot + kRingTileBytes + 2 * wv * 1024);
+    copy16_to_lds(bb, b_dma[1], slot + kRingTileBytes + (2 * wv + 1) * 1024);
+    const int grp = GS == 0 ? 0 : ((kt * kPrefillBK) >> p.g_shift);
+    copy4_to_lds_lane(aux_src + (uint64_t)grp * aux_step, slot + kRingAuxOff + wv * kRingAuxBytes);
+  };
 
   auto load_a = [&](int kt, u32x4 (&ar)[AP]) {
     if (KM == 0 || kt < KF) {
@@ -905,6 +1014,34 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
         dst[e][v] = GS > 0 ? __builtin_fmaf(sc[e], d, dst[e][v]) : sc[e] * d;
       }
   };
+  // Activation operand of row block i, 32-row half ks: from LDS buffer `buf`,
+  // or (RING) from the slot at byte offset `buf`.
+  auto aop_at = [&](uint32_t buf, int ks, int i) -> u32x4 {
+    if constexpr (RING)
+      return *(const u32x4*)(smem + buf + a_rd[ks] + i * 16 * kPrefillBK * 2);
+    else
+      return *(const u32x4*)&As[buf][(i * 16 + c) * RH + ks * 32 + 8 * g];
+  };
+  // A slab's weights, scales and zero points from the ring slot at byte
+  // offset `so` (RING): rows 2r and 2r + 1 of the lane's 8 in one register.
+  auto ring_slab = [&](uint32_t so, int ks, Slab& sl, auto posc) {
+    constexpr int POS = decltype(posc)::value;
+    constexpr bool closes = GS > 0 && (POS + 1) % (GS > 0 ? GS : 1) == 0;
+    const unsigned char* bp = smem + so + b_rd + ks * 32 * 128;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      sl.q[r] = u16x2{*(const uint16_t*)(bp + (2 * r) * 128), *(const uint16_t*)(bp + (2 * r + 1) * 128)};
+    if constexpr (closes || kTile) {
+      sl.s = *(const u32x2*)(smem + so + s_rd);
+      sl.valid = true;
+    }
+    if constexpr (HAS_ZP && (closes || kIntOp || kTile)) sl.z = *(const uint16_t*)(smem + so + z_rd);
+    if constexpr (kPreSum && closes) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+        asum[i] = *(const f32x4*)(smem + so + kRingAuxOff + i * kRingAuxBytes + kRingSumOff + 16 * g);
+    }
+  };
   // The MFMAs of one slab (LDS buffer `buf`, 32-row half `ks`). With one
   // slab per group (GS = 1) each row block is folded right after its MFMAs,
   // so only one row block's partials are live.
@@ -926,7 +1063,7 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
       bop[3] = tile_op<3>(Y, mag, nib(z4, 3), sl.s.y >> 16);
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
-        const u32x4 aop = *(const u32x4*)&As[buf][(i * 16 + c) * RH + ks * 32 + 8 * g];
+        const u32x4 aop = aop_at(buf, ks, i);
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[i][e] = mfma<T>(aop, bop[e], acc[i][e]);
       }
@@ -947,7 +1084,7 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
     if constexpr (closes) col_consts(sl.s, HAS_ZP ? sl.z : 0u, sl.valid, sc, bias);
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
-      const u32x4 aop = *(const u32x4*)&As[buf][(i * 16 + c) * RH + ks * 32 + 8 * g];
+      const u32x4 aop = aop_at(buf, ks, i);
       if constexpr (GS == 1) {
         const f32x4 as = kIntOp ? zero4 : mfma<T>(aop, ones, zero4);
         f32x4 pt[4];
@@ -955,7 +1092,7 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
         for (int e = 0; e < 4; ++e) pt[e] = mfma<T>(aop, bop[e], zero4);
         fold_block(sc, bias, as, pt, acc[i]);
       } else {
-        if constexpr (!kIntOp) asum[i] = mfma<T>(aop, ones, opens ? zero4 : asum[i]);
+        if constexpr (!kIntOp && !kPreSum) asum[i] = mfma<T>(aop, ones, opens ? zero4 : asum[i]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if constexpr (GS > 0)
@@ -993,28 +1130,82 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
   using Yes = std::true_type;
   using No = std::false_type;
 
-  Slab B0[2], B1[2];
-  load_a(kt_beg, a_next);
-  load_slab(kt_beg, 0, B0[0], C0{});
-  load_slab(kt_beg, 1, B0[1], C1{});
-  store_a(kt_beg & 1, a_next);
-  __syncthreads();
-  // kt_beg is even whenever a group spans two stages, so P = 0 opens groups
-  int kt = kt_beg;
-  for (; kt + 2 < kt_end; kt += 2) {
-    stage(kt, B0, B1, C0{}, Yes{});
-    stage(kt + 1, B1, B0, C1{}, Yes{});
-  }
-  if (kt + 2 == kt_end) {
-    stage(kt, B0, B1, C0{}, Yes{});
-    stage(kt + 1, B1, B0, C1{}, No{});
+  if constexpr (RING) {
+    // Stage kt (LATER: stages already issued after kt, 0..2; ISSUE: stage
+    // kt + 3 exists): wait for this wavefront's copies of stage kt, then the
+    // barrier (every wavefront's copies of kt have landed, and every
+    // wavefront is done with stage kt - 1, whose slot the copies of stage
+    // kt + 3 then reuse), then multiply stage kt out of its slot.
+    auto rstage = [&](int kt, auto pc, auto laterc, auto issuec) {
+      constexpr int P = decltype(pc)::value;
+      constexpr int LATER = decltype(laterc)::value;
+      static_assert(kRingSlots == 4, "three stages in flight");
+      if constexpr (LATER >= 0) {
+        ring_wait<5 * LATER>();
+      } else {  // the last stages: LATER = kt_end - 1 - kt
+        const int later = kt_end - 1 - kt;
+        if (later >= 2) ring_wait<10>(); else if (later == 1) ring_wait<5>(); else ring_wait<0>();
+      }
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (decltype(issuec)::value) ring_issue(kt + kRingSlots - 1);
+      const uint32_t so = (uint32_t)((kt & (kRingSlots - 1)) * kRingSlotBytes);
+      Slab sl;
+      ring_slab(so, 0, sl, std::integral_constant<int, 2 * P>{});
+      slab(so, 0, sl, std::integral_constant<int, 2 * P>{});
+      ring_slab(so, 1, sl, std::integral_constant<int, 2 * P + 1>{});
+      slab(so, 1, sl, std::integral_constant<int, 2 * P + 1>{});
+    };
+    using L2 = std::integral_constant<int, 2>;
+    using Lr = std::integral_constant<int, -1>;
+#pragma unroll
+    for (int s = 0; s < kRingSlots - 1; ++s)
+      if (kt_beg + s < kt_end) ring_issue(kt_beg + s);
+    // kt_beg is even whenever a group spans two stages, so P = 0 opens groups
+    int kt = kt_beg;
+    for (; kt + 4 < kt_end; kt += 2) {
+      rstage(kt, C0{}, L2{}, Yes{});
+      rstage(kt + 1, C1{}, L2{}, Yes{});
+    }
+    // the last 1..4 stages; at most one more to issue (stage kt + 3, when
+    // four remain)
+    if (kt + 3 < kt_end) {
+      rstage(kt, C0{}, L2{}, Yes{});
+      rstage(kt + 1, C1{}, Lr{}, No{});
+      kt += 2;
+    }
+    for (; kt < kt_end; kt += 2) {
+      rstage(kt, C0{}, Lr{}, No{});
+      if (kt + 1 < kt_end) rstage(kt + 1, C1{}, Lr{}, No{});
+    }
   } else {
-    stage(kt, B0, B1, C0{}, No{});
+    Slab B0[2], B1[2];
+    load_a(kt_beg, a_next);
+    load_slab(kt_beg, 0, B0[0], C0{});
+    load_slab(kt_beg, 1, B0[1], C1{});
+    store_a(kt_beg & 1, a_next);
+    __syncthreads();
+    // kt_beg is even whenever a group spans two stages, so P = 0 opens groups
+    int kt = kt_beg;
+    for (; kt + 2 < kt_end; kt += 2) {
+      stage(kt, B0, B1, C0{}, Yes{});
+      stage(kt + 1, B1, B0, C1{}, Yes{});
+    }
+    if (kt + 2 == kt_end) {
+      stage(kt, B0, B1, C0{}, Yes{});
+      stage(kt + 1, B1, B0, C1{}, No{});
+    } else {
+      stage(kt, B0, B1, C0{}, No{});
+    }
   }
 
   // ---- epilogue: lane holds rows i*16 + 4g + v, columns ncol + e
   const bool col_ok = ncol < p.N;
   if constexpr (GS == 0) {  // one group: fold this split's sums (the fold is linear)
+    if constexpr (kPreSum) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) asum[i] = *(const f32x4*)(p.asum + m0 + 16 * i + 4 * g);
+    }
     const u32x2 sv = *(const u32x2*)(p.sc + ncolc);
     const uint32_t z4 = HAS_ZP ? ((const uint16_t*)p.qz)[ncolc >> 2] : 0u;
     float sc[4], bias[4];
@@ -1056,6 +1247,25 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
         *(f32x4*)d = f32x4{acc[i][0][v], acc[i][1][v], acc[i][2][v], acc[i][3][v]};
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Activation sums for the bf16 ring prefill: out[g][r] = sum over group g's
+// rows k of a[r][k], computed exactly as the prefill's wavefronts would (the
+// MFMA against a ones operand, one 32-row slab after another, from zero), so
+// that the folds see the same fp32 values. Workgroup = 64 rows x one group;
+// wavefront w takes rows 16w .. 16w + 15. Rows past M repeat row M - 1.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void asum_kernel(AsumParams p) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, c = lane & 15;
+  const int r0 = blockIdx.x * kPrefillBM + 16 * wave;
+  const int grp = blockIdx.y;
+  const uint16_t* arow = p.a + (int64_t)min(r0 + c, p.M - 1) * p.K + (int64_t)grp * p.G + 8 * g;
+  const u32x4 ones = u32x4{BF16::kOnePair, BF16::kOnePair, BF16::kOnePair, BF16::kOnePair};
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < p.G / 32; ++s) acc = mfma<BF16>(*(const u32x4*)(arow + 32 * s), ones, acc);
+  if (c == 0) *(f32x4*)(p.out + (int64_t)grp * p.rows + r0 + 4 * g) = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -1413,18 +1623,29 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, bool has_zp, int mode
 template <typename T, bool Z, int GS, int KM>
 static hipError_t prefill_go(const PrefillParams& p, int grid, hipStream_t st) {
   const dim3 g(grid), b(kPrefillThreads);
+  if constexpr (KM == 0 && GS != 1) {
+    if (p.ring) {
+      if (p.bm != 64) return hipErrorInvalidValue;
+      if (p.S > 1)
+        hipLaunchKernelGGL((prefill_kernel<T, Z, GS, KM, true, 64, true>), g, b, 0, st, p);
+      else
+        hipLaunchKernelGGL((prefill_kernel<T, Z, GS, KM, false, 64, true>), g, b, 0, st, p);
+      return hipGetLastError();
+    }
+  }
+  if (p.ring) return hipErrorInvalidValue;
   if (p.S > 1) {
     if constexpr (KM == 0) {
       if (p.bm == 32) {
-        hipLaunchKernelGGL((prefill_kernel<T, Z, GS, KM, true, 32>), g, b, 0, st, p);
+        hipLaunchKernelGGL((prefill_kernel<T, Z, GS, KM, true, 32, false>), g, b, 0, st, p);
         return hipGetLastError();
       }
     }
     if (p.bm != 64) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_kernel<T, Z, GS, KM, true, 64>), g, b, 0, st, p);
+    hipLaunchKernelGGL((prefill_kernel<T, Z, GS, KM, true, 64, false>), g, b, 0, st, p);
   } else {
     if (p.bm != 64) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_kernel<T, Z, GS, KM, false, 64>), g, b, 0, st, p);
+    hipLaunchKernelGGL((prefill_kernel<T, Z, GS, KM, false, 64, false>), g, b, 0, st, p);
   }
   return hipGetLastError();
 }
@@ -1453,6 +1674,10 @@ hipError_t launch_prefill_reduce(const PrefillReduceParams& p, int dtype, hipStr
     hipLaunchKernelGGL((prefill_reduce_kernel<F16>), dim3(grid), dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL((prefill_reduce_kernel<BF16>), dim3(grid), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+hipError_t launch_asum(const AsumParams& p, hipStream_t st) {
+  hipLaunchKernelGGL(asum_kernel, dim3(p.rows / kPrefillBM, p.K / p.G), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 hipError_t launch_prefill(const PrefillParams& p, int dtype, bool has_zp, int grid,
