@@ -471,6 +471,7 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, void* ws, hip
       ap.K = (int32_t)g.K;
       ap.G = g.G;
       ap.rows = (int32_t)prefill_asum_rows(g.M);
+      ap.scale = (g.qzeros == nullptr && g.G != g.K) ? -(128.0f + (float)g.zp_bias) : 1.0f;
       e = launch_asum(ap, stream);
       if (e != hipSuccess)
         return fail(W4A16_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

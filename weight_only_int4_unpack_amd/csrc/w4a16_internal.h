@@ -81,6 +81,8 @@ inline bool prefill_ring_ok(int64_t K, int64_t N, int32_t G, int64_t bm) {
 // values are bit-identical) instead of four times per tile inside the GEMM.
 // They sit in the workspace after the counter region, [K/G][rows padded to
 // 64] fp32, and reach the GEMM through the ring's per-wavefront blocks.
+// Without zero points (and G < K) they are stored times -(128 + zp_bias)
+// and start each group's partial sums.
 inline int64_t prefill_asum_rows(int64_t M) { return (M + kPrefillBM - 1) / kPrefillBM * kPrefillBM; }
 inline bool prefill_asum_pre(int64_t K, int64_t N, int32_t G, int32_t dtype, int64_t bm, int64_t S) {
   return dtype == W4A16_BF16 && S == 1 && prefill_ring_ok(K, N, G, bm);
@@ -163,6 +165,7 @@ struct AsumParams {
   const uint16_t* a;  // [M, K] bf16
   float* out;         // [K/G][rows] fp32, rows = prefill_asum_rows(M)
   int32_t M, K, G, rows;
+  float scale;        // 1, or -(128 + zp_bias) without zero points and G < K
 };
 
 struct DequantParams {

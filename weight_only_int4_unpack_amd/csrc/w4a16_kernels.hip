@@ -815,8 +815,13 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
   // base + q.
   constexpr bool kTile = T::kIsF16 && (GS == 1 || GS == 2) && !SPLIT;
   constexpr bool kIntOp = T::kIsF16 && !kTile;
-  // bf16 ring without K splits: activation sums precomputed (p.asum)
+  // bf16 ring without K splits: activation sums precomputed (p.asum). With
+  // one zero point for every column (b = base + zp_bias) and groups below K,
+  // the pass stores -b * sum a instead, and each group's partials start from
+  // it rather than from zero, so the fold is acc += s * part (one FMA per
+  // output instead of two).
   constexpr bool kPreSum = RING && !SPLIT && !T::kIsF16;
+  constexpr bool kInitSum = kPreSum && !HAS_ZP && GS > 0;
 
   f32x4 acc[MB][4];   // output accumulator
   f32x4 part[MB][4];  // current group's sum of a (base + q)   (GS > 0)
@@ -1010,7 +1015,7 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
     for (int e = 0; e < 4; ++e)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float d = kIntOp ? src[e][v] : __builtin_fmaf(-bias[e], as[v], src[e][v]);
+        const float d = (kIntOp || kInitSum) ? src[e][v] : __builtin_fmaf(-bias[e], as[v], src[e][v]);
         dst[e][v] = GS > 0 ? __builtin_fmaf(sc[e], d, dst[e][v]) : sc[e] * d;
       }
   };
@@ -1036,7 +1041,8 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
       sl.valid = true;
     }
     if constexpr (HAS_ZP && (closes || kIntOp || kTile)) sl.z = *(const uint16_t*)(smem + so + z_rd);
-    if constexpr (kPreSum && closes) {
+    constexpr bool opens = GS > 0 && POS % (GS > 0 ? GS : 1) == 0;
+    if constexpr (kPreSum && (kInitSum ? opens : closes)) {
 #pragma unroll
       for (int i = 0; i < MB; ++i)
         asum[i] = *(const f32x4*)(smem + so + kRingAuxOff + i * kRingAuxBytes + kRingSumOff + 16 * g);
@@ -1096,7 +1102,7 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if constexpr (GS > 0)
-            part[i][e] = mfma<T>(aop, bop[e], opens ? zero4 : part[i][e]);
+            part[i][e] = mfma<T>(aop, bop[e], opens ? (kInitSum ? asum[i] : zero4) : part[i][e]);
           else
             acc[i][e] = mfma<T>(aop, bop[e], acc[i][e]);
         }
@@ -1250,10 +1256,11 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
 }
 
 // ---------------------------------------------------------------------------
-// Activation sums for the bf16 ring prefill: out[g][r] = sum over group g's
-// rows k of a[r][k], computed exactly as the prefill's wavefronts would (the
-// MFMA against a ones operand, one 32-row slab after another, from zero), so
-// that the folds see the same fp32 values. Workgroup = 64 rows x one group;
+// Activation sums for the bf16 ring prefill: out[g][r] = scale * (sum over
+// group g's rows k of a[r][k]), the sum computed exactly as the prefill's
+// wavefronts would (the MFMA against a ones operand, one 32-row slab after
+// another, from zero). scale is 1, or -(base + zp_bias) when every column
+// shares that zero point (one rounding). Workgroup = 64 rows x one group;
 // wavefront w takes rows 16w .. 16w + 15. Rows past M repeat row M - 1.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void asum_kernel(AsumParams p) {
@@ -1265,7 +1272,7 @@ __global__ __launch_bounds__(256) void asum_kernel(AsumParams p) {
   const u32x4 ones = u32x4{BF16::kOnePair, BF16::kOnePair, BF16::kOnePair, BF16::kOnePair};
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < p.G / 32; ++s) acc = mfma<BF16>(*(const u32x4*)(arow + 32 * s), ones, acc);
-  if (c == 0) *(f32x4*)(p.out + (int64_t)grp * p.rows + r0 + 4 * g) = acc;
+  if (c == 0) *(f32x4*)(p.out + (int64_t)grp * p.rows + r0 + 4 * g) = acc * p.scale;
 }
 
 // ---------------------------------------------------------------------------
