@@ -295,23 +295,28 @@ def test_q_equals_z_gives_zero(dtype, zp):
 
 
 def _factored_zero_bound(p, zp):
-    """Bound on |out| when q == z in the factored form. For output (m, n),
-    each group's fold computes s (P - b S) with P = sum a (b + q) and S = sum a
-    accumulated in fp32 over at most G terms (one group: the route's fold
-    never spans two), b + q <= B (bf16: 128 + 15; fp16: 1024 + 15, the even
-    nibble positions being the larger). Standard summation error bounds give
-    |P^ - P| <= g_G sum |a|(b + q) and |S^ - S| <= g_G sum |a|, g_G = G u / (1 - G u),
-    u = 2^-24, so |fold| <= 2 g_G B s sum |a| per group; the fold's own FMA,
-    the sums over groups, wavefronts and splits add roundings relative to
-    these already tiny terms (factor 1.01), and the cast to the output type
-    one ulp of the result (at least the smallest subnormal)."""
+    """Bound on |out| when q == z in the factored forms (exact result 0). For
+    output (m, n) and one group: S^ = fl(sum a) over at most G terms errs by at
+    most g_G A (A = sum |a|, g_n = n u / (1 - n u), u = 2^-24); the operand is
+    b + q = b (b = base + z <= B: bf16 128 + 15, fp16 1024 + 15).
+    Fold form: P^ = fl(sum a b) errs by at most g_G B A, and fl(P^ - b S^)
+    by at most 2 g_G B A (1 + u).
+    Seeded form (bf16 prefill without zero points): the partial starts from
+    C0 = fl(-b S^) (|C0 + b S^| <= u B A (1 + g_G)) and accumulates the G
+    products onto it, G + 1 terms each at most B A (1 + g_G): the result errs
+    by at most 2 g_{G+1} B A (1 + g_G) from C0 + b S = -b (S^ - S) + (C0 + b S^),
+    so |partial| <= (g_G + u + 2 g_{G+1}) B A (1 + g_G).
+    Both are below (3 g_{G+1} + u) B A (1 + g_G); times s, summed over groups,
+    wavefronts and splits (roundings relative to these tiny terms: factor
+    1.01), and one ulp of the output type (at least its smallest subnormal)."""
     a = np.abs(O.to_f32(p.a_bits, p.dtype).astype(np.float64))             # [M, K]
     s = np.abs(O.to_f32(p.s_bits, p.dtype).astype(np.float64))             # [K/G, N]
     s_k = np.repeat(s, p.G, axis=0)                                        # [K, N]
     u = 2.0 ** -24
     g = p.G * u / (1 - p.G * u)
+    g1 = (p.G + 1) * u / (1 - (p.G + 1) * u)
     B = 143.0 if p.dtype == "bf16" else 1039.0
-    bound = 2 * g * B * (a @ s_k) * 1.01                                   # [M, N]
+    bound = (3 * g1 + u) * (1 + g) * B * (a @ s_k) * 1.01                  # [M, N]
     tiny = 2.0 ** -24 if p.dtype == "fp16" else 2.0 ** -133
     return bound * (1 + 2.0 ** -7) + tiny
 

@@ -898,7 +898,7 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
   }
   // the five copies of stage kt into slot kt % kRingSlots
   auto ring_issue = [&](int kt) {
-    const uint32_t slot = ring_lds + (uint32_t)((kt & (kRingSlots - 1)) * kRingSlotBytes);
+    const uint32_t slot = ring_lds + ((uint32_t)kt % kRingSlots) * kRingSlotBytes;
     const char* ab = (const char*)p.a + ((int64_t)m0 * p.K + (int64_t)kt * kPrefillBK) * 2;
     copy16_to_lds(ab, a_dma[0], slot + 2 * wv * 1024);
     copy16_to_lds(ab, a_dma[1], slot + (2 * wv + 1) * 1024);
@@ -1145,38 +1145,38 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
     auto rstage = [&](int kt, auto pc, auto laterc, auto issuec) {
       constexpr int P = decltype(pc)::value;
       constexpr int LATER = decltype(laterc)::value;
-      static_assert(kRingSlots == 4, "three stages in flight");
+      static_assert(kRingSlots == 3 || kRingSlots == 4, "one or two stages in flight");
       if constexpr (LATER >= 0) {
         ring_wait<5 * LATER>();
       } else {  // the last stages: LATER = kt_end - 1 - kt
         const int later = kt_end - 1 - kt;
-        if (later >= 2) ring_wait<10>(); else if (later == 1) ring_wait<5>(); else ring_wait<0>();
+        if (kRingSlots == 4 && later >= 2) ring_wait<10>(); else if (later >= 1) ring_wait<5>(); else ring_wait<0>();
       }
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (decltype(issuec)::value) ring_issue(kt + kRingSlots - 1);
-      const uint32_t so = (uint32_t)((kt & (kRingSlots - 1)) * kRingSlotBytes);
+      const uint32_t so = ((uint32_t)kt % kRingSlots) * kRingSlotBytes;
       Slab sl;
       ring_slab(so, 0, sl, std::integral_constant<int, 2 * P>{});
       slab(so, 0, sl, std::integral_constant<int, 2 * P>{});
       ring_slab(so, 1, sl, std::integral_constant<int, 2 * P + 1>{});
       slab(so, 1, sl, std::integral_constant<int, 2 * P + 1>{});
     };
-    using L2 = std::integral_constant<int, 2>;
+    using Lmax = std::integral_constant<int, kRingSlots - 2>;
     using Lr = std::integral_constant<int, -1>;
 #pragma unroll
     for (int s = 0; s < kRingSlots - 1; ++s)
       if (kt_beg + s < kt_end) ring_issue(kt_beg + s);
     // kt_beg is even whenever a group spans two stages, so P = 0 opens groups
     int kt = kt_beg;
-    for (; kt + 4 < kt_end; kt += 2) {
-      rstage(kt, C0{}, L2{}, Yes{});
-      rstage(kt + 1, C1{}, L2{}, Yes{});
+    for (; kt + kRingSlots < kt_end; kt += 2) {
+      rstage(kt, C0{}, Lmax{}, Yes{});
+      rstage(kt + 1, C1{}, Lmax{}, Yes{});
     }
-    // the last 1..4 stages; at most one more to issue (stage kt + 3, when
-    // four remain)
-    if (kt + 3 < kt_end) {
-      rstage(kt, C0{}, L2{}, Yes{});
+    // the last kRingSlots stages or fewer; at most one more to issue (stage
+    // kt + kRingSlots - 1, when kRingSlots remain)
+    if (kt + kRingSlots - 1 < kt_end) {
+      rstage(kt, C0{}, Lmax{}, Yes{});
       rstage(kt + 1, C1{}, Lr{}, No{});
       kt += 2;
     }
