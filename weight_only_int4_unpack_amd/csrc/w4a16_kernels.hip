@@ -714,17 +714,22 @@ __device__ __forceinline__ const void* scalar_ptr(const void* p) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
+// LDS destination = lds (wave-uniform) + OFF (a compile-time byte offset)
+template <int OFF>
 __device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  static_assert(OFF >= 0 && OFF < (1 << 20), "LDS offset");
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(scalar_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "v"(voff), "s"(scalar_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds)), "n"(OFF)
                : "memory");
 }
 // 4 bytes per lane from the lane's own address
+template <int OFF>
 __device__ __forceinline__ void copy4_to_lds_lane(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+  static_assert(OFF >= 0 && OFF < (1 << 20), "LDS offset");
+  asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :
-               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)), "n"(OFF)
                : "memory");
 }
 // Wait until at most N of this wavefront's vector-memory operations are in
@@ -897,16 +902,19 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
     z_rd = (uint32_t)(kRingAuxOff + wave * kRingAuxBytes + 128 + 2 * c);
   }
   // the five copies of stage kt into slot kt % kRingSlots
-  auto ring_issue = [&](int kt) {
-    const uint32_t slot = ring_lds + ((uint32_t)kt % kRingSlots) * kRingSlotBytes;
+  // (slot SL = (kt - kt_beg) % kRingSlots, a compile-time constant)
+  auto ring_issue = [&](int kt, auto slc) {
+    constexpr int SO = decltype(slc)::value * kRingSlotBytes;
+    const uint32_t wtile = ring_lds + 2 * wv * 1024;               // this wavefront's two tile blocks
+    const uint32_t waux = ring_lds + wv * kRingAuxBytes;           // and its scale/zero block
     const char* ab = (const char*)p.a + ((int64_t)m0 * p.K + (int64_t)kt * kPrefillBK) * 2;
-    copy16_to_lds(ab, a_dma[0], slot + 2 * wv * 1024);
-    copy16_to_lds(ab, a_dma[1], slot + (2 * wv + 1) * 1024);
+    copy16_to_lds<SO>(ab, a_dma[0], wtile);
+    copy16_to_lds<SO + 1024>(ab, a_dma[1], wtile);
     const char* bb = (const char*)p.bq + (int64_t)kt * kPrefillBK * (p.N / 2) + tn * (kPrefillBN / 2);
-    copy16_to_lds(bb, b_dma[0], slot + kRingTileBytes + 2 * wv * 1024);
-    copy16_to_lds(bb, b_dma[1], slot + kRingTileBytes + (2 * wv + 1) * 1024);
+    copy16_to_lds<SO + kRingTileBytes>(bb, b_dma[0], wtile);
+    copy16_to_lds<SO + kRingTileBytes + 1024>(bb, b_dma[1], wtile);
     const int grp = GS == 0 ? 0 : ((kt * kPrefillBK) >> p.g_shift);
-    copy4_to_lds_lane(aux_src + (uint64_t)grp * aux_step, slot + kRingAuxOff + wv * kRingAuxBytes);
+    copy4_to_lds_lane<SO + kRingAuxOff>(aux_src + (uint64_t)grp * aux_step, waux);
   };
 
   auto load_a = [&](int kt, u32x4 (&ar)[AP]) {
@@ -1142,48 +1150,57 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
     // barrier (every wavefront's copies of kt have landed, and every
     // wavefront is done with stage kt - 1, whose slot the copies of stage
     // kt + 3 then reuse), then multiply stage kt out of its slot.
-    auto rstage = [&](int kt, auto pc, auto laterc, auto issuec) {
-      constexpr int P = decltype(pc)::value;
+    // stage kt in slot SL = (kt - kt_beg) % kRingSlots
+    auto rstage = [&](int kt, auto slc, auto laterc, auto issuec) {
+      constexpr int SL = decltype(slc)::value;
+      constexpr int P = SL & 1;  // kt - kt_beg even: P = 0 (opens a two-stage group)
       constexpr int LATER = decltype(laterc)::value;
-      static_assert(kRingSlots == 3 || kRingSlots == 4, "one or two stages in flight");
+      static_assert(kRingSlots == 4, "three stages in flight, slots alternate parity");
       if constexpr (LATER >= 0) {
         ring_wait<5 * LATER>();
       } else {  // the last stages: LATER = kt_end - 1 - kt
         const int later = kt_end - 1 - kt;
-        if (kRingSlots == 4 && later >= 2) ring_wait<10>(); else if (later >= 1) ring_wait<5>(); else ring_wait<0>();
+        if (later >= 2) ring_wait<10>(); else if (later == 1) ring_wait<5>(); else ring_wait<0>();
       }
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (decltype(issuec)::value) ring_issue(kt + kRingSlots - 1);
-      const uint32_t so = ((uint32_t)kt % kRingSlots) * kRingSlotBytes;
+      if constexpr (decltype(issuec)::value)
+        ring_issue(kt + kRingSlots - 1, std::integral_constant<int, (SL + kRingSlots - 1) % kRingSlots>{});
+      constexpr uint32_t so = SL * kRingSlotBytes;
       Slab sl;
       ring_slab(so, 0, sl, std::integral_constant<int, 2 * P>{});
       slab(so, 0, sl, std::integral_constant<int, 2 * P>{});
       ring_slab(so, 1, sl, std::integral_constant<int, 2 * P + 1>{});
       slab(so, 1, sl, std::integral_constant<int, 2 * P + 1>{});
     };
-    using Lmax = std::integral_constant<int, kRingSlots - 2>;
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    using L2 = std::integral_constant<int, 2>;
     using Lr = std::integral_constant<int, -1>;
-#pragma unroll
-    for (int s = 0; s < kRingSlots - 1; ++s)
-      if (kt_beg + s < kt_end) ring_issue(kt_beg + s);
-    // kt_beg is even whenever a group spans two stages, so P = 0 opens groups
+    if (kt_beg < kt_end) ring_issue(kt_beg, S0{});
+    if (kt_beg + 1 < kt_end) ring_issue(kt_beg + 1, S1{});
+    if (kt_beg + 2 < kt_end) ring_issue(kt_beg + 2, S2{});
+    // kt_beg is even whenever a group spans two stages, so even slots open groups.
+    // Four stages per trip while every one of them still issues a later stage.
     int kt = kt_beg;
-    for (; kt + kRingSlots < kt_end; kt += 2) {
-      rstage(kt, C0{}, Lmax{}, Yes{});
-      rstage(kt + 1, C1{}, Lmax{}, Yes{});
+    for (; kt + 6 < kt_end; kt += 4) {
+      rstage(kt, S0{}, L2{}, Yes{});
+      rstage(kt + 1, S1{}, L2{}, Yes{});
+      rstage(kt + 2, S2{}, L2{}, Yes{});
+      rstage(kt + 3, S3{}, L2{}, Yes{});
     }
-    // the last kRingSlots stages or fewer; at most one more to issue (stage
-    // kt + kRingSlots - 1, when kRingSlots remain)
-    if (kt + kRingSlots - 1 < kt_end) {
-      rstage(kt, C0{}, Lmax{}, Yes{});
-      rstage(kt + 1, C1{}, Lr{}, No{});
-      kt += 2;
-    }
-    for (; kt < kt_end; kt += 2) {
-      rstage(kt, C0{}, Lr{}, No{});
-      if (kt + 1 < kt_end) rstage(kt + 1, C1{}, Lr{}, No{});
-    }
+    // the last 1..6 stages (kt - kt_beg is a multiple of 4: slots start at 0)
+    if (kt < kt_end) rstage(kt, S0{}, Lr{}, std::false_type{});
+    if (kt + 3 < kt_end) ring_issue(kt + 3, S3{});
+    if (kt + 1 < kt_end) rstage(kt + 1, S1{}, Lr{}, std::false_type{});
+    if (kt + 4 < kt_end) ring_issue(kt + 4, S0{});
+    if (kt + 2 < kt_end) rstage(kt + 2, S2{}, Lr{}, std::false_type{});
+    if (kt + 5 < kt_end) ring_issue(kt + 5, S1{});
+    if (kt + 3 < kt_end) rstage(kt + 3, S3{}, Lr{}, std::false_type{});
+    if (kt + 4 < kt_end) rstage(kt + 4, S0{}, Lr{}, std::false_type{});
+    if (kt + 5 < kt_end) rstage(kt + 5, S1{}, Lr{}, std::false_type{});
   } else {
     Slab B0[2], B1[2];
     load_a(kt_beg, a_next);
