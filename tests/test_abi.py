@@ -244,13 +244,16 @@ def test_selector_prefill_tiles():
     p = W.plan(2048, 5120, 17408, 128, False, torch.bfloat16)
     assert (p.block_m, p.block_n, p.block_k) == (64, 256, 64)
     assert p.grid % 8 == 0 and p.grid >= 32 * 68
-    # K % 64 == 0, G != 32, N % 32 == 0: the operands go through the LDS ring,
-    # 4 slots of two 8 KB tiles and four 256-byte scale/zero-point blocks
+    # K % 64 == 0, N % 32 == 0: the operands go through the LDS ring, 4 slots of
+    # two 8 KB tiles and four per-wavefront blocks of scales, zero points and
+    # activation sums (256 bytes; 512 for groups of 32, two per stage)
     assert p.lds_bytes == 4 * (2 * 64 * 64 * 2 + 4 * 256)
     assert p.splits == 1                       # 2176 tiles: no K split
-    # groups of 32 (or K % 64 != 0): the double-buffered activation tile
-    assert W.plan(2048, 5120, 17408, 32, False, torch.bfloat16).lds_bytes == 2 * 64 * 80 * 2
+    assert W.plan(2048, 5120, 17408, 32, False, torch.bfloat16).lds_bytes == \
+        4 * (2 * 64 * 64 * 2 + 4 * 512)
+    # K % 64 != 0 (or N % 32 != 0): the double-buffered activation tile
     assert W.plan(2048, 5000, 17408, 5000, False, torch.bfloat16).lds_bytes == 2 * 64 * 80 * 2
+    assert W.plan(2048, 5120, 17400, 128, False, torch.bfloat16).lds_bytes == 2 * 64 * 80 * 2
     q = W.plan(100, 4096, 4096, 32, True, torch.float16)
     assert q.grid == 2 * 16 * q.splits and q.splits > 1     # 32 tiles, K split
 
@@ -263,8 +266,9 @@ def test_selector_prefill_splits(M, K, N, G):
     p = W.plan(M, K, N, G, True, torch.bfloat16, route=W.ROUTE_PREFILL)
     # tile rows: 64, or 32 for M <= 64 when K % 64 == 0 and K splits
     assert p.block_m == (64 if K % 64 or M > 64 or p.splits == 1 else 32)
-    ring = p.block_m == 64 and K % 64 == 0 and G != 32 and N % 32 == 0
-    assert p.lds_bytes == (4 * (2 * 64 * 64 * 2 + 4 * 256) if ring else 2 * p.block_m * 80 * 2)
+    ring = p.block_m == 64 and K % 64 == 0 and N % 32 == 0
+    blk = 512 if G == 32 and K != 32 else 256
+    assert p.lds_bytes == (4 * (2 * 64 * 64 * 2 + 4 * blk) if ring else 2 * p.block_m * 80 * 2)
     tiles = -(-M // p.block_m) * -(-N // 256)
     KT = -(-K // 64)
     S, ks = p.splits, p.steps_per_wave
@@ -339,8 +343,10 @@ def test_workspace_bytes_follow_the_plan():
         W.WORKSPACE_COUNTER_BYTES + 40 * 2048 * 4
     assert W.workspace_bytes(300, 5120, 17408, 5120, torch.bfloat16) == \
         W.WORKSPACE_COUNTER_BYTES + 1 * 320 * 4
-    # groups of 32 keep the in-kernel sums
-    assert W.workspace_bytes(2048, 5120, 17408, 32, torch.bfloat16) == 0
+    assert W.workspace_bytes(2048, 5120, 17408, 32, torch.bfloat16) == \
+        W.WORKSPACE_COUNTER_BYTES + 160 * 2048 * 4
+    # K % 64 != 0: no ring, the sums stay in the GEMM
+    assert W.workspace_bytes(2048, 5024, 17408, 32, torch.bfloat16) == 0
     # fewer CUs, fewer splits wanted: never more scratch than for 256
     assert W.workspace_bytes(64, 4096, 4096, 32, torch.float16, num_cus=32) <= \
         W.workspace_bytes(64, 4096, 4096, 32, torch.float16)

@@ -139,14 +139,15 @@ def test_small_prefill_tiles_exact_bitwise(M, dtype):
     assert np.array_equal(got, want), f"M={M}: {int((got != want).sum())} differ"
 
 
-# The LDS-ring prefill (64-row tiles, K % 64 == 0, G != 32, N % 32 == 0):
+# The LDS-ring prefill (64-row tiles, K % 64 == 0, N % 32 == 0):
 # ragged M (200 = 3 x 64 + 8) and N (544 = 2 x 256 + 32: the last tile's
 # weight pieces past N are clamped), both dtypes, with and without zero
 # points (without them bf16 takes seeded partials). Unsplit, the stage counts
 # KT walk every tail of the loop (it runs four stages per trip while seven
 # remain, then 1..6); split, every split has one to three stages.
 RING_K = [(64 * kt, 64) for kt in (1, 2, 3, 4, 5, 6, 9, 10, 11)] + \
-         [(64 * kt, 128) for kt in (2, 4, 6, 10)] + [(192, 192), (448, 448)]
+         [(64 * kt, 128) for kt in (2, 4, 6, 10)] + [(192, 192), (448, 448)] + \
+         [(64 * kt, 32) for kt in (1, 2, 5, 7)]
 
 
 @pytest.mark.parametrize("K,G", RING_K)
@@ -158,7 +159,8 @@ def test_prefill_ring_parity(K, G, dtype, zp):
     unit = 2 if G == 128 else 1
     for stages in sorted({KT, unit, 3 * unit}):
         plan = W.plan(M, K, N, G, zp, TORCH_DT[dtype], route=W.ROUTE_PREFILL, steps_per_wave=stages)
-        assert plan.block_m == 64 and plan.lds_bytes == 4 * (2 * 64 * 64 * 2 + 4 * 256)
+        blk = 512 if G == 32 else 256
+        assert plan.block_m == 64 and plan.lds_bytes == 4 * (2 * 64 * 64 * 2 + 4 * blk)
         got = dev_to_bits(p.gpu_gemm(plan=plan))
         assert_within_tolerance(got, p.oracle_gemm(), dtype,
                                 f"K={K} G={G} {dtype} zp={zp} stages={stages} splits={plan.splits}")
@@ -166,7 +168,7 @@ def test_prefill_ring_parity(K, G, dtype, zp):
 
 # bit for bit on exact inputs through the ring, unsplit and split
 @pytest.mark.parametrize("dtype,zp,G", [("bf16", False, 128), ("bf16", True, 64), ("fp16", True, 128),
-                                         ("bf16", False, 640)])
+                                         ("bf16", False, 640), ("bf16", True, 32), ("fp16", False, 32)])
 def test_prefill_ring_exact_bitwise(dtype, zp, G):
     M, K, N = 136, 640, 800
     q = _exact_problem(M, K, N, G, dtype, zp, seed=700 + G)

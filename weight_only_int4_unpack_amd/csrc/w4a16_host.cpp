@@ -266,7 +266,7 @@ w4a16_status plan_prefill_bm(int64_t M, int64_t K, int64_t N, int32_t G, int32_t
   pl->steps_per_wave = (int32_t)ks;
   pl->grid = (int32_t)(per_xcd * kXcds);
   pl->threads = kPrefillThreads;
-  pl->lds_bytes = prefill_ring_ok(K, N, G, BM) ? kRingBytes : prefill_lds_bytes((int)BM);
+  pl->lds_bytes = prefill_ring_ok(K, N, G, BM) ? prefill_ring_lds_bytes(K, G) : prefill_lds_bytes((int)BM);
   // K splits: counter region, then the fp32 partials; bf16 through the ring
   // without splits: counter region, then the precomputed activation sums
   pl->workspace_bytes = S > 1 ? (int64_t)(kCounterBytes + S * M * N * 4)

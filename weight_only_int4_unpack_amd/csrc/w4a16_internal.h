@@ -55,25 +55,31 @@ inline int prefill_lds_bytes(int bm) {
   return 2 * bm * kPrefillLdsRowHalves * 2;
 }
 // Prefill through an LDS ring: every operand of a 64-row K stage (activation
-// tile, packed weight tile, the group's scales and zero points) is copied by
-// the load units straight into one of kRingSlots LDS slots, kRingSlots - 1
-// stages ahead of the stage being multiplied, without passing through
-// registers. Taken for 64-row tiles when K % 64 == 0, G != 32 and N % 32 == 0
-// (every 16-byte weight piece of a tile row then lies inside the row).
+// tile, packed weight tile, the group's scales, zero points and precomputed
+// activation sums) is copied by the load units straight into one of
+// kRingSlots LDS slots, kRingSlots - 1 stages ahead of the stage being
+// multiplied, without passing through registers. Taken for 64-row tiles when
+// K % 64 == 0 and N % 32 == 0 (every 16-byte weight piece of a tile row then
+// lies inside the row).
 constexpr int kRingSlots = 4;
 constexpr int kRingTileBytes = 64 * kPrefillBK * 2;  // 64 rows x 64 halves; also 64 K rows x 256 nibbles
-// per wavefront, its 64 columns' scales (128 B) and zero-point words (32 B),
-// in a 256-byte block
 constexpr int kRingAuxOff = 2 * kRingTileBytes;
-constexpr int kRingAuxBytes = 256;
-constexpr int kRingSumOff = 160;  // within a block: 16 precomputed activation sums (bf16, no K split)
-constexpr int kRingSlotBytes = kRingAuxOff + 4 * kRingAuxBytes;
-constexpr int kRingBytes = kRingSlots * kRingSlotBytes;
-static_assert(kRingSlotBytes % 16 == 0, "16-byte aligned slots");
-static_assert(2 * kRingBytes <= kLdsPerCu, "two ring workgroups per CU");
+// Per wavefront, a block with its 64 columns' scales (128 B per group),
+// zero-point words (32 B per group) and 16 rows' activation sums (64 B per
+// group) of the stage's groups: one group per stage in 256 bytes (scales at
+// 0, zero points at 128, sums at 160), or, for groups of 32, two groups in
+// 512 bytes (scales at 0 and 128, zero points at 256 and 288, sums at 320
+// and 384).
+constexpr int ring_aux_bytes(bool two_groups) { return two_groups ? 512 : 256; }
+constexpr int ring_slot_bytes(bool two_groups) { return kRingAuxOff + 4 * ring_aux_bytes(two_groups); }
+constexpr int ring_bytes(bool two_groups) { return kRingSlots * ring_slot_bytes(two_groups); }
+static_assert(ring_slot_bytes(false) % 16 == 0 && ring_slot_bytes(true) % 16 == 0, "16-byte aligned slots");
+static_assert(2 * ring_bytes(true) <= kLdsPerCu, "two ring workgroups per CU");
 inline bool prefill_ring_ok(int64_t K, int64_t N, int32_t G, int64_t bm) {
-  return bm == kPrefillBM && K % kPrefillBK == 0 && G != 32 && N % 32 == 0 && N <= (1 << 26);
+  (void)G;
+  return bm == kPrefillBM && K % kPrefillBK == 0 && N % 32 == 0 && N <= (1 << 26);
 }
+inline int prefill_ring_lds_bytes(int64_t K, int32_t G) { return ring_bytes(G == 32 && K != 32); }
 // bf16 through the ring without K splits: the activation sums of every
 // (group, row), which the factored numerics need at each group's fold, come
 // from a pass over A before the GEMM (asum_kernel: the same MFMA chain

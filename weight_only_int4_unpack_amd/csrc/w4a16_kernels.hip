@@ -780,11 +780,11 @@ template <typename T, bool HAS_ZP, int GS, int KM, bool SPLIT, int BM, bool RING
 __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_kernel(
     PrefillParams p) {
   static_assert(BM == 32 || BM == 64, "tile rows");
-  static_assert(!RING || (BM == 64 && KM == 0 && GS != 1), "ring: 64-row tiles, full stages, G != 32");
+  static_assert(!RING || (BM == 64 && KM == 0), "ring: 64-row tiles, full stages");
   constexpr int RH = kPrefillLdsRowHalves;
   constexpr int MB = BM / 16;
   constexpr int AP = BM / 32;  // 16-byte A pieces per thread per stage
-  constexpr int kLds = RING ? kRingBytes : 2 * BM * RH * 2;
+  constexpr int kLds = RING ? ring_bytes(GS == 1) : 2 * BM * RH * 2;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
   auto As = reinterpret_cast<uint16_t(*)[BM * RH]>(smem);
 
@@ -854,21 +854,31 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
 
   // ---- LDS ring (RING). A slot holds one stage: the activation tile (64
   // rows x 128 B), the weight tile (64 K rows x 128 B: 256 columns of
-  // nibbles), and per wavefront a 256-byte block with the scales (128 B)
-  // and packed zero-point words (32 B) of its 64 columns in the stage's
-  // group. Tiles are stored in 1 KB blocks of 8 rows; within a row the
-  // 16-byte pieces are permuted (XOR) so that the operand reads meet
+  // nibbles), and per wavefront a block with its 64 columns' scales and
+  // packed zero-point words and its 16 rows' precomputed activation sums for
+  // the stage's group, or two groups when G = 32 (layout beside
+  // ring_aux_bytes). Tiles are stored in 1 KB blocks of 8 rows; within a row
+  // the 16-byte pieces are permuted (XOR) so that the operand reads meet
   // distinct LDS banks: activation row r keeps piece j at j ^ (r & 7) (the
   // 16 rows one MFMA operand read spans hit 8 distinct pieces per 8 lanes);
   // weight row k keeps piece j at j ^ 2((k >> 3) & 3) (the 4 rows one
   // 16-bit read spans, 8 apart, hit 4 distinct piece pairs). Each wavefront
-  // copies blocks 2w and 2w + 1 of both tiles and its own scale/zero block:
-  // five copies per stage.
+  // copies blocks 2w and 2w + 1 of both tiles and fills its own block: one
+  // copy of 4 bytes per lane, two for two groups with zero points or sums.
+  constexpr bool kTwo = GS == 1;                 // two groups per stage
+  constexpr int kAuxB = ring_aux_bytes(kTwo);
+  constexpr int kSlotB = ring_slot_bytes(kTwo);
+  constexpr int kSumOff = kTwo ? 320 : 160;      // sums of the stage's (first) group in a block
+  constexpr bool kAux2 = kTwo && (HAS_ZP || kPreSum);
+  constexpr int kCopies = 5 + (kAux2 ? 1 : 0);   // copies per wavefront per stage
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   uint32_t a_dma[2] = {0u, 0u}, b_dma[2] = {0u, 0u};
   uint32_t a_rd[2] = {0u, 0u}, b_rd = 0u, s_rd = 0u, z_rd = 0u, ring_lds = 0u;
-  const char* aux_src = nullptr;  // per lane: the scale pair / zero word of group 0
-  uint32_t aux_step = 0u;         // bytes between groups
+  // per lane: source of its 4 bytes of the block for the stage's first
+  // group, and the bytes between groups (second copy: aux2_*)
+  const char* aux_src = nullptr;
+  const char* aux2_src = nullptr;
+  uint32_t aux_step = 0u, aux2_step = 0u;
   if constexpr (RING) {
     ring_lds = lds_addr(smem);
 #pragma unroll
@@ -881,40 +891,70 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
       const int cc = min(tn * 8 + bp, p.N / 32 - 1) - tn * 8;  // pieces past N: clamped, never stored
       b_dma[j] = (uint32_t)(row * (p.N / 2) + cc * 16);
     }
-    // lanes 0..31: scale pairs of the wavefront's 64 columns; 32..39: their
-    // 8 zero-point words; 40..55 (kPreSum): the activation sums of tile rows
-    // 16w .. 16w + 15; the rest repeat lane 0's pair into the block's pad
     const int col0 = tn * kPrefillBN + wv * 64;
-    if (HAS_ZP && lane >= 32 && lane < 40) {
-      aux_src = (const char*)p.qz + (int64_t)min(col0 / 8 + lane - 32, p.N / 8 - 1) * 4;
-      aux_step = (uint32_t)(p.N / 2);
-    } else if (kPreSum && lane >= 40 && lane < 56) {
-      aux_src = (const char*)(p.asum + m0 + 16 * wv + (lane - 40));
-      aux_step = (uint32_t)(p.asum_rows * 4);
+    auto scale_src = [&](int l) {  // scale pair of columns col0 + 2l, 2l + 1
+      return (const char*)p.sc + (int64_t)min(col0 + 2 * l, p.N - 2) * 2;
+    };
+    auto zero_src = [&](int l) {   // zero-point word of columns col0 + 8l .. 8l + 7
+      return (const char*)p.qz + (int64_t)min(col0 / 8 + l, p.N / 8 - 1) * 4;
+    };
+    auto sum_src = [&](int l) {    // activation sum of tile row 16w + l
+      return (const char*)(p.asum + m0 + 16 * wv + l);
+    };
+    const uint32_t s_step = (uint32_t)(p.N * 2), z_step = (uint32_t)(p.N / 2);
+    const uint32_t a_step = (uint32_t)(p.asum_rows * 4);
+    if constexpr (!kTwo) {
+      // lanes 0..31: scale pairs; 32..39: zero-point words; 40..55 (kPreSum):
+      // activation sums; the rest repeat lane 0's pair into the block's pad
+      if (HAS_ZP && lane >= 32 && lane < 40) {
+        aux_src = zero_src(lane - 32);
+        aux_step = z_step;
+      } else if (kPreSum && lane >= 40 && lane < 56) {
+        aux_src = sum_src(lane - 40);
+        aux_step = a_step;
+      } else {
+        aux_src = scale_src(lane < 32 ? lane : 0);
+        aux_step = s_step;
+      }
     } else {
-      aux_src = (const char*)p.sc + (int64_t)min(col0 + 2 * (lane < 32 ? lane : 0), p.N - 2) * 2;
-      aux_step = (uint32_t)(p.N * 2);
+      // first copy: lanes 0..31 the first group's scale pairs, 32..63 the
+      // second's; second copy: lanes 0..15 zero-point words (8 per group),
+      // 16..47 activation sums (16 per group), the rest repeat lane 0's pair
+      aux_src = scale_src(lane & 31) + (lane >> 5) * s_step;
+      aux_step = s_step;
+      if (HAS_ZP && lane < 16) {
+        aux2_src = zero_src(lane & 7) + (lane >> 3) * z_step;
+        aux2_step = z_step;
+      } else if (kPreSum && lane >= 16 && lane < 48) {
+        aux2_src = sum_src((lane - 16) & 15) + ((lane - 16) >> 4) * a_step;
+        aux2_step = a_step;
+      } else {
+        aux2_src = scale_src(0);
+        aux2_step = s_step;
+      }
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) a_rd[ks] = (uint32_t)(c * 128 + (((ks * 4 + g) ^ (c & 7)) * 16));
     b_rd = (uint32_t)(kRingTileBytes + 8 * g * 128 + (((2 * wave + (c >> 3)) ^ (2 * g)) * 16) + (c & 7) * 2);
-    s_rd = (uint32_t)(kRingAuxOff + wave * kRingAuxBytes + 8 * c);
-    z_rd = (uint32_t)(kRingAuxOff + wave * kRingAuxBytes + 128 + 2 * c);
+    s_rd = (uint32_t)(kRingAuxOff + wave * kAuxB + 8 * c);
+    z_rd = (uint32_t)(kRingAuxOff + wave * kAuxB + (kTwo ? 256 : 128) + 2 * c);
   }
-  // the five copies of stage kt into slot kt % kRingSlots
-  // (slot SL = (kt - kt_beg) % kRingSlots, a compile-time constant)
+  // the copies of stage kt into slot SL = (kt - kt_beg) % kRingSlots (a
+  // compile-time constant)
   auto ring_issue = [&](int kt, auto slc) {
-    constexpr int SO = decltype(slc)::value * kRingSlotBytes;
+    constexpr int SO = decltype(slc)::value * kSlotB;
     const uint32_t wtile = ring_lds + 2 * wv * 1024;               // this wavefront's two tile blocks
-    const uint32_t waux = ring_lds + wv * kRingAuxBytes;           // and its scale/zero block
+    const uint32_t waux = ring_lds + wv * kAuxB;                   // and its scale/zero/sum block
     const char* ab = (const char*)p.a + ((int64_t)m0 * p.K + (int64_t)kt * kPrefillBK) * 2;
     copy16_to_lds<SO>(ab, a_dma[0], wtile);
     copy16_to_lds<SO + 1024>(ab, a_dma[1], wtile);
     const char* bb = (const char*)p.bq + (int64_t)kt * kPrefillBK * (p.N / 2) + tn * (kPrefillBN / 2);
     copy16_to_lds<SO + kRingTileBytes>(bb, b_dma[0], wtile);
     copy16_to_lds<SO + kRingTileBytes + 1024>(bb, b_dma[1], wtile);
-    const int grp = GS == 0 ? 0 : ((kt * kPrefillBK) >> p.g_shift);
+    const int grp = GS == 0 ? 0 : ((kt * kPrefillBK) >> p.g_shift);  // the stage's first group
     copy4_to_lds_lane<SO + kRingAuxOff>(aux_src + (uint64_t)grp * aux_step, waux);
+    if constexpr (kAux2)
+      copy4_to_lds_lane<SO + kRingAuxOff + 256>(aux2_src + (uint64_t)grp * aux2_step, waux);
   };
 
   auto load_a = [&](int kt, u32x4 (&ar)[AP]) {
@@ -1044,16 +1084,18 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       sl.q[r] = u16x2{*(const uint16_t*)(bp + (2 * r) * 128), *(const uint16_t*)(bp + (2 * r + 1) * 128)};
+    const uint32_t gk = kTwo ? ks : 0;  // the slab's group within the stage
     if constexpr (closes || kTile) {
-      sl.s = *(const u32x2*)(smem + so + s_rd);
+      sl.s = *(const u32x2*)(smem + so + s_rd + gk * 128);
       sl.valid = true;
     }
-    if constexpr (HAS_ZP && (closes || kIntOp || kTile)) sl.z = *(const uint16_t*)(smem + so + z_rd);
+    if constexpr (HAS_ZP && (closes || kIntOp || kTile))
+      sl.z = *(const uint16_t*)(smem + so + z_rd + gk * 32);
     constexpr bool opens = GS > 0 && POS % (GS > 0 ? GS : 1) == 0;
     if constexpr (kPreSum && (kInitSum ? opens : closes)) {
 #pragma unroll
       for (int i = 0; i < MB; ++i)
-        asum[i] = *(const f32x4*)(smem + so + kRingAuxOff + i * kRingAuxBytes + kRingSumOff + 16 * g);
+        asum[i] = *(const f32x4*)(smem + so + kRingAuxOff + i * kAuxB + kSumOff + gk * 64 + 16 * g);
     }
   };
   // The MFMAs of one slab (LDS buffer `buf`, 32-row half `ks`). With one
@@ -1100,10 +1142,10 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
     for (int i = 0; i < MB; ++i) {
       const u32x4 aop = aop_at(buf, ks, i);
       if constexpr (GS == 1) {
-        const f32x4 as = kIntOp ? zero4 : mfma<T>(aop, ones, zero4);
+        const f32x4 as = (kIntOp || kInitSum) ? zero4 : kPreSum ? asum[i] : mfma<T>(aop, ones, zero4);
         f32x4 pt[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pt[e] = mfma<T>(aop, bop[e], zero4);
+        for (int e = 0; e < 4; ++e) pt[e] = mfma<T>(aop, bop[e], kInitSum ? asum[i] : zero4);
         fold_block(sc, bias, as, pt, acc[i]);
       } else {
         if constexpr (!kIntOp && !kPreSum) asum[i] = mfma<T>(aop, ones, opens ? zero4 : asum[i]);
@@ -1157,16 +1199,16 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
       constexpr int LATER = decltype(laterc)::value;
       static_assert(kRingSlots == 4, "three stages in flight, slots alternate parity");
       if constexpr (LATER >= 0) {
-        ring_wait<5 * LATER>();
+        ring_wait<kCopies * LATER>();
       } else {  // the last stages: LATER = kt_end - 1 - kt
         const int later = kt_end - 1 - kt;
-        if (later >= 2) ring_wait<10>(); else if (later == 1) ring_wait<5>(); else ring_wait<0>();
+        if (later >= 2) ring_wait<2 * kCopies>(); else if (later == 1) ring_wait<kCopies>(); else ring_wait<0>();
       }
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (decltype(issuec)::value)
         ring_issue(kt + kRingSlots - 1, std::integral_constant<int, (SL + kRingSlots - 1) % kRingSlots>{});
-      constexpr uint32_t so = SL * kRingSlotBytes;
+      constexpr uint32_t so = SL * kSlotB;
       Slab sl;
       ring_slab(so, 0, sl, std::integral_constant<int, 2 * P>{});
       slab(so, 0, sl, std::integral_constant<int, 2 * P>{});
@@ -1647,7 +1689,7 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, bool has_zp, int mode
 template <typename T, bool Z, int GS, int KM>
 static hipError_t prefill_go(const PrefillParams& p, int grid, hipStream_t st) {
   const dim3 g(grid), b(kPrefillThreads);
-  if constexpr (KM == 0 && GS != 1) {
+  if constexpr (KM == 0) {
     if (p.ring) {
       if (p.bm != 64) return hipErrorInvalidValue;
       if (p.S > 1)
