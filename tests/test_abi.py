@@ -266,9 +266,10 @@ def test_selector_prefill_splits(M, K, N, G):
     p = W.plan(M, K, N, G, True, torch.bfloat16, route=W.ROUTE_PREFILL)
     # tile rows: 64, or 32 for M <= 64 when K % 64 == 0 and K splits
     assert p.block_m == (64 if K % 64 or M > 64 or p.splits == 1 else 32)
-    ring = p.block_m == 64 and K % 64 == 0 and N % 32 == 0
+    ring = K % 64 == 0 and N % 32 == 0
     blk = 512 if G == 32 and K != 32 else 256
-    assert p.lds_bytes == (4 * (2 * 64 * 64 * 2 + 4 * blk) if ring else 2 * p.block_m * 80 * 2)
+    assert p.lds_bytes == (4 * (p.block_m * 64 * 2 + 64 * 128 + 4 * blk) if ring
+                           else 2 * p.block_m * 80 * 2)
     tiles = -(-M // p.block_m) * -(-N // 256)
     KT = -(-K // 64)
     S, ks = p.splits, p.steps_per_wave

@@ -166,6 +166,26 @@ def test_prefill_ring_parity(K, G, dtype, zp):
                                 f"K={K} G={G} {dtype} zp={zp} stages={stages} splits={plan.splits}")
 
 
+# The ring's 32-row tiles (few rows, K splits): M within one tile (12, 16) or
+# over two with a ragged second (40, 64), every group span, both dtypes,
+# zero points, N % 256 = 32; the selector's split and a forced one.
+RING_SMALL = [(M, G, dtype, zp) for M in (12, 16, 40, 64) for G in (32, 64, 128, 1024)
+              for dtype in ("fp16", "bf16") for zp in (False, True) if (G + M + zp) % 3 != 1]
+
+
+@pytest.mark.parametrize("M,G,dtype,zp", RING_SMALL)
+def test_prefill_ring_small_tiles_parity(M, G, dtype, zp):
+    K, N = 1024, 800
+    p = random_problem(M, K, N, G, dtype, zp, seed=M * 5 + G + 1)
+    for stages in (0, 6 if G == 128 else 3):
+        plan = W.plan(M, K, N, G, zp, TORCH_DT[dtype], route=W.ROUTE_PREFILL, steps_per_wave=stages)
+        blk = 512 if G == 32 else 256
+        assert plan.block_m == 32 and plan.splits > 1
+        assert plan.lds_bytes == 4 * (32 * 64 * 2 + 64 * 128 + 4 * blk)
+        assert_within_tolerance(dev_to_bits(p.gpu_gemm(plan=plan)), p.oracle_gemm(), dtype,
+                                f"M={M} G={G} {dtype} zp={zp} splits={plan.splits}")
+
+
 # bit for bit on exact inputs through the ring, unsplit and split
 @pytest.mark.parametrize("dtype,zp,G", [("bf16", False, 128), ("bf16", True, 64), ("fp16", True, 128),
                                          ("bf16", False, 640), ("bf16", True, 32), ("fp16", False, 32)])

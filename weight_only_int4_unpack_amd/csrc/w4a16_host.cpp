@@ -266,7 +266,7 @@ w4a16_status plan_prefill_bm(int64_t M, int64_t K, int64_t N, int32_t G, int32_t
   pl->steps_per_wave = (int32_t)ks;
   pl->grid = (int32_t)(per_xcd * kXcds);
   pl->threads = kPrefillThreads;
-  pl->lds_bytes = prefill_ring_ok(K, N, G, BM) ? prefill_ring_lds_bytes(K, G) : prefill_lds_bytes((int)BM);
+  pl->lds_bytes = prefill_ring_ok(K, N, BM) ? prefill_ring_lds_bytes(K, G, BM) : prefill_lds_bytes((int)BM);
   // K splits: counter region, then the fp32 partials; bf16 through the ring
   // without splits: counter region, then the precomputed activation sums
   pl->workspace_bytes = S > 1 ? (int64_t)(kCounterBytes + S * M * N * 4)
@@ -462,7 +462,7 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, void* ws, hip
     p.zp_bias = g.zp_bias;
     p.g_shift = g.G == 32 ? 5 : g.G == 64 ? 6 : g.G == 128 ? 7 : 0;
     p.bm = pl.block_m;
-    p.ring = prefill_ring_ok(g.K, g.N, g.G, pl.block_m) ? 1 : 0;
+    p.ring = prefill_ring_ok(g.K, g.N, pl.block_m) ? 1 : 0;
     if (prefill_asum_pre(g.K, g.N, g.G, g.dtype, pl.block_m, pl.splits)) {
       AsumParams ap{};
       ap.a = (const uint16_t*)g.a;

@@ -58,28 +58,34 @@ inline int prefill_lds_bytes(int bm) {
 // tile, packed weight tile, the group's scales, zero points and precomputed
 // activation sums) is copied by the load units straight into one of
 // kRingSlots LDS slots, kRingSlots - 1 stages ahead of the stage being
-// multiplied, without passing through registers. Taken for 64-row tiles when
-// K % 64 == 0 and N % 32 == 0 (every 16-byte weight piece of a tile row then
-// lies inside the row).
+// multiplied, without passing through registers. Taken when K % 64 == 0 and
+// N % 32 == 0 (every 16-byte weight piece of a tile row then lies inside the
+// row), for 64-row tiles and for the 32-row tiles of K-split launches.
 constexpr int kRingSlots = 4;
-constexpr int kRingTileBytes = 64 * kPrefillBK * 2;  // 64 rows x 64 halves; also 64 K rows x 256 nibbles
-constexpr int kRingAuxOff = 2 * kRingTileBytes;
-// Per wavefront, a block with its 64 columns' scales (128 B per group),
+constexpr int kRingWeightBytes = kPrefillBK * kPrefillBN / 2;  // 64 K rows x 256 nibbles
+// Slot layout: the activation tile (bm rows x 128 B), the weight tile, then
+// per wavefront a block with its 64 columns' scales (128 B per group),
 // zero-point words (32 B per group) and 16 rows' activation sums (64 B per
 // group) of the stage's groups: one group per stage in 256 bytes (scales at
 // 0, zero points at 128, sums at 160), or, for groups of 32, two groups in
 // 512 bytes (scales at 0 and 128, zero points at 256 and 288, sums at 320
 // and 384).
+constexpr int ring_a_bytes(int bm) { return bm * kPrefillBK * 2; }
+constexpr int ring_aux_off(int bm) { return ring_a_bytes(bm) + kRingWeightBytes; }
 constexpr int ring_aux_bytes(bool two_groups) { return two_groups ? 512 : 256; }
-constexpr int ring_slot_bytes(bool two_groups) { return kRingAuxOff + 4 * ring_aux_bytes(two_groups); }
-constexpr int ring_bytes(bool two_groups) { return kRingSlots * ring_slot_bytes(two_groups); }
-static_assert(ring_slot_bytes(false) % 16 == 0 && ring_slot_bytes(true) % 16 == 0, "16-byte aligned slots");
-static_assert(2 * ring_bytes(true) <= kLdsPerCu, "two ring workgroups per CU");
-inline bool prefill_ring_ok(int64_t K, int64_t N, int32_t G, int64_t bm) {
-  (void)G;
-  return bm == kPrefillBM && K % kPrefillBK == 0 && N % 32 == 0 && N <= (1 << 26);
+constexpr int ring_slot_bytes(int bm, bool two_groups) {
+  return ring_aux_off(bm) + 4 * ring_aux_bytes(two_groups);
 }
-inline int prefill_ring_lds_bytes(int64_t K, int32_t G) { return ring_bytes(G == 32 && K != 32); }
+constexpr int ring_bytes(int bm, bool two_groups) { return kRingSlots * ring_slot_bytes(bm, two_groups); }
+static_assert(ring_slot_bytes(32, false) % 16 == 0 && ring_slot_bytes(64, true) % 16 == 0,
+              "16-byte aligned slots");
+static_assert(2 * ring_bytes(64, true) <= kLdsPerCu, "two ring workgroups per CU");
+inline bool prefill_ring_ok(int64_t K, int64_t N, int64_t bm) {
+  return (bm == kPrefillBM || bm == 32) && K % kPrefillBK == 0 && N % 32 == 0 && N <= (1 << 26);
+}
+inline int prefill_ring_lds_bytes(int64_t K, int32_t G, int64_t bm) {
+  return ring_bytes((int)bm, G == 32 && K != 32);
+}
 // bf16 through the ring without K splits: the activation sums of every
 // (group, row), which the factored numerics need at each group's fold, come
 // from a pass over A before the GEMM (asum_kernel: the same MFMA chain
@@ -91,7 +97,8 @@ inline int prefill_ring_lds_bytes(int64_t K, int32_t G) { return ring_bytes(G ==
 // and start each group's partial sums.
 inline int64_t prefill_asum_rows(int64_t M) { return (M + kPrefillBM - 1) / kPrefillBM * kPrefillBM; }
 inline bool prefill_asum_pre(int64_t K, int64_t N, int32_t G, int32_t dtype, int64_t bm, int64_t S) {
-  return dtype == W4A16_BF16 && S == 1 && prefill_ring_ok(K, N, G, bm);
+  (void)G;
+  return dtype == W4A16_BF16 && S == 1 && bm == kPrefillBM && prefill_ring_ok(K, N, bm);
 }
 inline int64_t prefill_asum_bytes(int64_t M, int64_t K, int32_t G) {
   return (K / G) * prefill_asum_rows(M) * (int64_t)sizeof(float);

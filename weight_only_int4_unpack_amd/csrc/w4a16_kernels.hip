@@ -777,14 +777,14 @@ __device__ __forceinline__ void ring_wait() {
 // weight being dequantised twice as often). 16-row tiles were slower than 32
 // at M = 16 (14.3 us; with four workgroups per CU they spilled to scratch).
 template <typename T, bool HAS_ZP, int GS, int KM, bool SPLIT, int BM, bool RING>
-__global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_kernel(
+__global__ __launch_bounds__(kPrefillThreads, (BM == 64 || RING) ? 2 : 3) void prefill_kernel(
     PrefillParams p) {
   static_assert(BM == 32 || BM == 64, "tile rows");
-  static_assert(!RING || (BM == 64 && KM == 0), "ring: 64-row tiles, full stages");
+  static_assert(!RING || (KM == 0 && (BM == 64 || SPLIT)), "ring: full stages; 32-row tiles split K");
   constexpr int RH = kPrefillLdsRowHalves;
   constexpr int MB = BM / 16;
   constexpr int AP = BM / 32;  // 16-byte A pieces per thread per stage
-  constexpr int kLds = RING ? ring_bytes(GS == 1) : 2 * BM * RH * 2;
+  constexpr int kLds = RING ? ring_bytes(BM, GS == 1) : 2 * BM * RH * 2;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
   auto As = reinterpret_cast<uint16_t(*)[BM * RH]>(smem);
 
@@ -867,10 +867,13 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
   // copy of 4 bytes per lane, two for two groups with zero points or sums.
   constexpr bool kTwo = GS == 1;                 // two groups per stage
   constexpr int kAuxB = ring_aux_bytes(kTwo);
-  constexpr int kSlotB = ring_slot_bytes(kTwo);
+  constexpr int kSlotB = ring_slot_bytes(BM, kTwo);
+  constexpr int kBOff = ring_a_bytes(BM);        // weight tile
+  constexpr int kAuxOff = ring_aux_off(BM);      // per-wavefront blocks
+  constexpr int kABlk = BM / 32;                 // activation blocks each wavefront copies
   constexpr int kSumOff = kTwo ? 320 : 160;      // sums of the stage's (first) group in a block
   constexpr bool kAux2 = kTwo && (HAS_ZP || kPreSum);
-  constexpr int kCopies = 5 + (kAux2 ? 1 : 0);   // copies per wavefront per stage
+  constexpr int kCopies = kABlk + 3 + (kAux2 ? 1 : 0);  // copies per wavefront per stage
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   uint32_t a_dma[2] = {0u, 0u}, b_dma[2] = {0u, 0u};
   uint32_t a_rd[2] = {0u, 0u}, b_rd = 0u, s_rd = 0u, z_rd = 0u, ring_lds = 0u;
@@ -885,11 +888,13 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
     for (int j = 0; j < 2; ++j) {
       const int blk = 2 * wv + j;
       const int row = 8 * blk + (lane >> 3);
-      const int ap = (lane & 7) ^ (row & 7);
-      a_dma[j] = (uint32_t)((min(m0 + row, p.M - 1) - m0) * p.K * 2 + ap * 16);
       const int bp = (lane & 7) ^ (2 * (blk & 3));
       const int cc = min(tn * 8 + bp, p.N / 32 - 1) - tn * 8;  // pieces past N: clamped, never stored
       b_dma[j] = (uint32_t)(row * (p.N / 2) + cc * 16);
+      // activation blocks: kABlk per wavefront (rows 8 kABlk w + 8j + lane / 8)
+      const int arow = 8 * (kABlk * wv + j) + (lane >> 3);
+      const int ap = (lane & 7) ^ (arow & 7);
+      a_dma[j] = (uint32_t)((min(m0 + arow, p.M - 1) - m0) * p.K * 2 + ap * 16);
     }
     const int col0 = tn * kPrefillBN + wv * 64;
     auto scale_src = [&](int l) {  // scale pair of columns col0 + 2l, 2l + 1
@@ -935,26 +940,27 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) a_rd[ks] = (uint32_t)(c * 128 + (((ks * 4 + g) ^ (c & 7)) * 16));
-    b_rd = (uint32_t)(kRingTileBytes + 8 * g * 128 + (((2 * wave + (c >> 3)) ^ (2 * g)) * 16) + (c & 7) * 2);
-    s_rd = (uint32_t)(kRingAuxOff + wave * kAuxB + 8 * c);
-    z_rd = (uint32_t)(kRingAuxOff + wave * kAuxB + (kTwo ? 256 : 128) + 2 * c);
+    b_rd = (uint32_t)(kBOff + 8 * g * 128 + (((2 * wave + (c >> 3)) ^ (2 * g)) * 16) + (c & 7) * 2);
+    s_rd = (uint32_t)(kAuxOff + wave * kAuxB + 8 * c);
+    z_rd = (uint32_t)(kAuxOff + wave * kAuxB + (kTwo ? 256 : 128) + 2 * c);
   }
   // the copies of stage kt into slot SL = (kt - kt_beg) % kRingSlots (a
   // compile-time constant)
   auto ring_issue = [&](int kt, auto slc) {
     constexpr int SO = decltype(slc)::value * kSlotB;
-    const uint32_t wtile = ring_lds + 2 * wv * 1024;               // this wavefront's two tile blocks
-    const uint32_t waux = ring_lds + wv * kAuxB;                   // and its scale/zero/sum block
+    const uint32_t wa = ring_lds + kABlk * wv * 1024;              // this wavefront's activation blocks,
+    const uint32_t wb = ring_lds + 2 * wv * 1024;                  // weight blocks
+    const uint32_t waux = ring_lds + wv * kAuxB;                   // and scale/zero/sum block
     const char* ab = (const char*)p.a + ((int64_t)m0 * p.K + (int64_t)kt * kPrefillBK) * 2;
-    copy16_to_lds<SO>(ab, a_dma[0], wtile);
-    copy16_to_lds<SO + 1024>(ab, a_dma[1], wtile);
+    copy16_to_lds<SO>(ab, a_dma[0], wa);
+    if constexpr (kABlk == 2) copy16_to_lds<SO + 1024>(ab, a_dma[1], wa);
     const char* bb = (const char*)p.bq + (int64_t)kt * kPrefillBK * (p.N / 2) + tn * (kPrefillBN / 2);
-    copy16_to_lds<SO + kRingTileBytes>(bb, b_dma[0], wtile);
-    copy16_to_lds<SO + kRingTileBytes + 1024>(bb, b_dma[1], wtile);
+    copy16_to_lds<SO + kBOff>(bb, b_dma[0], wb);
+    copy16_to_lds<SO + kBOff + 1024>(bb, b_dma[1], wb);
     const int grp = GS == 0 ? 0 : ((kt * kPrefillBK) >> p.g_shift);  // the stage's first group
-    copy4_to_lds_lane<SO + kRingAuxOff>(aux_src + (uint64_t)grp * aux_step, waux);
+    copy4_to_lds_lane<SO + kAuxOff>(aux_src + (uint64_t)grp * aux_step, waux);
     if constexpr (kAux2)
-      copy4_to_lds_lane<SO + kRingAuxOff + 256>(aux2_src + (uint64_t)grp * aux2_step, waux);
+      copy4_to_lds_lane<SO + kAuxOff + 256>(aux2_src + (uint64_t)grp * aux2_step, waux);
   };
 
   auto load_a = [&](int kt, u32x4 (&ar)[AP]) {
@@ -1095,7 +1101,7 @@ __global__ __launch_bounds__(kPrefillThreads, BM == 64 ? 2 : 3) void prefill_ker
     if constexpr (kPreSum && (kInitSum ? opens : closes)) {
 #pragma unroll
       for (int i = 0; i < MB; ++i)
-        asum[i] = *(const f32x4*)(smem + so + kRingAuxOff + i * kAuxB + kSumOff + gk * 64 + 16 * g);
+        asum[i] = *(const f32x4*)(smem + so + kAuxOff + i * kAuxB + kSumOff + gk * 64 + 16 * g);
     }
   };
   // The MFMAs of one slab (LDS buffer `buf`, 32-row half `ks`). With one
@@ -1691,8 +1697,11 @@ static hipError_t prefill_go(const PrefillParams& p, int grid, hipStream_t st) {
   const dim3 g(grid), b(kPrefillThreads);
   if constexpr (KM == 0) {
     if (p.ring) {
-      if (p.bm != 64) return hipErrorInvalidValue;
-      if (p.S > 1)
+      if (p.bm == 32 && p.S > 1)
+        hipLaunchKernelGGL((prefill_kernel<T, Z, GS, KM, true, 32, true>), g, b, 0, st, p);
+      else if (p.bm != 64)
+        return hipErrorInvalidValue;
+      else if (p.S > 1)
         hipLaunchKernelGGL((prefill_kernel<T, Z, GS, KM, true, 64, true>), g, b, 0, st, p);
       else
         hipLaunchKernelGGL((prefill_kernel<T, Z, GS, KM, false, 64, true>), g, b, 0, st, p);
