@@ -199,11 +199,11 @@ w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dty
 
 // Prefill: 64 x 256 tiles. When there are fewer tiles than CUs, K is split
 // across workgroups (whole groups per split, at least two 64-row stages
-// each) so that about one workgroup per CU runs; each split writes an fp32
-// partial of the M real rows and a second, fully parallel kernel adds them in
-// split order. (Measured at K = N = 4096: one workgroup per CU beat two at
-// M = 16 and 256, since every split adds M x N x 8 bytes of partial traffic;
-// 13.4 vs 14.8 us at M = 16, 32.7 vs 34.0 us at M = 256.)
+// each); each split writes an fp32 partial of the M real rows and a second,
+// fully parallel kernel adds them in split order. Every split adds M x N x 8
+// bytes of partial traffic, so the register-staged kernel ran best at one
+// workgroup per CU (13.4 vs 14.8 us at M = 16, 32.7 vs 34.0 us at M = 256,
+// K = N = 4096); the ring's 64-row tiles at two (below).
 //
 // Tile rows: 64, or 32 for M <= 64 when K % 64 == 0 and the launch splits
 // K, so that fewer MFMA rows are padding and more workgroups fit a CU
@@ -236,7 +236,11 @@ w4a16_status plan_prefill_bm(int64_t M, int64_t K, int64_t N, int32_t G, int32_t
   const int64_t KT = ceil_div(K, kPrefillBK);
   const int64_t unit = ((int64_t)G != K && G == 128) ? 2 : 1;  // stages per group
   int64_t S = 1, ks = KT;
-  const int64_t want = (int64_t)num_cus;
+  // fewer tiles than CUs: split to about one workgroup per CU for 32-row
+  // tiles, two for 64-row ring tiles (K = N = 4096, M = 256, 64 tiles: 8
+  // splits 34.0 us, 4 splits 35.9 us; M = 16 and 64 on 32-row tiles are
+  // fastest at 16 and 8 splits)
+  const int64_t want = (int64_t)num_cus * ((BM == kPrefillBM && prefill_ring_ok(K, N, BM)) ? 2 : 1);
   if (ks_forced != 0) {
     if (ks_forced < 0 || ks_forced % unit != 0)
       return fail(W4A16_ERR_PLAN, "prefill stages per workgroup must be a positive multiple of %lld",
@@ -247,7 +251,7 @@ w4a16_status plan_prefill_bm(int64_t M, int64_t K, int64_t N, int32_t G, int32_t
       return fail(W4A16_ERR_PLAN, "%lld stages per workgroup give %lld K splits (at most %d)",
                   (long long)ks_forced, (long long)S, kPrefillMaxSplits);
     if (S == 1) ks = KT;
-  } else if (tiles < want) {
+  } else if (tiles < (int64_t)num_cus) {
     const int64_t s_max = std::max<int64_t>(1, std::min<int64_t>(kPrefillMaxSplits, KT / (2 * unit)));
     const int64_t s0 = std::min<int64_t>(s_max, ceil_div(want, tiles));
     if (s0 > 1) {
