@@ -156,8 +156,11 @@ def test_gemm_bias_checks():
 
 
 def test_group_64_is_kept_not_substituted():
-    p = W.plan(8, 2112, 5120, 64, True, torch.float16)
-    assert p.route == W.ROUTE_DECODE
+    # both routes plan groups of 64 as given (the decode route with its exact
+    # one-fold operand, as the group holds a wavefront's two steps)
+    assert W.plan(8, 2112, 5120, 64, True, torch.float16).route == W.ROUTE_PREFILL
+    p = W.plan(8, 2112, 5120, 64, True, torch.float16, route=W.ROUTE_DECODE)
+    assert p.route == W.ROUTE_DECODE and p.decode_mode == 1
     # a non-multiple K for G=64 is an error, never a fallback to another G
     assert _gemm(M=8, K=2100, N=5120, G=64) == W.ERR_SHAPE
 
@@ -196,17 +199,30 @@ def test_python_wrapper_validates_shapes():
 
 # ------------------------------------------------------------ selector
 def test_selector_routes_on_runtime_m():
-    for M in (1, 2, 4, 5, 6, 8):
-        assert W.plan(M, 4096, 4096, 32, True, torch.float16).route == W.ROUTE_DECODE
-    for M in (9, 16, 17, 64, 256, 2048, 4096):
-        assert W.plan(M, 4096, 4096, 32, True, torch.float16).route == W.ROUTE_PREFILL
+    D, P = W.ROUTE_DECODE, W.ROUTE_PREFILL
+    # fp16 groups of 32, N <= 8192: decode for one row, the ring prefill's
+    # K split (32-row tiles) from two rows on
+    assert W.plan(1, 4096, 4096, 32, True, torch.float16).route == D
+    for M in (2, 4, 5, 6, 8, 9, 16, 17, 64, 256, 2048, 4096):
+        assert W.plan(M, 4096, 4096, 32, True, torch.float16).route == P
     assert W.plan(0, 4096, 4096, 32, True, torch.float16).route == W.ROUTE_NONE
-    # per-channel scales: decode up to 16 rows, with fewer splits above 8 rows
+    # other groups: decode below 4 rows, prefill from 4 rows with >= 8M weights
+    for M, route in ((1, D), (2, D), (3, D), (4, P), (8, P), (9, P)):
+        assert W.plan(M, 4096, 4096, 128, False, torch.bfloat16).route == route, M
+    # small weights (K = N = 2048) and wide N (14336, 17408) stay on decode
+    assert W.plan(4, 2048, 2048, 128, False, torch.bfloat16).route == D
+    assert W.plan(4, 4096, 14336, 128, False, torch.bfloat16).route == D
+    assert W.plan(8, 5120, 17408, 128, False, torch.bfloat16).route == D
+    # K % 64 != 0 or N % 32 != 0 (no ring): decode up to 8 rows
+    assert W.plan(8, 4160 - 32, 4096, 4128, True, torch.float16).route == D
+    assert W.plan(8, 4096, 4104, 128, True, torch.float16).route == D
+    # per-channel scales: the decode route up to 16 rows where the prefill
+    # ring does not win (here: wide N), with fewer splits above 8 rows
     for M in (9, 12, 16):
-        p = W.plan(M, 4096, 4096, 4096, True, torch.float16)
-        assert p.route == W.ROUTE_DECODE and p.decode_mode == 1 and p.steps_per_wave == 4
-    assert W.plan(8, 4096, 4096, 4096, True, torch.float16).steps_per_wave == 2
-    assert W.plan(17, 4096, 4096, 4096, True, torch.float16).route == W.ROUTE_PREFILL
+        p = W.plan(M, 4096, 14336, 4096, True, torch.float16)
+        assert p.route == D and p.decode_mode == 1
+        assert W.plan(M, 4096, 4096, 4096, True, torch.float16).route == P
+    assert W.plan(17, 4096, 14336, 4096, True, torch.float16).route == P
 
 
 def test_selector_decode_shapes():
@@ -223,7 +239,7 @@ def test_selector_decode_shapes():
                   steps_per_wave=8).decode_mode == 2
     # K = 2112 is 66 steps of 32 rows; groups of 64 hold a wavefront's 2 steps,
     # so the exact operand with one in-place fold (mode 1) applies
-    p = W.plan(8, 2112, 5120, 64, True, torch.float16)
+    p = W.plan(8, 2112, 5120, 64, True, torch.float16, route=W.ROUTE_DECODE)
     assert p.splits * 4 * p.steps_per_wave >= 66
     assert p.steps_per_wave == 2 and p.decode_mode == 1
     # fp16 groups of 32 with 2 steps per wavefront: the rounded weight (mode 0)
@@ -237,7 +253,7 @@ def test_selector_decode_shapes():
     p = W.plan(4, 4096, 4096, 32, True, torch.bfloat16, route=W.ROUTE_DECODE, steps_per_wave=4)
     assert p.decode_mode == 2
     # per-channel: one group spans every step
-    assert W.plan(8, 4096, 4096, 4096, True, torch.float16).decode_mode == 1
+    assert W.plan(8, 4096, 4096, 4096, True, torch.float16, route=W.ROUTE_DECODE).decode_mode == 1
 
 
 def test_selector_prefill_tiles():
@@ -398,7 +414,9 @@ def test_bf16_decode_mode_0_rejected():
     # the selector never picks it for bf16
     for G in (32, 64, 128, 4096):
         for M in range(1, 9):
-            assert W.plan(M, 4096, 4096, G, True, torch.bfloat16).decode_mode != 0
+            for N in (4096, 14336):
+                p = W.plan(M, 4096, N, G, True, torch.bfloat16)
+                assert p.route != W.ROUTE_DECODE or p.decode_mode != 0
 
 
 def test_k_limit_and_counter_limit():

@@ -218,10 +218,11 @@ def test_prefill_bf16_long_k_splits(stages):
     assert np.array_equal(got, want), f"stages={stages}: {int((got != want).sum())} differ"
 
 
-# per-channel scales take the decode route up to 16 rows (fewer splits above
-# 8 rows); aligned and ragged shapes, through the selector's own plan
+# per-channel scales take the decode route up to 16 rows where the ring
+# prefill does not apply or win (fewer splits above 8 rows); aligned K with
+# N % 32 != 0, and ragged K, through the selector's own plan
 @pytest.mark.parametrize("M", [9, 12, 16])
-@pytest.mark.parametrize("K,N,dtype", [(4096, 4096, "fp16"), (2120, 520, "bf16")])
+@pytest.mark.parametrize("K,N,dtype", [(4096, 4104, "fp16"), (2120, 520, "bf16")])
 def test_per_channel_decode_route_mid_m(M, K, N, dtype):
     p = random_problem(M, K, N, K, dtype, True, seed=400 + M + K)
     plan = W.plan(M, K, N, K, True, TORCH_DT[dtype])

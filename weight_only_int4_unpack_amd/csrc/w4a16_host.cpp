@@ -291,17 +291,29 @@ w4a16_status make_plan(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype
     pl->route = W4A16_ROUTE_NONE;
     return W4A16_OK;
   }
-  // Decode for M <= 8; per-channel scales (one group) also up to 16 rows,
-  // where the decode kernel's single in-place fold beat the prefill's K-split
-  // route (K = N = 4096, M = 16: 12.0 vs 12.9 us; M = 12: 11.4 vs 12.5 us).
-  // With groups of 32 the prefill route stays faster at M = 12 and 16.
-  // (N beyond what the counter region serves, 2^20 columns, has column
-  // blocks enough to fill the GPU on the prefill route's tiles)
-  if (route == 0)
-    route = ((M <= w4a16::kAutoDecodeMaxM || (M <= w4a16::kDecodeMaxM && (int64_t)G == K)) &&
-             ceil_div(N, w4a16::kDecodeCols) <= w4a16::kMaxCounterBlocks)
-                ? W4A16_ROUTE_DECODE
-                : W4A16_ROUTE_PREFILL;
+  // Decode for M <= 8 and per-channel scales (one group) up to 16 rows,
+  // unless the prefill route's K split through the LDS ring (32-row tiles)
+  // is faster: with few column tiles (N <= 8192) it wins from 2 rows on for
+  // fp16 with groups of 32 (the decode kernel then feeds rounded weights)
+  // and from 4 rows on with 8M weights or more; it loses at one row, for
+  // wide N (its few splits stream too slowly) and for small weights.
+  // Measured graph-replayed, decode -> prefill: K = N = 4096 fp16 G = 32,
+  // M = 2 10.5 -> 9.9, M = 5 14.1 -> 9.8 us; K = 2112, N = 5120 fp16 G = 64,
+  // M = 8 9.4 -> 8.6 us; K = 8192, N = 4096 bf16 G = 128, M = 4 17.6 -> 11.6
+  // us; per-channel K = N = 4096, M = 16 12.1 -> 10.5 us; kept on decode:
+  // K = 5120, N = 17408 bf16 M = 8 16.4 vs 21.8 us, K = 4096, N = 14336
+  // M = 4 12.3 vs 18.1 us, M = 1 everywhere but the largest fp16 G = 32
+  // shapes, K = N = 2048 bf16 M = 4 7.0 vs 7.7 us. (N beyond what the
+  // counter region serves, 2^20 columns, has column blocks enough to fill
+  // the GPU on the prefill route's tiles.)
+  if (route == 0) {
+    bool decode = (M <= w4a16::kAutoDecodeMaxM || (M <= w4a16::kDecodeMaxM && (int64_t)G == K)) &&
+                  ceil_div(N, w4a16::kDecodeCols) <= w4a16::kMaxCounterBlocks;
+    if (decode && w4a16::prefill_ring_ok(K, N, 32) && N <= 8192 &&
+        ((dtype == W4A16_F16 && G == 32 && M >= 2) || (M >= 4 && K * N >= (8ll << 20))))
+      decode = false;
+    route = decode ? W4A16_ROUTE_DECODE : W4A16_ROUTE_PREFILL;
+  }
   if (route == W4A16_ROUTE_DECODE) {
     if (M > w4a16::kDecodeMaxM)
       return fail(W4A16_ERR_PLAN, "decode route needs M <= %d (got %lld)", w4a16::kDecodeMaxM,
