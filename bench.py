@@ -268,15 +268,11 @@ def context_matmul(torch, M=2048, K=5120, N=17408, launches=20):
                    f"{launches} launches graph-replayed"}
 
 
-def forced_prefill(name, stages, torch, W, synthetic, launches=40):
-    """Graph-replayed per-launch time of one workload on the prefill route
-    with the K stages per split forced (w4a16_gemm_planned; the library's
-    workspace of the capturing stream is made by one uncaptured call first)."""
-    w = synthetic.WORKLOADS[name]
+def plan_time(w, pl, torch, W, synthetic, launches=40):
+    """Graph-replayed per-launch time of workload w with plan pl
+    (w4a16_gemm_planned; the library's workspace of the capturing stream is
+    made by one uncaptured call first)."""
     L = Launch(w, torch, W, synthetic, rotate=True)
-    dt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
-    pl = W.plan(w.M, w.K, w.N, w.group_size, w.has_zp, dt, route=W.ROUTE_PREFILL,
-                steps_per_wave=stages)
     run = lambda i: W.gemm(L.a, *L.sets[i % len(L.sets)][:2], L.sets[i % len(L.sets)][2],
                            w.group_size, 8, out=L.out, plan=pl)
     side = torch.cuda.Stream()
@@ -298,8 +294,17 @@ def forced_prefill(name, stages, torch, W, synthetic, launches=40):
     g.replay()
     t1.record()
     torch.cuda.synchronize()
+    return round(t0.elapsed_time(t1) * 1e3 / launches, 2)
+
+
+def forced_prefill(name, stages, torch, W, synthetic):
+    """One workload on the prefill route with the K stages per split forced."""
+    w = synthetic.WORKLOADS[name]
+    dt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
+    pl = W.plan(w.M, w.K, w.N, w.group_size, w.has_zp, dt, route=W.ROUTE_PREFILL,
+                steps_per_wave=stages)
     return {"workload": name, "stages_per_split": pl.steps_per_wave, "splits": pl.splits,
-            "workgroups": pl.grid, "us_per_launch": round(t0.elapsed_time(t1) * 1e3 / launches, 2)}
+            "workgroups": pl.grid, "us_per_launch": plan_time(w, pl, torch, W, synthetic)}
 
 
 def issue_probe(torch, iters=4000):
