@@ -714,14 +714,18 @@ __device__ __forceinline__ const void* scalar_ptr(const void* p) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
-// LDS destination = lds (wave-uniform) + OFF (a compile-time byte offset)
+// LDS destination = lds (wave-uniform) + OFF (a compile-time byte offset).
+// The scalar add that forms m0 also writes SCC, which the compiler may be
+// carrying between the two halves of a 64-bit address add around this
+// statement: SCC is declared clobbered (without it, a carry lost here put a
+// pointer 4 GiB low whenever its low half wrapped, and the load faulted).
 template <int OFF>
 __device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voff, uint32_t lds) {
   static_assert(OFF >= 0 && OFF < (1 << 20), "LDS offset");
   asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(scalar_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds)), "n"(OFF)
-               : "memory");
+               : "memory", "scc");
 }
 // 4 bytes per lane from the lane's own address
 template <int OFF>
@@ -730,7 +734,7 @@ __device__ __forceinline__ void copy4_to_lds_lane(const void* src, uint32_t lds)
   asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :
                : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)), "n"(OFF)
-               : "memory");
+               : "memory", "scc");
 }
 // Wait until at most N of this wavefront's vector-memory operations are in
 // flight (they complete in issue order); also a compiler barrier for memory.
