@@ -880,7 +880,7 @@ __global__ __launch_bounds__(kPrefillThreads, (BM == 64 || RING) ? 2 : 3) void p
   constexpr int kCopies = kABlk + 3 + (kAux2 ? 1 : 0);  // copies per wavefront per stage
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   uint32_t a_dma[2] = {0u, 0u}, b_dma[2] = {0u, 0u};
-  uint32_t a_rd[2] = {0u, 0u}, b_rd = 0u, s_rd = 0u, z_rd = 0u, ring_lds = 0u;
+  uint32_t a_rd[2] = {0u, 0u}, b_rd = 0u, b_sel = 0u, s_rd = 0u, z_rd = 0u, ring_lds = 0u;
   // per lane: source of its 4 bytes of the block for the stage's first
   // group, and the bytes between groups (second copy: aux2_*)
   const char* aux_src = nullptr;
@@ -944,7 +944,9 @@ __global__ __launch_bounds__(kPrefillThreads, (BM == 64 || RING) ? 2 : 3) void p
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) a_rd[ks] = (uint32_t)(c * 128 + (((ks * 4 + g) ^ (c & 7)) * 16));
-    b_rd = (uint32_t)(kBOff + 8 * g * 128 + (((2 * wave + (c >> 3)) ^ (2 * g)) * 16) + (c & 7) * 2);
+    // the dword holding the lane's 16 bits of a weight row (its half: c & 1)
+    b_rd = (uint32_t)(kBOff + 8 * g * 128 + (((2 * wave + (c >> 3)) ^ (2 * g)) * 16) + (c & 6) * 2);
+    b_sel = (c & 1) ? 0x07060302u : 0x05040100u;
     s_rd = (uint32_t)(kAuxOff + wave * kAuxB + 8 * c);
     z_rd = (uint32_t)(kAuxOff + wave * kAuxB + (kTwo ? 256 : 128) + 2 * c);
   }
@@ -1086,14 +1088,16 @@ __global__ __launch_bounds__(kPrefillThreads, (BM == 64 || RING) ? 2 : 3) void p
       return *(const u32x4*)&As[buf][(i * 16 + c) * RH + ks * 32 + 8 * g];
   };
   // A slab's weights, scales and zero points from the ring slot at byte
-  // offset `so` (RING): rows 2r and 2r + 1 of the lane's 8 in one register.
+  // offset `so` (RING): rows 2r and 2r + 1 of the lane's 8 in one register,
+  // from one two-dword LDS read (the dwords of both rows that hold the
+  // lane's 16 bits, 128 bytes apart) and one byte permute.
   auto ring_slab = [&](uint32_t so, int ks, Slab& sl, auto posc) {
     constexpr int POS = decltype(posc)::value;
     constexpr bool closes = GS > 0 && (POS + 1) % (GS > 0 ? GS : 1) == 0;
-    const unsigned char* bp = smem + so + b_rd + ks * 32 * 128;
+    const uint32_t* bp = (const uint32_t*)(smem + so + b_rd + ks * 32 * 128);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      sl.q[r] = u16x2{*(const uint16_t*)(bp + (2 * r) * 128), *(const uint16_t*)(bp + (2 * r + 1) * 128)};
+      sl.q[r] = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(bp[(2 * r + 1) * 32], bp[(2 * r) * 32], b_sel));
     const uint32_t gk = kTwo ? ks : 0;  // the slab's group within the stage
     if constexpr (closes || kTile) {
       sl.s = *(const u32x2*)(smem + so + s_rd + gk * 128);
