@@ -104,6 +104,38 @@ __device__ __forceinline__ uint32_t magic_pair(uint32_t y, const DqRegs& k) {
   }
 }
 
+// A 64-bit right shift of the word pair {y1, y0}: y1 >> s in the high word,
+// y0 >> s in the low word save for y1's low bits, which enter from bit 32 - s
+// up (s <= 12: bit 20 and above).
+template <int S>
+__device__ __forceinline__ uint64_t shr64(uint64_t y) {
+  static_assert(S > 0 && S <= 12, "shift");
+  uint64_t r;
+  asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "n"(S), "v"(y));
+  return r;
+}
+// magic_pair of four words (two row pairs each). Where a pair needs a shift
+// (bf16 e > 0: 4e; fp16 e >= 2: 8), one 64-bit shift serves two words: the
+// masks keep bits 0..7 and 16..23 only, below the bits the other word
+// shifts in (bf16 2048 x 5120 x 17408 prefill 348.6 -> 338.4 us, decode
+// M = 1 13.97 -> 13.47 us). PAIRED = false keeps one 32-bit shift per word:
+// on the few-row fp16 routes that feed the integer operand (K-split
+// prefill) or the rounded one (decode mode 0) it measured as fast or faster
+// (K = N = 4096, M = 5: 9.47 against 9.68 us).
+template <typename T, int E, bool PAIRED = true>
+__device__ __forceinline__ u32x4 magic_op(const uint32_t* y, const DqRegs& mag) {
+  constexpr int S = T::kIsF16 ? (E >= 2 ? 8 : 0) : 4 * E;
+  if constexpr (S == 0 || !PAIRED) {
+    return u32x4{magic_pair<T, E>(y[0], mag), magic_pair<T, E>(y[1], mag),
+                 magic_pair<T, E>(y[2], mag), magic_pair<T, E>(y[3], mag)};
+  } else {
+    const uint32_t m = (T::kIsF16 && (E & 1)) ? mag.m_hi : mag.m_lo;
+    const uint64_t s01 = shr64<S>(((uint64_t)y[1] << 32) | y[0]);
+    const uint64_t s23 = shr64<S>(((uint64_t)y[3] << 32) | y[2]);
+    return u32x4{((uint32_t)s01 & m) | mag.mag, ((uint32_t)(s01 >> 32) & m) | mag.mag,
+                 ((uint32_t)s23 & m) | mag.mag, ((uint32_t)(s23 >> 32) & m) | mag.mag};
+  }
+}
 // ---------------------------------------------------------------------------
 // Exact dequantisation of one pair to RNE_dtype((q - z) * s).
 //   fp16: (base + q) - (base + z) is the exact integer q - z (for e odd,
@@ -144,8 +176,8 @@ __device__ __forceinline__ ColBF16 make_col(BF16, uint32_t s_bits, uint32_t z) {
 }
 
 template <int E>
-__device__ __forceinline__ uint32_t exact_pair(F16, uint32_t y, const DqRegs& mag, const ColF16& c) {
-  f16x2 h = __builtin_bit_cast(f16x2, magic_pair<F16, E>(y, mag));
+__device__ __forceinline__ uint32_t exact_from_magic(F16, uint32_t mg, const ColF16& c) {
+  f16x2 h = __builtin_bit_cast(f16x2, mg);
   if constexpr (E & 1) {
     const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
     h = __builtin_elementwise_fma(h, sixteenth, -c.bias);
@@ -158,8 +190,8 @@ __device__ __forceinline__ uint32_t exact_pair(F16, uint32_t y, const DqRegs& ma
 // fp16 pair of column e as the exact integer q - z (no scale): the prefill
 // operand when the scale is applied to fp32 sums instead.
 template <int E>
-__device__ __forceinline__ uint32_t int_pair(uint32_t y, const DqRegs& mag, f16x2 bias) {
-  f16x2 h = __builtin_bit_cast(f16x2, magic_pair<F16, E>(y, mag));
+__device__ __forceinline__ uint32_t int_from_magic(uint32_t mg, f16x2 bias) {
+  f16x2 h = __builtin_bit_cast(f16x2, mg);
   if constexpr (E & 1) {
     const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
     h = __builtin_elementwise_fma(h, sixteenth, -bias);
@@ -174,8 +206,9 @@ template <int E>
 __device__ __forceinline__ u32x4 int_op(const uint32_t* y, const DqRegs& mag, uint32_t z) {
   const uint32_t b = (E & 1) ? (0x5400u | (z << 4)) : (0x6400u | z);
   const f16x2 bias = __builtin_bit_cast(f16x2, b * 0x10001u);
-  return u32x4{int_pair<E>(y[0], mag, bias), int_pair<E>(y[1], mag, bias),
-               int_pair<E>(y[2], mag, bias), int_pair<E>(y[3], mag, bias)};
+  const u32x4 m = magic_op<F16, E, false>(y, mag);
+  return u32x4{int_from_magic<E>(m[0], bias), int_from_magic<E>(m[1], bias),
+               int_from_magic<E>(m[2], bias), int_from_magic<E>(m[3], bias)};
 }
 // fp16 operand RNE((q - z) * s) of column e: the exact integer q - z (as in
 // int_op) times the scale in one packed multiply, which rounds once. Same
@@ -187,21 +220,26 @@ __device__ __forceinline__ u32x4 tile_op(const uint32_t* y, const DqRegs& mag, u
   const uint32_t b = (E & 1) ? (0x5400u | (z << 4)) : (0x6400u | z);
   const f16x2 bias = __builtin_bit_cast(f16x2, b * 0x10001u);
   const f16x2 sc = __builtin_bit_cast(f16x2, (s_bits & 0xFFFFu) * 0x10001u);
+  const u32x4 m = magic_op<F16, E>(y, mag);
   u32x4 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, int_pair<E>(y[i], mag, bias)) * sc);
+    r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, int_from_magic<E>(m[i], bias)) * sc);
   return r;
 }
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 template <int E>
-__device__ __forceinline__ uint32_t exact_pair(BF16, uint32_t y, const DqRegs& mag, const ColBF16& c) {
-  const uint32_t p = magic_pair<BF16, E>(y, mag);
+__device__ __forceinline__ uint32_t exact_from_magic(BF16, uint32_t p, const ColBF16& c) {
   const f32x2 v = {__builtin_fmaf(__builtin_bit_cast(float, p << 16), c.scale, c.c),
                    __builtin_fmaf(__builtin_bit_cast(float, p & 0xFFFF0000u), c.scale, c.c)};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));  // one RNE each
+}
+template <int E, typename T>
+__device__ __forceinline__ uint32_t exact_pair(T, uint32_t y, const DqRegs& mag,
+                                               const typename Col<T>::type& c) {
+  return exact_from_magic<E>(T{}, magic_pair<T, E>(y, mag), c);
 }
 
 __device__ __forceinline__ uint32_t nib(uint32_t w, int j) { return (w >> (4 * j)) & 0xFu; }
@@ -256,16 +294,12 @@ enum { kSit = 0, kOneGrp = 1, kMulti = 2 };
 constexpr int kRing = 4;
 
 template <typename T, int E>
-__device__ __forceinline__ u32x4 magic_op(const uint32_t* y, const DqRegs& mag) {
-  return u32x4{magic_pair<T, E>(y[0], mag), magic_pair<T, E>(y[1], mag),
-               magic_pair<T, E>(y[2], mag), magic_pair<T, E>(y[3], mag)};
-}
-template <typename T, int E>
 __device__ __forceinline__ u32x4 exact_op(const uint32_t* y, const DqRegs& mag, uint32_t s_bits,
                                           uint32_t z) {
   const auto cc = make_col<E>(T{}, s_bits, z);
-  return u32x4{exact_pair<E>(T{}, y[0], mag, cc), exact_pair<E>(T{}, y[1], mag, cc),
-               exact_pair<E>(T{}, y[2], mag, cc), exact_pair<E>(T{}, y[3], mag, cc)};
+  const u32x4 m = magic_op<T, E, false>(y, mag);
+  return u32x4{exact_from_magic<E>(T{}, m[0], cc), exact_from_magic<E>(T{}, m[1], cc),
+               exact_from_magic<E>(T{}, m[2], cc), exact_from_magic<E>(T{}, m[3], cc)};
 }
 
 __device__ __forceinline__ uint32_t half_of(const u32x4 (&sv)[2], int t) {
