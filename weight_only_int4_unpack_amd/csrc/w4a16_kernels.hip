@@ -761,6 +761,21 @@ __device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voff, 
                : "v"(voff), "s"(scalar_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds)), "n"(OFF)
                : "memory", "scc");
 }
+// Two 1 KB blocks with one m0: the instruction offset moves the global and
+// the LDS address alike, so the first block goes at m0 - 1024 (its lane
+// offset passed plus 1024, never below zero) and the second at m0.
+template <int OFF>
+__device__ __forceinline__ void copy16x2_to_lds(const void* sbase, uint32_t voff0p, uint32_t voff1,
+                                                uint32_t lds) {
+  static_assert(OFF >= 0 && OFF + 1024 < (1 << 20), "LDS offset");
+  asm volatile(
+      "s_add_u32 m0, %3, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2 offset:-1024\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "v"(voff0p), "v"(voff1), "s"(scalar_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds)),
+        "n"(OFF + 1024)
+      : "memory", "scc");
+}
 // 4 bytes per lane from the lane's own address
 template <int OFF>
 __device__ __forceinline__ void copy4_to_lds_lane(const void* src, uint32_t lds) {
@@ -992,11 +1007,12 @@ __global__ __launch_bounds__(kPrefillThreads, (BM == 64 || RING) ? 2 : 3) void p
     const uint32_t wb = ring_lds + 2 * wv * 1024;                  // weight blocks
     const uint32_t waux = ring_lds + wv * kAuxB;                   // and scale/zero/sum block
     const char* ab = (const char*)p.a + ((int64_t)m0 * p.K + (int64_t)kt * kPrefillBK) * 2;
-    copy16_to_lds<SO>(ab, a_dma[0], wa);
-    if constexpr (kABlk == 2) copy16_to_lds<SO + 1024>(ab, a_dma[1], wa);
+    if constexpr (kABlk == 2)
+      copy16x2_to_lds<SO>(ab, a_dma[0] + 1024u, a_dma[1], wa);
+    else
+      copy16_to_lds<SO>(ab, a_dma[0], wa);
     const char* bb = (const char*)p.bq + (int64_t)kt * kPrefillBK * (p.N / 2) + tn * (kPrefillBN / 2);
-    copy16_to_lds<SO + kBOff>(bb, b_dma[0], wb);
-    copy16_to_lds<SO + kBOff + 1024>(bb, b_dma[1], wb);
+    copy16x2_to_lds<SO + kBOff>(bb, b_dma[0] + 1024u, b_dma[1], wb);
     const int grp = GS == 0 ? 0 : ((kt * kPrefillBK) >> p.g_shift);  // the stage's first group
     copy4_to_lds_lane<SO + kAuxOff>(aux_src + (uint64_t)grp * aux_step, waux);
     if constexpr (kAux2)
