@@ -266,7 +266,7 @@ __device__ __forceinline__ uint32_t join_rows(uint32_t w0, uint32_t w1, int h) {
 // ---------------------------------------------------------------------------
 // Decode: M <= 16. A workgroup owns 256 output columns and a contiguous range
 // of 4L steps of 32 K-rows; each of its 4 wavefronts streams L of them
-// through a ring of D = min(L, 4) register slots: the loads of D steps are in
+// through a ring of D = min(L, 2) register slots: the loads of D steps are in
 // flight from the start, and each slot is refilled with step j + D as soon as
 // step j has been consumed. Lane (g, c) loads, per step, rows 8g..8g+7 of
 // words 2c, 2c+1 of the block (16 columns) and feeds 16 MFMAs (column offset
@@ -291,7 +291,12 @@ __device__ __forceinline__ uint32_t join_rows(uint32_t w0, uint32_t w1, int h) {
 // sit dirty in a per-XCD L2, and they are read back with agent-scope loads.
 // ---------------------------------------------------------------------------
 enum { kSit = 0, kOneGrp = 1, kMulti = 2 };
-constexpr int kRing = 4;
+// Two slots: with four, a CU's oldest wavefronts (served first) drew all
+// their data before the next ones got any, so the last workgroup's steps all
+// arrived at the end and were computed one after another; with two, each
+// wavefront's later steps are requested as its earlier ones are consumed
+// (decode 5120 x 17408 bf16: M = 1 13.02 -> 12.78 us, M = 5 14.38 -> 14.18 us).
+constexpr int kRing = 2;
 
 template <typename T, int E>
 __device__ __forceinline__ u32x4 exact_op(const uint32_t* y, const DqRegs& mag, uint32_t s_bits,
