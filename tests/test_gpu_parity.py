@@ -35,7 +35,7 @@ def _routes(M):
     selector's choice, the prefill kernel, and every decode mode."""
     out = [("auto", lambda p: None), ("prefill", lambda p: _plan(p, W.ROUTE_PREFILL))]
     if 1 <= M <= 16:
-        def big(p):   # the fast layout takes 1, 2 or 4 steps per wavefront
+        def big(p):   # the fast layout takes 1, 2, 4 or 8 steps per wavefront
             return 4 if (p.N % 16 == 0 and p.K % 8 == 0) else 1
 
         def sit(p):   # the rounded-weight operand (mode 0) is fp16 only
@@ -474,6 +474,21 @@ def test_edge_shapes(M, K, N, G, dtype, zp):
     for label, mk in _routes(M):
         got = dev_to_bits(p.gpu_gemm(plan=mk(p)))
         assert_within_tolerance(got, want, dtype, f"{label}")
+
+
+# eight 32-row steps per wavefront: the two register slots of the decode's
+# ring are refilled six times; every operand mode that takes it, a K split of
+# two, N = 4 x 256 + 32 (a ragged last column block)
+@pytest.mark.parametrize("M,dtype,G,zp,mode", [(5, "bf16", 128, True, 2), (1, "fp16", 64, True, 2),
+                                               (16, "fp16", 32, True, 0), (8, "bf16", 2048, False, 1),
+                                               (3, "fp16", 2048, True, 1)])
+def test_decode_eight_steps(M, dtype, G, zp, mode):
+    K, N = 2048, 1056
+    p = random_problem(M, K, N, G, dtype, zp, seed=880 + G + mode + M)
+    plan = _plan(p, W.ROUTE_DECODE, L=8, mode=mode)
+    assert (plan.steps_per_wave, plan.splits, plan.decode_mode) == (8, 2, mode)
+    got = dev_to_bits(p.gpu_gemm(plan=plan))
+    assert_within_tolerance(got, p.oracle_gemm(), dtype, f"L=8 mode={mode} G={G}")
 
 
 def test_decode_every_m_up_to_16():
