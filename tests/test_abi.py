@@ -158,9 +158,9 @@ def test_gemm_bias_checks():
 def test_group_64_is_kept_not_substituted():
     # both routes plan groups of 64 as given (the decode route with its exact
     # one-fold operand, as the group holds a wavefront's two steps)
-    assert W.plan(8, 2112, 5120, 64, True, torch.float16).route == W.ROUTE_PREFILL
-    p = W.plan(8, 2112, 5120, 64, True, torch.float16, route=W.ROUTE_DECODE)
-    assert p.route == W.ROUTE_DECODE and p.decode_mode == 1
+    p = W.plan(8, 2112, 5120, 64, True, torch.float16)
+    assert p.route == W.ROUTE_DECODE and p.decode_mode == 1 and p.steps_per_wave == 2
+    assert W.plan(8, 2112, 5120, 64, True, torch.float16, route=W.ROUTE_PREFILL).route == W.ROUTE_PREFILL
     # a non-multiple K for G=64 is an error, never a fallback to another G
     assert _gemm(M=8, K=2100, N=5120, G=64) == W.ERR_SHAPE
 
@@ -200,28 +200,41 @@ def test_python_wrapper_validates_shapes():
 # ------------------------------------------------------------ selector
 def test_selector_routes_on_runtime_m():
     D, P = W.ROUTE_DECODE, W.ROUTE_PREFILL
-    # fp16 groups of 32, N <= 8192: decode for one row, the ring prefill's
-    # K split (32-row tiles) from two rows on
-    assert W.plan(1, 4096, 4096, 32, True, torch.float16).route == D
-    for M in (2, 4, 5, 6, 8, 9, 16, 17, 64, 256, 2048, 4096):
+    # K = N = 4096, fp16 groups of 32: decode up to 8 rows, one step per
+    # wavefront inside its group (mode 1, 32 splits); the prefill above
+    for M in (1, 2, 4, 5, 6, 8):
+        p = W.plan(M, 4096, 4096, 32, True, torch.float16)
+        assert (p.route, p.steps_per_wave, p.decode_mode, p.splits) == (D, 1, 1, 32), M
+    for M in (9, 16, 17, 64, 256, 2048, 4096):
         assert W.plan(M, 4096, 4096, 32, True, torch.float16).route == P
     assert W.plan(0, 4096, 4096, 32, True, torch.float16).route == W.ROUTE_NONE
-    # other groups: decode below 4 rows, prefill from 4 rows with >= 8M weights
-    for M, route in ((1, D), (2, D), (3, D), (4, P), (8, P), (9, P)):
+    # K = N = 8192, fp16 groups of 32: mode 1 would take 64 splits, allowed at
+    # one row only; from two rows the ring prefill's K split (N <= 8192)
+    p = W.plan(1, 8192, 8192, 32, True, torch.float16)
+    assert (p.route, p.decode_mode, p.splits) == (D, 1, 64)
+    for M in (2, 4, 8):
+        assert W.plan(M, 8192, 8192, 32, True, torch.float16).route == P
+    # ... but wide N keeps the decode, with the rounded weights (mode 0)
+    p = W.plan(5, 5120, 17408, 32, True, torch.float16)
+    assert (p.route, p.decode_mode, p.steps_per_wave) == (D, 0, 4)
+    # groups of 128: decode up to 8 rows, prefill from 9
+    for M, route in ((1, D), (2, D), (4, D), (8, D), (9, P)):
         assert W.plan(M, 4096, 4096, 128, False, torch.bfloat16).route == route, M
-    # small weights (K = N = 2048) and wide N (14336, 17408) stay on decode
+    assert W.plan(4, 8192, 4096, 128, False, torch.bfloat16).route == D
     assert W.plan(4, 2048, 2048, 128, False, torch.bfloat16).route == D
     assert W.plan(4, 4096, 14336, 128, False, torch.bfloat16).route == D
     assert W.plan(8, 5120, 17408, 128, False, torch.bfloat16).route == D
     # K % 64 != 0 or N % 32 != 0 (no ring): decode up to 8 rows
     assert W.plan(8, 4160 - 32, 4096, 4128, True, torch.float16).route == D
     assert W.plan(8, 4096, 4104, 128, True, torch.float16).route == D
-    # per-channel scales: the decode route up to 16 rows where the prefill
-    # ring does not win (here: wide N), with fewer splits above 8 rows
+    # per-channel scales: the decode route up to 16 rows, with fewer splits
+    # above 8 rows
     for M in (9, 12, 16):
-        p = W.plan(M, 4096, 14336, 4096, True, torch.float16)
-        assert p.route == D and p.decode_mode == 1
-        assert W.plan(M, 4096, 4096, 4096, True, torch.float16).route == P
+        for N in (14336, 4096):
+            p = W.plan(M, 4096, N, 4096, True, torch.float16)
+            assert p.route == D and p.decode_mode == 1
+    assert W.plan(8, 4096, 4096, 4096, True, torch.float16).steps_per_wave == 2
+    assert W.plan(16, 4096, 4096, 4096, True, torch.float16).steps_per_wave == 4
     assert W.plan(17, 4096, 14336, 4096, True, torch.float16).route == P
 
 
@@ -243,8 +256,8 @@ def test_selector_decode_shapes():
     assert p.splits * 4 * p.steps_per_wave >= 66
     assert p.steps_per_wave == 2 and p.decode_mode == 1
     # fp16 groups of 32 with 2 steps per wavefront: the rounded weight (mode 0)
-    q = W.plan(1, 4096, 4096, 32, True, torch.float16)
-    assert q.steps_per_wave == 2 and q.decode_mode == 0
+    q = W.plan(1, 4096, 4096, 32, True, torch.float16, route=W.ROUTE_DECODE, steps_per_wave=2)
+    assert q.decode_mode == 0
     assert p.workspace_bytes >= p.splits * 8 * 5120 * 4 or p.splits == 1
     # partials of 4 wavefronts, then scales and packed zeros of the staged groups
     ng = 4 * p.steps_per_wave // 2 + 1

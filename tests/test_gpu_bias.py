@@ -24,7 +24,7 @@ CASES = [
     (4, 256, 512, 128, "fp16", False, W.ROUTE_DECODE, False),     # decode, one split
     (1, 4096, 4096, 32, "fp16", True, W.ROUTE_DECODE, True),      # decode, last-arrival sum
     (5, 4096, 4104, 32, "bf16", True, W.ROUTE_DECODE, True),      # N % 32 != 0: no ring
-    (5, 4096, 4096, 32, "bf16", True, W.ROUTE_PREFILL, True),     # few rows: ring, K split
+    (9, 4096, 4096, 32, "bf16", True, W.ROUTE_PREFILL, True),     # few rows: ring, K split
     (8, 2112, 520, 64, "fp16", True, W.ROUTE_DECODE, True),       # ragged N
     (2000, 256, 4104, 64, "fp16", True, W.ROUTE_PREFILL, False),  # prefill, ragged N and M
     (300, 512, 264, 32, "fp16", False, W.ROUTE_PREFILL, True),    # prefill split, ragged N

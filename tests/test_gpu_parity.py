@@ -491,6 +491,28 @@ def test_decode_eight_steps(M, dtype, G, zp, mode):
     assert_within_tolerance(got, p.oracle_gemm(), dtype, f"L=8 mode={mode} G={G}")
 
 
+# The arrival counters of the split decode sit as far apart as the counter
+# region allows (one per 128-byte line for up to 64 column blocks, closer
+# for more), and each launch leaves its counters zero for the next. Split
+# launches with 8, 1024 and 68 column blocks (slots 32, 4 and 32 apart) on
+# one stream share the library's workspace; the first shape runs again at
+# the end, so a counter left nonzero anywhere would cut a hand-off short.
+def test_decode_counter_slots_reused_across_strides():
+    cases = [(3, 1024, 2048, 128, "fp16", True, 1, 1),     # 8 column blocks
+             (1, 256, 262144, 128, "bf16", False, 1, 1),   # 1024 column blocks
+             (5, 1024, 17408, 128, "bf16", False, 2, 1)]   # 68 column blocks
+    probs = []
+    for i, (M, K, N, G, dtype, zp, L, mode) in enumerate(cases):
+        p = random_problem(M, K, N, G, dtype, zp, seed=890 + i)
+        plan = _plan(p, W.ROUTE_DECODE, L=L, mode=mode)
+        assert plan.splits > 1, plan.as_dict()
+        cols = np.unique(np.r_[0:64, N - 64:N, np.random.default_rng(i).integers(0, N, 256)])
+        probs.append((p, plan, cols, p.oracle_gemm(cols=cols)))
+    for p, plan, cols, want in probs + probs[:1]:
+        got = dev_to_bits(p.gpu_gemm(plan=plan))[:, cols]
+        assert_within_tolerance(got, want, p.dtype, f"N={p.N} splits={plan.splits}")
+
+
 def test_decode_every_m_up_to_16():
     p16 = random_problem(16, 1024, 1024, 128, "bf16", False, seed=21)
     for M in range(1, 17):

@@ -100,6 +100,108 @@ int decode_ng_max(int64_t K, int32_t G, int64_t L) {
   return (int)std::max<int64_t>(1, (kDecodeWaves * L) / SG + 1);
 }
 
+// Arrival counters of a split decode: one per (column block, wavefront),
+// spread over the counter region as far apart as it allows, up to one per
+// 128-byte line, so that the atomics on different counters do not queue on
+// one line. Packed four to a line, the counter atomics of K = N = 4096 fp16
+// G = 32 at M = 5 (2048 arrivals on 64 counters) took 3-4 us to return and
+// the launch 14.0 us; spread, 9.6 us (M = 1, one step per wavefront: 8.7 ->
+// 7.4 us).
+int32_t decode_counter_stride(int64_t NB) {
+  using namespace w4a16;
+  const int64_t slots = kCounterBytes / (int64_t)sizeof(int32_t);
+  int32_t cs = 1;
+  while (2 * cs <= kCounterStrideMax && 2 * cs * NB * kDecodeWaves <= slots) cs *= 2;
+  return cs;
+}
+
+// Steps per wavefront (L) of a decode launch when the caller leaves them
+// open; *one_group tells whether the choice keeps each wavefront's steps
+// inside one group (mode 1). mode_forced < 0: any mode.
+//
+// Mode 1 comes first: it loads its scales straight into registers and folds
+// once, where modes 0 and 2 stage the workgroup's scales in LDS behind a
+// barrier that waits for the stream's first loads. Its candidates are the L
+// whose steps fit in one group and whose K split count S stays at most 64
+// at one row, 32 above (each split adds partials that the last arrival
+// loads). Among them: the L whose grid is resident at once (3 wavefronts
+// per SIMD, fewer if LDS says so) and whose workgroup count is closest, by
+// ratio, to max(column blocks, min(CUs, weight bytes / 32 KiB)); with none
+// resident, the longest. Without a mode 1 candidate: the resident L closest
+// to max(column blocks, weight bytes / 32 KiB), else 8. Ties go to the
+// smaller L. Measured on MI355X (graph-replayed, weights rotated), chosen
+// plan against the next best: K=N=4096 fp16 G=32 M=1 L=1 7.4 us (L=2, mode
+// 0: 8.3), M=5 9.3 (9.6); K=8192, N=4096 bf16 G=128 M=4 L=4 8.8 (L=2: 9.7);
+// K=N=16384 fp16 G=128 M=1 L=4 31.1 (L=8, mode 2: 34.3); K=5120, N=17408
+// bf16 G=64 M=5 L=2 17.2 (L=4, mode 2: 20.7); K=5120, N=17408 fp16 G=32
+// M=5 L=4, mode 0, 21.1 (L=1, 40 splits: 24.9).
+int64_t decode_auto_steps(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype, int num_cus,
+                          int32_t mode_forced, bool* one_group_out) {
+  using namespace w4a16;
+  const int64_t KS = ceil_div(K, kStepRows);
+  const int64_t NB = ceil_div(N, kDecodeCols);
+  const int64_t SG = ((int64_t)G == K) ? KS : G / kStepRows;
+  const bool one_group = ((int64_t)G == K);
+  const bool aligned = (N % 16 == 0) && (K % 8 == 0);
+  auto fits_one_of = [&](int64_t l) { return one_group || (SG >= l && SG % l == 0); };
+  *one_group_out = fits_one_of(1);
+  if (!aligned) return 1;  // off the fast layout: one step per wavefront
+  const double bytes = (double)K * (double)N / 2.0;
+  // above 8 rows each split's hand-off carries twice the partials: aim at
+  // half the workgroups (K = N = 4096, per-channel, M = 16: 4 steps per
+  // wavefront, 10.2 us, against 11.3 us with 2)
+  const double halve = M > w4a16::kAutoDecodeMaxM ? 2.0 : 1.0;
+  auto resident = [&](int64_t l, int m) {
+    const int64_t lds = decode_lds_bytes((int)M, decode_ng_max(K, G, (int)l));
+    const int64_t by_lds = std::max<int64_t>(1, kLdsPerCu / std::max<int64_t>(1, lds));
+    const int64_t per_simd = std::min<int64_t>(m == 2 ? 2 : 3, by_lds);
+    return ceil_div(KS, l) * NB <= per_simd * 4 * (int64_t)num_cus;
+  };
+  auto closest = [&](auto&& take, double target, int64_t& L) {
+    double best = 1e300;
+    bool any = false;
+    for (int64_t l = 1; l <= kDecodeMaxSteps; l *= 2) {
+      if (!take(l)) continue;
+      const double grid = (double)(ceil_div(KS, kDecodeWaves * l) * NB);
+      const double d = std::fabs(std::log(grid / target));
+      if (d < best - 1e-9) {
+        best = d;
+        L = l;
+        any = true;
+      }
+    }
+    return any;
+  };
+  if (mode_forced < 0 || mode_forced == 1) {
+    const int64_t smax = M == 1 ? 64 : 32;
+    auto cand = [&](int64_t l) {
+      return fits_one_of(l) && (mode_forced == 1 || ceil_div(KS, kDecodeWaves * l) <= smax);
+    };
+    int64_t L = 0;
+    for (int64_t l = 1; l <= kDecodeMaxSteps; l *= 2)
+      if (cand(l)) L = l;  // the longest candidate
+    if (L > 0) {
+      *one_group_out = true;
+      const double target = std::max<double>((double)NB, std::min<double>((double)num_cus,
+                                                                          bytes / 32768.0)) / halve;
+      closest([&](int64_t l) { return cand(l) && resident(l, 1); }, target, L);
+      return L;
+    }
+  }
+  *one_group_out = false;
+  auto mode_of = [&](int64_t l) {
+    if (mode_forced >= 0) return (int)mode_forced;
+    if (fits_one_of(l)) return 1;
+    return (dtype == W4A16_F16 && G <= 64) ? 0 : 2;
+  };
+  int64_t L = kDecodeMaxSteps;  // nothing resident: longest streams
+  const double target = std::max<double>((double)NB, bytes / 32768.0) / halve;
+  closest([&](int64_t l) { return (mode_of(l) != 1 || fits_one_of(l)) && resident(l, mode_of(l)); },
+          target, L);
+  *one_group_out = fits_one_of(L) && mode_of(L) == 1;
+  return L;
+}
+
 w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype, int num_cus,
                          int32_t L_forced, int32_t mode_forced, w4a16_plan_t* pl) {
   using namespace w4a16;
@@ -126,41 +228,8 @@ w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dty
     return (dtype == W4A16_F16 && G <= 64) ? 0 : 2;
   };
   if (L == 0) {
-    // Among the L whose whole grid is resident at once (wavefronts per SIMD:
-    // 3 for the modes with one accumulator set, <= 168 VGPRs; 2 for kMulti;
-    // fewer if LDS says so), take the one whose workgroup count is closest,
-    // by ratio, to max(NB, weight bytes / 32 KiB): large problems want many
-    // short streams for bandwidth, small ones few K-splits, since each split
-    // adds a cross-workgroup hand-off to the critical path. Ties go to the
-    // smaller L. (Measured on MI355X: 4 steps at 5120 x 17408, 2 at
-    // 2112 x 5120 and 4096 x 4096, no split for the 256 x 512 tiny shape.)
-    L = 1;
-    if (aligned) {
-      const double bytes = (double)K * (double)N / 2.0;
-      // above 8 rows each split's hand-off carries twice the partials: aim at
-      // half the workgroups (K = N = 4096, M = 16: 4 steps per wavefront,
-      // 8 splits, 16.2 us, against 17.2 us with 2 steps and 16 splits)
-      const double target = std::max<double>((double)NB, bytes / 32768.0) /
-                            (M > w4a16::kAutoDecodeMaxM ? 2.0 : 1.0);
-      double best = 1e300;
-      bool any = false;
-      for (int64_t l = 1; l <= kDecodeMaxSteps; l *= 2) {
-        const int m = mode_forced >= 0 ? mode_forced : auto_mode(l);
-        if (m == 1 && !fits_one_of(l)) continue;
-        const int64_t lds = decode_lds_bytes((int)M, decode_ng_max(K, G, (int)l));
-        const int64_t by_lds = std::max<int64_t>(1, kLdsPerCu / std::max<int64_t>(1, lds));
-        const int64_t per_simd = std::min<int64_t>(m == 2 ? 2 : 3, by_lds);
-        const int64_t grid = ceil_div(KS, kDecodeWaves * l) * NB;
-        if (ceil_div(KS, l) * NB > per_simd * 4 * (int64_t)num_cus) continue;  // not resident
-        const double d = std::fabs(std::log((double)grid / target));
-        if (d < best - 1e-9) {
-          best = d;
-          L = l;
-          any = true;
-        }
-      }
-      if (!any) L = kDecodeMaxSteps;  // nothing resident: longest streams
-    }
+    bool in_one = false;
+    L = decode_auto_steps(M, K, N, G, dtype, num_cus, mode_forced, &in_one);
   }
   int32_t mode = mode_forced;
   const bool fits_one = fits_one_of(L);
@@ -292,26 +361,26 @@ w4a16_status make_plan(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype
     return W4A16_OK;
   }
   // Decode for M <= 8 and per-channel scales (one group) up to 16 rows,
-  // unless the prefill route's K split through the LDS ring (32-row tiles)
-  // is faster: with few column tiles (N <= 8192) it wins from 2 rows on for
-  // fp16 with groups of 32 (the decode kernel then feeds rounded weights)
-  // and from 4 rows on with 8M weights or more; it loses at one row, for
-  // wide N (its few splits stream too slowly) and for small weights.
-  // Measured graph-replayed, decode -> prefill: K = N = 4096 fp16 G = 32,
-  // M = 2 10.5 -> 9.9, M = 5 14.1 -> 9.8 us; K = 2112, N = 5120 fp16 G = 64,
-  // M = 8 9.4 -> 8.6 us; K = 8192, N = 4096 bf16 G = 128, M = 4 17.6 -> 11.6
-  // us; per-channel K = N = 4096, M = 16 12.1 -> 10.5 us; kept on decode:
-  // K = 5120, N = 17408 bf16 M = 8 16.4 vs 21.8 us, K = 4096, N = 14336
-  // M = 4 12.3 vs 18.1 us, M = 1 everywhere but the largest fp16 G = 32
-  // shapes, K = N = 2048 bf16 M = 4 7.0 vs 7.7 us. (N beyond what the
+  // except where from 2 rows on, with few column tiles (N <= 8192), the
+  // decode cannot keep each wavefront's steps inside one group at few enough
+  // K splits (mode 1, above): there the prefill route's K split through the
+  // LDS ring (32-row tiles) is faster. Measured graph-replayed on MI355X,
+  // decode against prefill: K = N = 4096 fp16 G = 32 M = 2 7.6 vs 9.5, M = 5
+  // 9.3 vs 9.6 us; K = 2112, N = 5120 fp16 G = 64 M = 8 7.6 vs 8.5; K = 8192,
+  // N = 4096 bf16 G = 128 M = 4 8.8 vs 11.2; per-channel K = N = 4096 M = 16
+  // 10.2 vs 10.7; K = N = 8192 bf16 G = 128 M = 8 14.6 vs 15.0; sent to the
+  // prefill: K = N = 8192 fp16 G = 32 M = 4 (64 splits for mode 1) 16.5
+  // against 17.1 (mode 1) and 18+ (mode 0, 4 steps). (N beyond what the
   // counter region serves, 2^20 columns, has column blocks enough to fill
   // the GPU on the prefill route's tiles.)
   if (route == 0) {
     bool decode = (M <= w4a16::kAutoDecodeMaxM || (M <= w4a16::kDecodeMaxM && (int64_t)G == K)) &&
                   ceil_div(N, w4a16::kDecodeCols) <= w4a16::kMaxCounterBlocks;
-    if (decode && w4a16::prefill_ring_ok(K, N, 32) && N <= 8192 &&
-        ((dtype == W4A16_F16 && G == 32 && M >= 2) || (M >= 4 && K * N >= (8ll << 20))))
-      decode = false;
+    if (decode && M >= 2 && N <= 8192 && w4a16::prefill_ring_ok(K, N, 32)) {
+      bool in_one = false;
+      decode_auto_steps(M, K, N, G, dtype, num_cus, -1, &in_one);
+      if (!in_one) decode = false;
+    }
     route = decode ? W4A16_ROUTE_DECODE : W4A16_ROUTE_PREFILL;
   }
   if (route == W4A16_ROUTE_DECODE) {
@@ -459,6 +528,7 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, void* ws, hip
     if (pl.splits > 1) {
       p.ws = partials;
       p.counters = counters;
+      p.cstride = decode_counter_stride(p.NB);
     }
     e = launch_decode(p, g.dtype, g.qzeros != nullptr, pl.decode_mode, pl.grid, pl.lds_bytes,
                       stream);

@@ -40,6 +40,8 @@ constexpr int64_t kLdsPerCu = 160 * 1024;  // gfx950 LDS per CU
 constexpr int64_t kCounterBytes = W4A16_WORKSPACE_COUNTER_BYTES;
 // decode column blocks the region serves: one int32 counter per wavefront each
 constexpr int64_t kMaxCounterBlocks = kCounterBytes / (kDecodeWaves * (int64_t)sizeof(int32_t));
+// most int32 slots between consecutive counters (one counter per 128 B line)
+constexpr int32_t kCounterStrideMax = 32;
 // the fixed device array of the entry point that allocates nothing
 constexpr int64_t kStaticPartialBytes = 32ll << 20;
 constexpr int64_t kStaticScratchBytes = kCounterBytes + kStaticPartialBytes;
@@ -136,7 +138,8 @@ struct DecodeParams {
   const uint16_t* bias;  // nullable [N]
   uint16_t* out;
   float* ws;          // [S, M, N] fp32 partials (S > 1)
-  int32_t* counters;  // [NB][4] arrival counters per wavefront, zero between launches
+  int32_t* counters;  // [NB][4] arrival counters per wavefront, zero between launches,
+                      // cstride int32 apart
   int32_t M, K, N, G, zp_bias;
   int32_t KS;         // K steps of 32 rows
   int32_t SG;         // steps per group
@@ -145,6 +148,7 @@ struct DecodeParams {
   int32_t L;          // steps per wavefront
   int32_t S;          // splits across workgroups
   int32_t NB;         // column blocks
+  int32_t cstride;    // int32 slots from one arrival counter to the next
 };
 
 struct PrefillParams {

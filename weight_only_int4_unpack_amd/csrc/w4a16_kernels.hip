@@ -654,7 +654,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
   // 15 -> 84 us at M = 5, for no change in what this code relies on.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  int32_t* counter = p.counters + b * kDecodeWaves + wv;
+  int32_t* counter = p.counters + (b * kDecodeWaves + wv) * p.cstride;
   int prev = 0;
   if (lane == 0)
     prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
