@@ -217,9 +217,18 @@ def test_selector_routes_on_runtime_m():
     # ... but wide N keeps the decode, with the rounded weights (mode 0)
     p = W.plan(5, 5120, 17408, 32, True, torch.float16)
     assert (p.route, p.decode_mode, p.steps_per_wave) == (D, 0, 4)
-    # groups of 128: decode up to 8 rows, prefill from 9
-    for M, route in ((1, D), (2, D), (4, D), (8, D), (9, P)):
+    # groups of 128: 4 steps of a wavefront inside one group, so the decode
+    # up to 16 rows (few splits), the prefill above
+    for M, route in ((1, D), (2, D), (4, D), (8, D), (9, D), (16, D), (17, P)):
         assert W.plan(M, 4096, 4096, 128, False, torch.bfloat16).route == route, M
+    p = W.plan(16, 4096, 4096, 128, False, torch.bfloat16)
+    assert (p.steps_per_wave, p.splits, p.decode_mode) == (4, 8, 1)
+    # ... unless above 8 rows the splits would exceed 16 (K = 14336: 28)
+    assert W.plan(8, 14336, 4096, 128, True, torch.float16).route == D
+    assert W.plan(16, 14336, 4096, 128, True, torch.float16).route == P
+    # above 8 rows the workgroup target halves, but not below 64
+    p = W.plan(16, 2048, 2048, 128, False, torch.bfloat16)
+    assert (p.route, p.steps_per_wave, p.grid) == (D, 2, 64)
     assert W.plan(4, 8192, 4096, 128, False, torch.bfloat16).route == D
     assert W.plan(4, 2048, 2048, 128, False, torch.bfloat16).route == D
     assert W.plan(4, 4096, 14336, 128, False, torch.bfloat16).route == D

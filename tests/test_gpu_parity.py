@@ -513,6 +513,31 @@ def test_decode_counter_slots_reused_across_strides():
         assert_within_tolerance(got, want, p.dtype, f"N={p.N} splits={plan.splits}")
 
 
+# The last arrival of a split decode with several rows per wavefront (M >= 5)
+# and at least two windows of splits keeps a sliding window of partial
+# loads in flight, wrapping the surplus split indices of its last window and
+# reading zeros for rows past M. K = 4128 is 129 steps: 33 splits at one
+# step per wavefront, so the last window holds one real split. Every M from
+# 5 to 16 (row blocks of 8 and 16, wavefronts with one and two rows), and
+# exact-integer data for a bitwise check of M = 5, 8, 13; N = 520 (off the
+# fast layout: 16-row blocks at every M) for M = 6.
+@pytest.mark.parametrize("N,Ms", [(512, range(5, 17)), (520, (6,))])
+def test_decode_sliding_partial_window_every_m(N, Ms):
+    K, G = 4128, 32
+    p16 = random_problem(16, K, N, G, "fp16", True, seed=900 + N)
+    for M in Ms:
+        p = make_problem({"a_bits": p16.a_bits[:M], "q": W.unpack_int4(p16.b_q),
+                          "s_bits": p16.s_bits, "z": W.unpack_int4(p16.qz)}, M, K, N, G, "fp16")
+        plan = _plan(p, W.ROUTE_DECODE, L=1)
+        assert plan.splits == 33, plan.as_dict()
+        got = dev_to_bits(p.gpu_gemm(plan=plan))
+        assert_within_tolerance(got, p.oracle_gemm(), "fp16", f"M={M}")
+    for M in ((5, 8, 13) if N == 512 else Ms):
+        q = _exact_problem(M, K, N, G, "fp16", True, seed=910 + M)
+        got = dev_to_bits(q.gpu_gemm(plan=_plan(q, W.ROUTE_DECODE, L=1)))
+        assert np.array_equal(got, q.oracle_gemm()), f"M={M}"
+
+
 def test_decode_every_m_up_to_16():
     p16 = random_problem(16, 1024, 1024, 128, "bf16", False, seed=21)
     for M in range(1, 17):

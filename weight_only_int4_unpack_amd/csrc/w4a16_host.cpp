@@ -116,15 +116,16 @@ int32_t decode_counter_stride(int64_t NB) {
 }
 
 // Steps per wavefront (L) of a decode launch when the caller leaves them
-// open; *one_group tells whether the choice keeps each wavefront's steps
-// inside one group (mode 1). mode_forced < 0: any mode.
+// open; *one_group tells whether the choice came from the mode 1 candidates
+// below (each wavefront's steps inside one group, few splits). mode_forced
+// < 0: any mode.
 //
 // Mode 1 comes first: it loads its scales straight into registers and folds
 // once, where modes 0 and 2 stage the workgroup's scales in LDS behind a
 // barrier that waits for the stream's first loads. Its candidates are the L
 // whose steps fit in one group and whose K split count S stays at most 64
-// at one row, 32 above (each split adds partials that the last arrival
-// loads). Among them: the L whose grid is resident at once (3 wavefronts
+// at one row, 32 up to 8 rows, 16 above (each split adds partials that the
+// last arrival loads). Among them: the L whose grid is resident at once (3 wavefronts
 // per SIMD, fewer if LDS says so) and whose workgroup count is closest, by
 // ratio, to max(column blocks, min(CUs, weight bytes / 32 KiB)); with none
 // resident, the longest. Without a mode 1 candidate: the resident L closest
@@ -148,9 +149,10 @@ int64_t decode_auto_steps(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dt
   if (!aligned) return 1;  // off the fast layout: one step per wavefront
   const double bytes = (double)K * (double)N / 2.0;
   // above 8 rows each split's hand-off carries twice the partials: aim at
-  // half the workgroups (K = N = 4096, per-channel, M = 16: 4 steps per
-  // wavefront, 10.2 us, against 11.3 us with 2)
-  const double halve = M > w4a16::kAutoDecodeMaxM ? 2.0 : 1.0;
+  // half the workgroups, but not below 64 (K = N = 4096, per-channel,
+  // M = 16: 4 steps per wavefront, 10.2 us, against 11.3 us with 2; K = N =
+  // 2048 bf16 G = 128 M = 16: 2 steps, 7.5 us, against 8.1 with 4)
+  auto aim = [&](double t) { return M > w4a16::kAutoDecodeMaxM ? std::max(t / 2.0, 64.0) : t; };
   auto resident = [&](int64_t l, int m) {
     const int64_t lds = decode_lds_bytes((int)M, decode_ng_max(K, G, (int)l));
     const int64_t by_lds = std::max<int64_t>(1, kLdsPerCu / std::max<int64_t>(1, lds));
@@ -173,7 +175,7 @@ int64_t decode_auto_steps(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dt
     return any;
   };
   if (mode_forced < 0 || mode_forced == 1) {
-    const int64_t smax = M == 1 ? 64 : 32;
+    const int64_t smax = M == 1 ? 64 : M <= w4a16::kAutoDecodeMaxM ? 32 : 16;
     auto cand = [&](int64_t l) {
       return fits_one_of(l) && (mode_forced == 1 || ceil_div(KS, kDecodeWaves * l) <= smax);
     };
@@ -182,8 +184,8 @@ int64_t decode_auto_steps(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dt
       if (cand(l)) L = l;  // the longest candidate
     if (L > 0) {
       *one_group_out = true;
-      const double target = std::max<double>((double)NB, std::min<double>((double)num_cus,
-                                                                          bytes / 32768.0)) / halve;
+      const double target = aim(std::max<double>((double)NB, std::min<double>((double)num_cus,
+                                                                             bytes / 32768.0)));
       closest([&](int64_t l) { return cand(l) && resident(l, 1); }, target, L);
       return L;
     }
@@ -195,10 +197,9 @@ int64_t decode_auto_steps(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dt
     return (dtype == W4A16_F16 && G <= 64) ? 0 : 2;
   };
   int64_t L = kDecodeMaxSteps;  // nothing resident: longest streams
-  const double target = std::max<double>((double)NB, bytes / 32768.0) / halve;
+  const double target = aim(std::max<double>((double)NB, bytes / 32768.0));
   closest([&](int64_t l) { return (mode_of(l) != 1 || fits_one_of(l)) && resident(l, mode_of(l)); },
           target, L);
-  *one_group_out = fits_one_of(L) && mode_of(L) == 1;
   return L;
 }
 
@@ -360,8 +361,12 @@ w4a16_status make_plan(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype
     pl->route = W4A16_ROUTE_NONE;
     return W4A16_OK;
   }
-  // Decode for M <= 8 and per-channel scales (one group) up to 16 rows,
-  // except where from 2 rows on, with few column tiles (N <= 8192), the
+  // Decode for M <= 8, and up to 16 rows for per-channel scales (one group)
+  // or where the decode keeps each wavefront's 2 or more steps inside one
+  // group (mode 1, above; M = 16: K = 5120, N = 17408 bf16 G = 128 18.7 vs
+  // 21.3 us, K = 8192, N = 4096 11.2 vs 12.7 us; M = 12, K = 4096, N = 14336
+  // 13.1 vs 17.7 us; groups of 32 stay on the prefill: K = N = 4096 fp16
+  // M = 16 11.3 vs 11.5 us), except where from 2 rows on, with few column tiles (N <= 8192), the
   // decode cannot keep each wavefront's steps inside one group at few enough
   // K splits (mode 1, above): there the prefill route's K split through the
   // LDS ring (32-row tiles) is faster. Measured graph-replayed on MI355X,
@@ -374,13 +379,14 @@ w4a16_status make_plan(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype
   // counter region serves, 2^20 columns, has column blocks enough to fill
   // the GPU on the prefill route's tiles.)
   if (route == 0) {
-    bool decode = (M <= w4a16::kAutoDecodeMaxM || (M <= w4a16::kDecodeMaxM && (int64_t)G == K)) &&
-                  ceil_div(N, w4a16::kDecodeCols) <= w4a16::kMaxCounterBlocks;
-    if (decode && M >= 2 && N <= 8192 && w4a16::prefill_ring_ok(K, N, 32)) {
-      bool in_one = false;
-      decode_auto_steps(M, K, N, G, dtype, num_cus, -1, &in_one);
-      if (!in_one) decode = false;
-    }
+    const bool counters_ok = ceil_div(N, w4a16::kDecodeCols) <= w4a16::kMaxCounterBlocks;
+    bool in_one = false;
+    const int64_t L_auto = M <= w4a16::kDecodeMaxM
+                               ? decode_auto_steps(M, K, N, G, dtype, num_cus, -1, &in_one)
+                               : 0;
+    bool decode = counters_ok && (M <= w4a16::kAutoDecodeMaxM ||
+                                  (M <= w4a16::kDecodeMaxM && ((int64_t)G == K || (in_one && L_auto >= 2))));
+    if (decode && M >= 2 && N <= 8192 && w4a16::prefill_ring_ok(K, N, 32) && !in_one) decode = false;
     route = decode ? W4A16_ROUTE_DECODE : W4A16_ROUTE_PREFILL;
   }
   if (route == W4A16_ROUTE_DECODE) {

@@ -327,6 +327,11 @@ __device__ __forceinline__ void store_wt4(__amdgpu_buffer_rsrc_t r, uint32_t off
 __device__ __forceinline__ f32x4 load_wt4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kSc1));
 }
+// the same with a wave-uniform part of the offset in the scalar operand
+__device__ __forceinline__ f32x4 load_wt4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(f32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kSc1));
+}
 // Four adjacent outputs, rounded to the activation type, in one 8-byte store.
 template <typename T>
 __device__ __forceinline__ void store_out4(T, uint16_t* dst, f32x4 v) {
@@ -353,7 +358,9 @@ struct DecodeSlot {
 };
 
 // MT: M rounded up to 4, 8 or 16 (compile-time row count of the reductions).
-template <typename T, bool HAS_ZP, int MODE, bool ALIGNED, int L, int MT>
+// SLIDE: the last arrival keeps a sliding window of partial loads in flight
+// (several rows, more splits than one window).
+template <typename T, bool HAS_ZP, int MODE, bool ALIGNED, int L, int MT, bool SLIDE>
 __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams p) {
   constexpr int D = L < kRing ? L : kRing;
   extern __shared__ __attribute__((aligned(16))) float red[];
@@ -660,32 +667,84 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
     prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (__builtin_amdgcn_readfirstlane(prev) != p.S - 1) return;
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  // last arrival: add the S partials of each row in split order, up to QB
-  // splits' loads of all the wavefront's rows in flight at once
+  // last arrival: add the S partials of each row in split order, QB splits'
+  // loads of the wavefront's rows in flight (the partial buffer holds S x M
+  // rows of row_bytes; every real load below lies inside it)
   if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   constexpr int QB = RPT <= 2 ? 16 : 4;
+  const int S = p.S;
+  const uint32_t split_bytes = (uint32_t)M * row_bytes;
   f32x4 sum[RPT];
 #pragma unroll
   for (int r = 0; r < RPT; ++r) sum[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int q0 = 0; q0 < p.S; q0 += QB) {
+  if constexpr (!SLIDE) {
+    // windows of QB splits: their loads, then their adds (one round trip
+    // per window)
+    for (int q0 = 0; q0 < S; q0 += QB) {
+      f32x4 tq[QB][RPT];
+#pragma unroll
+      for (int u = 0; u < QB; ++u)
+        if (q0 + u < S) {
+#pragma unroll
+          for (int r = 0; r < RPT; ++r)
+            if (wv + 4 * r < M)
+              tq[u][r] = load_wt4(wsr, (uint32_t)(wv + 4 * r) * row_bytes + lane_off,
+                                  (uint32_t)(q0 + u) * split_bytes);
+        }
+#pragma unroll
+      for (int u = 0; u < QB; ++u)
+        if (q0 + u < S) {
+#pragma unroll
+          for (int r = 0; r < RPT; ++r)
+            if (wv + 4 * r < M) sum[r] += tq[u][r];
+        }
+    }
+  } else {
+    // S >= 2 QB, several rows: a window in flight throughout, a partial's
+    // register slot refilled with the load QB splits ahead as soon as it is
+    // added. Every load is issued without a branch and every loaded value is
+    // consumed, so that the waits count loads in order instead of draining
+    // them; the scheduling barriers keep each add next to its refill. Split
+    // indices past S wrap to q - S (distinct splits already added, in the
+    // scalar offset); a row past M gets a vector offset past the buffer's
+    // end, where the bounds check of buffer loads returns zeros without a
+    // memory access, and its sum is never stored. (With one row the
+    // compiler copies the loaded slots and drains the loads at every window,
+    // so one row keeps the windows above.)
+    static_assert(RPT >= 2, "sliding window: several rows");
+    uint32_t row_off[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+      row_off[r] = wv + 4 * r < M ? (uint32_t)(wv + 4 * r) * row_bytes + lane_off
+                                  : (uint32_t)S * split_bytes;
+    auto split_off = [&](int q) { return (uint32_t)(q < S ? q : q - S) * split_bytes; };
     f32x4 tq[QB][RPT];
 #pragma unroll
-    for (int u = 0; u < QB; ++u) {
-      const int q = q0 + u;
-      if (q < p.S) {
+    for (int u = 0; u < QB; ++u)
 #pragma unroll
-        for (int r = 0; r < RPT; ++r)
-          if (wv + 4 * r < M)
-            tq[u][r] = load_wt4(wsr, (uint32_t)(q * M + wv + 4 * r) * row_bytes + lane_off);
+      for (int r = 0; r < RPT; ++r) tq[u][r] = load_wt4(wsr, row_off[r], split_off(u));
+    int q0 = 0;
+    for (; q0 + QB < S; q0 += QB) {  // windows with another after them: all QB splits real
+#pragma unroll
+      for (int u = 0; u < QB; ++u) {
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+          sum[r] += tq[u][r];
+          tq[u][r] = load_wt4(wsr, row_off[r], split_off(q0 + QB + u));
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
-    for (int u = 0; u < QB; ++u)
-      if (q0 + u < p.S) {
+    for (int u = 0; u < QB; ++u) {  // the last window: splits q0 + u < S
+      const bool real = q0 + u < S;
 #pragma unroll
-        for (int r = 0; r < RPT; ++r)
-          if (wv + 4 * r < M) sum[r] += tq[u][r];
+      for (int r = 0; r < RPT; ++r) {
+        const f32x4 t = sum[r] + tq[u][r];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sum[r][v] = real ? t[v] : sum[r][v];
       }
+    }
   }
   if (col_ok) {
     const f32x4 bv = bias4(T{}, p.bias, col4);
@@ -1696,30 +1755,40 @@ __global__ __launch_bounds__(kKpThreads) void kpacked_kernel(KPackedParams p) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <typename T, bool Z, int MODE, bool AL, int L, int MT>
+template <typename T, bool Z, int MODE, bool AL, int L, int MT, bool SLIDE>
 static hipError_t decode_go(const DecodeParams& p, int grid, int lds, hipStream_t st) {
   if (lds > 65536) {  // above the default dynamic LDS limit: raise it once
     static const hipError_t once = hipFuncSetAttribute(
-        (const void*)decode_kernel<T, Z, MODE, AL, L, MT>,
+        (const void*)decode_kernel<T, Z, MODE, AL, L, MT, SLIDE>,
         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 64);
     if (once != hipSuccess) return once;
   }
-  hipLaunchKernelGGL((decode_kernel<T, Z, MODE, AL, L, MT>), dim3(grid), dim3(kDecodeThreads),
-                     lds, st, p);
+  hipLaunchKernelGGL((decode_kernel<T, Z, MODE, AL, L, MT, SLIDE>), dim3(grid),
+                     dim3(kDecodeThreads), lds, st, p);
   return hipGetLastError();
+}
+// rows rounded up to MT, and the last arrival's partial loads: windows one
+// after another for one row per wavefront or fewer than two windows of
+// splits (a window: 16 splits up to 8 rows, 4 above), else a sliding window
+// (K = N = 4096 fp16 G = 32, 32 splits: M = 5 9.4 -> 8.9 us, M = 8 10.3 ->
+// 9.1 us; at 20 splits, M = 5, it was 1 us slower)
+template <typename T, bool Z, int MODE, bool AL, int L, int MT>
+static hipError_t decode_slide(const DecodeParams& p, int grid, int lds, hipStream_t st) {
+  if (p.S >= 2 * (MT <= 8 ? 16 : 4)) return decode_go<T, Z, MODE, AL, L, MT, true>(p, grid, lds, st);
+  return decode_go<T, Z, MODE, AL, L, MT, false>(p, grid, lds, st);
 }
 template <typename T, bool Z, int MODE, bool AL, int L>
 static hipError_t decode_mt(const DecodeParams& p, int grid, int lds, hipStream_t st) {
-  if (p.M <= 4) return decode_go<T, Z, MODE, AL, L, 4>(p, grid, lds, st);
-  if (p.M <= 8) return decode_go<T, Z, MODE, AL, L, 8>(p, grid, lds, st);
-  return decode_go<T, Z, MODE, AL, L, 16>(p, grid, lds, st);
+  if (p.M <= 4) return decode_go<T, Z, MODE, AL, L, 4, false>(p, grid, lds, st);
+  if (p.M <= 8) return decode_slide<T, Z, MODE, AL, L, 8>(p, grid, lds, st);
+  return decode_slide<T, Z, MODE, AL, L, 16>(p, grid, lds, st);
 }
 template <typename T, bool Z, int MODE, bool AL>
 static hipError_t decode_l(const DecodeParams& p, int grid, int lds, hipStream_t st) {
   if constexpr (!AL) {
     // shapes off the fast layout run one step per wavefront, 16-row reductions
     if (p.L != 1) return hipErrorInvalidValue;
-    return decode_go<T, Z, MODE, AL, 1, 16>(p, grid, lds, st);
+    return decode_slide<T, Z, MODE, AL, 1, 16>(p, grid, lds, st);
   } else {
     switch (p.L) {
       case 1: return decode_mt<T, Z, MODE, AL, 1>(p, grid, lds, st);
