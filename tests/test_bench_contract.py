@@ -43,3 +43,32 @@ def test_traffic_record_is_tied_to_the_kernel_source(tmp_path):
     assert bench.load_traffic(str(p), "decode_m1+decode_m5", bench.kernel_source_hash()) == 123
     assert bench.load_traffic(str(p), "decode_m1+decode_m5", "0" * 16) is None
     assert bench.load_traffic(str(p), "prefill", bench.kernel_source_hash()) is None
+
+
+def test_traffic_summary_reads_the_rocprof_counter_files(tmp_path):
+    # two counter passes in rocprofv3's CSV form: the 256 MiB calibration copy
+    # and the two decode instantiations (rows rounded up to 4 and 8), each
+    # counter summed over its instances; FETCH_SIZE reads half the bytes
+    from weight_only_int4_unpack_amd import traffic
+    dec = ("void w4a16::(anonymous namespace)::decode_kernel<w4a16::(anonymous namespace)::BF16, "
+           "false, 1, true, 4, {mt}, false>(w4a16::DecodeParams)")
+    kib = {"FETCH_SIZE": {"copy": 131072.0, 4: 22000.0, 8: 24000.0},
+           "WRITE_SIZE": {"copy": 262144.0, 4: 700.0, 8: 3600.0}}
+    for counter, vals in kib.items():
+        d = tmp_path / counter
+        d.mkdir()
+        rows = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+        did = 0
+        for key, v in vals.items():
+            name = "__amd_rocclr_copyBuffer" if key == "copy" else dec.format(mt=key)
+            for _ in range(3):
+                did += 1
+                rows += [f'{did},"{name}",{counter},{v / 2}'] * 2   # two instances
+        (d / "bench_counter_collection.csv").write_text("\n".join(rows) + "\n")
+    rec = traffic.summarise(str(tmp_path / "FETCH_SIZE"), str(tmp_path / "WRITE_SIZE"))
+    r = rec["decode_m1+decode_m5"]
+    assert r["calibration"]["fetch_scale"] == 2.0 and r["calibration"]["write_scale"] == 1.0
+    assert r["read_bytes"] == {"M=1": 22000 * 2048, "M=5": 24000 * 2048}
+    assert r["write_bytes"] == {"M=1": 700 * 1024, "M=5": 3600 * 1024}
+    assert r["bytes_per_launch"] == (22000 * 2048 + 700 * 1024 + 24000 * 2048 + 3600 * 1024) // 2
+    assert r["kernel_sha"] == bench.kernel_source_hash()

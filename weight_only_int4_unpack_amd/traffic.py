@@ -73,8 +73,11 @@ def summarise(fetch_dir: str, write_dir: str) -> dict:
             groups_w[wnames[d]].append(v * wscale * 1024)
     per = {}
     for name in sorted(groups_f):
-        # the last template argument is the row count rounded up: 4 for M = 1, 8 for M = 5
-        rows = "M=1" if name.split("(w4a16::DecodeParams")[0].endswith(" 4>") else "M=5"
+        # template arguments (type, zero points, mode, aligned, steps, rows
+        # rounded up, sliding window): rows 4 for M = 1, 8 for M = 5
+        targs = [t.strip() for t in name.split("(w4a16::DecodeParams")[0].rsplit("<", 1)[1]
+                 .rstrip(">").split(",")]
+        rows = {"4": "M=1", "8": "M=5"}[targs[5]]
         per[rows] = {"read": statistics.mean(groups_f[name]),
                      "write": statistics.mean(groups_w[name]), "dispatches": len(groups_f[name])}
     sys.path.insert(0, ROOT)
