@@ -459,6 +459,8 @@ def test_canaries_and_inputs_untouched(M):
 
 @pytest.mark.parametrize("M,K,N,G,dtype,zp", [
     (1, 2120, 520, 2120, "fp16", True),     # K % 32 != 0, N % 256 != 0
+    (3, 2120, 512, 2120, "bf16", True),     # K % 32 != 0 on the fast layout: the last
+    (6, 1064, 1024, 1064, "fp16", False),   # step's weight rows past K read as zeros
     (7, 129, 264, 129, "bf16", False),      # K % 8 != 0 (per-channel)
     (16, 96, 24, 32, "fp16", True),         # fewer columns than one block
     (2, 4096, 8, 128, "bf16", True),        # N = 8
