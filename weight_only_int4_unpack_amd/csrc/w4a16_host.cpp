@@ -125,11 +125,12 @@ int32_t decode_counter_stride(int64_t NB) {
 // barrier that waits for the stream's first loads. Its candidates are the L
 // whose steps fit in one group and whose K split count S stays at most 64
 // at one row, 32 up to 8 rows, 16 above (each split adds partials that the
-// last arrival loads). Among them: the L whose grid is resident at once (3 wavefronts
-// per SIMD, fewer if LDS says so) and whose workgroup count is closest, by
-// ratio, to max(column blocks, min(CUs, weight bytes / 32 KiB)); with none
+// last arrival loads). Among them: the L whose grid is resident at once (3
+// wavefronts per SIMD, fewer if LDS says so) and whose workgroup count is
+// closest, by ratio, to max(column blocks, min(CUs, weight bytes / 32 KiB)),
+// halved above 8 rows but not below 64; with none
 // resident, the longest. Without a mode 1 candidate: the resident L closest
-// to max(column blocks, weight bytes / 32 KiB), else 8. Ties go to the
+// to max(column blocks, weight bytes / 32 KiB) (halved likewise), else 8. Ties go to the
 // smaller L. Measured on MI355X (graph-replayed, weights rotated), chosen
 // plan against the next best: K=N=4096 fp16 G=32 M=1 L=1 7.4 us (L=2, mode
 // 0: 8.3), M=5 9.3 (9.6); K=8192, N=4096 bf16 G=128 M=4 L=4 8.8 (L=2: 9.7);
@@ -145,8 +146,9 @@ int64_t decode_auto_steps(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dt
   const bool one_group = ((int64_t)G == K);
   const bool aligned = (N % 16 == 0) && (K % 8 == 0);
   auto fits_one_of = [&](int64_t l) { return one_group || (SG >= l && SG % l == 0); };
-  *one_group_out = fits_one_of(1);
-  if (!aligned) return 1;  // off the fast layout: one step per wavefront
+  // off the fast layout: one step per wavefront, always inside one group
+  *one_group_out = true;
+  if (!aligned) return 1;
   const double bytes = (double)K * (double)N / 2.0;
   // above 8 rows each split's hand-off carries twice the partials: aim at
   // half the workgroups, but not below 64 (K = N = 4096, per-channel,
