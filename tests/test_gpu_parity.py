@@ -515,6 +515,21 @@ def test_decode_counter_slots_reused_across_strides():
         assert_within_tolerance(got, want, p.dtype, f"N={p.N} splits={plan.splits}")
 
 
+# From 9 to 16 rows the selector keeps the decode where each wavefront's 2 or
+# more steps lie inside one group with at most 16 splits: groups of 128 and
+# 64, through the selector's own plan (16-row MFMA blocks, 4 rows per
+# wavefront in the hand-off)
+@pytest.mark.parametrize("M", [9, 12, 16])
+@pytest.mark.parametrize("K,N,G,dtype,zp", [(4096, 4096, 128, "bf16", False),
+                                            (2112, 5120, 64, "fp16", True)])
+def test_decode_route_mid_m_one_group(M, K, N, G, dtype, zp):
+    p = random_problem(M, K, N, G, dtype, zp, seed=950 + M + G)
+    plan = W.plan(M, K, N, G, zp, TORCH_DT[dtype])
+    assert plan.route == W.ROUTE_DECODE and plan.decode_mode == 1 and plan.steps_per_wave >= 2
+    assert plan.splits <= 16, plan.as_dict()
+    assert_within_tolerance(dev_to_bits(p.gpu_gemm()), p.oracle_gemm(), dtype, f"M={M}")
+
+
 # The last arrival of a split decode with several rows per wavefront (M >= 5)
 # and at least two windows of splits keeps a sliding window of partial
 # loads in flight, wrapping the surplus split indices of its last window and
