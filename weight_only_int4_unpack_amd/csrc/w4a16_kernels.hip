@@ -1291,6 +1291,40 @@ __global__ __launch_bounds__(kPrefillThreads, (BM == 64 || RING) ? 2 : 3) void p
       for (int i = 0; i < MB; ++i) fold_block(sc, bias, asum[i], part[i], acc[i]);
     }
   };
+  // The magic-operand path of slab() in two parts, so that a stage can form
+  // its second slab's operands between the first slab's MFMAs: the
+  // operands of a slab, and its MFMAs (then its fold), with hook(i) called
+  // after row block i's MFMAs (i < MB).
+  auto slab_ops = [&](const Slab& sl, u32x4 (&bop)[4]) {
+    uint32_t Y[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Y[r] = __builtin_bit_cast(uint32_t, sl.q[r]);
+    bop[0] = magic_op<T, 0>(Y, mag);
+    bop[1] = magic_op<T, 1>(Y, mag);
+    bop[2] = magic_op<T, 2>(Y, mag);
+    bop[3] = magic_op<T, 3>(Y, mag);
+  };
+  auto slab_mma = [&](uint32_t buf, int ks, const Slab& sl, const u32x4 (&bop)[4], auto posc,
+                      auto&& hook) {
+    constexpr int POS = decltype(posc)::value;
+    constexpr bool opens = GS > 0 && POS % (GS > 0 ? GS : 1) == 0;
+    constexpr bool closes = GS > 0 && (POS + 1) % (GS > 0 ? GS : 1) == 0;
+    float sc[4], bias[4];
+    if constexpr (closes) col_consts(sl.s, HAS_ZP ? sl.z : 0u, sl.valid, sc, bias);
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const u32x4 aop = aop_at(buf, ks, i);
+      if constexpr (!kPreSum) asum[i] = mfma<T>(aop, ones, opens ? zero4 : asum[i]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        part[i][e] = mfma<T>(aop, bop[e], opens ? (kInitSum ? asum[i] : zero4) : part[i][e]);
+      hook(i);
+    }
+    if constexpr (closes) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) fold_block(sc, bias, asum[i], part[i], acc[i]);
+    }
+  };
   // One stage (P: 0 or 1 within the unrolled body; LD: stage kt+1 exists):
   // prefetch stage kt+1 (A to registers, weights to `nxt`), compute stage
   // kt, publish the A tile.
@@ -1337,11 +1371,41 @@ __global__ __launch_bounds__(kPrefillThreads, (BM == 64 || RING) ? 2 : 3) void p
       if constexpr (decltype(issuec)::value)
         ring_issue(kt + kRingSlots - 1, std::integral_constant<int, (SL + kRingSlots - 1) % kRingSlots>{});
       constexpr uint32_t so = SL * kSlotB;
-      Slab sl;
-      ring_slab(so, 0, sl, std::integral_constant<int, 2 * P>{});
-      slab(so, 0, sl, std::integral_constant<int, 2 * P>{});
-      ring_slab(so, 1, sl, std::integral_constant<int, 2 * P + 1>{});
-      slab(so, 1, sl, std::integral_constant<int, 2 * P + 1>{});
+      if constexpr (!kTile && !kIntOp && GS > 1) {
+        // the second slab's operands formed between the first slab's MFMAs
+        // (one nibble position per row block), so that a wavefront's own
+        // VALU work runs while its matrix-core work does
+        using Q0 = std::integral_constant<int, 2 * P>;
+        using Q1 = std::integral_constant<int, 2 * P + 1>;
+        Slab s0, s1;
+        ring_slab(so, 0, s0, Q0{});
+        ring_slab(so, 1, s1, Q1{});
+        u32x4 b0[4], b1[4];
+        slab_ops(s0, b0);
+        uint32_t Y1[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Y1[r] = __builtin_bit_cast(uint32_t, s1.q[r]);
+        // nibble positions 4i / MB .. 4(i + 1) / MB - 1 behind row block i
+        auto form = [&](int e) {
+          switch (e) {
+            case 0: b1[0] = magic_op<T, 0>(Y1, mag); break;
+            case 1: b1[1] = magic_op<T, 1>(Y1, mag); break;
+            case 2: b1[2] = magic_op<T, 2>(Y1, mag); break;
+            default: b1[3] = magic_op<T, 3>(Y1, mag); break;
+          }
+        };
+        slab_mma(so, 0, s0, b0, Q0{}, [&](int i) {
+#pragma unroll
+          for (int e = i * 4 / MB; e < (i + 1) * 4 / MB; ++e) form(e);
+        });
+        slab_mma(so, 1, s1, b1, Q1{}, [](int) {});
+      } else {
+        Slab sl;
+        ring_slab(so, 0, sl, std::integral_constant<int, 2 * P>{});
+        slab(so, 0, sl, std::integral_constant<int, 2 * P>{});
+        ring_slab(so, 1, sl, std::integral_constant<int, 2 * P + 1>{});
+        slab(so, 1, sl, std::integral_constant<int, 2 * P + 1>{});
+      }
     };
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
