@@ -454,3 +454,49 @@ def test_k_limit_and_counter_limit():
         W.plan(1, 4096, N, 128, False, torch.bfloat16, route=W.ROUTE_DECODE)
     assert e.value.status == W.ERR_PLAN
     assert W.plan(1, 4096, 4096 * 256, 128, False, torch.bfloat16).route == W.ROUTE_DECODE
+
+
+def test_plan_invariants_over_random_shapes():
+    # the selector's plans on 4000 seeded random shapes: every plan is one the
+    # kernels can run, covers K exactly once and asks for enough scratch
+    rng = np.random.default_rng(2024)
+    D, P = W.ROUTE_DECODE, W.ROUTE_PREFILL
+    for _ in range(4000):
+        M = int(np.exp(rng.uniform(0, np.log(4096))))
+        G = int(rng.choice([32, 64, 128, 0]))
+        if G:
+            K = G * int(rng.integers(1, 16384 // G + 1))
+        else:
+            K = 8 * int(rng.integers(1, 2049)) + int(rng.choice([0, 0, 0, 1]))   # K % 8 != 0 now and then
+            G = K
+        N = 8 * int(np.exp(rng.uniform(0, np.log(8192))))
+        dt = torch.float16 if rng.integers(2) else torch.bfloat16
+        zp = bool(rng.integers(2))
+        p = W.plan(M, K, N, G, zp, dt)
+        d = p.as_dict()
+        what = (M, K, N, G, dt, zp, d)
+        assert d["lds_bytes"] <= 160 * 1024, what
+        assert W.workspace_bytes(M, K, N, G, dt) >= d["workspace_bytes"], what
+        if d["route"] == D:
+            KS, L, S = -(-K // 32), d["steps_per_wave"], d["splits"]
+            assert M <= 16 and L in (1, 2, 4, 8), what
+            assert S == -(-KS // (4 * L)) and (S - 1) * 4 * L < KS, what       # K once, no empty split
+            assert d["grid"] == -(-N // 256) * S, what
+            assert d["decode_mode"] in (0, 1, 2), what
+            if d["decode_mode"] == 0:
+                assert dt == torch.float16, what
+            if d["decode_mode"] == 1:
+                assert G == K or (G // 32) % L == 0, what                      # steps inside one group
+            if N % 16 or K % 8:
+                assert L == 1, what
+            if S > 1:
+                assert d["workspace_bytes"] >= W.WORKSPACE_COUNTER_BYTES + S * M * N * 4, what
+        else:
+            assert d["route"] == P, what
+            KT, bm, S = -(-K // 64), d["block_m"], d["splits"]
+            assert bm in (32, 64) and S == -(-KT // d["steps_per_wave"]), what
+            units = -(-M // bm) * -(-N // 256) * S                              # tiles x splits,
+            assert d["grid"] == -(-units // 8) * 8, what                         # padded to the 8 XCDs
+            if S > 1:
+                assert d["workspace_bytes"] >= W.WORKSPACE_COUNTER_BYTES + S * M * N * 4, what
+            assert M > 1 or N <= 8192 or K % 8, what   # one row takes the decode on wide N
