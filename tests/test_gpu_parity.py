@@ -589,3 +589,26 @@ def test_streams_are_respected():
         out = p.gpu_gemm()
     s.synchronize()
     assert_within_tolerance(dev_to_bits(out), want, "bf16", "side stream")
+
+
+# Seeded random shapes through the selector's own plan (whatever route, split
+# and mode it takes), every row and 96 sampled columns (both edges included)
+# against the oracle.
+def test_random_shapes_selector_plan():
+    rng = np.random.default_rng(77)
+    for t in range(40):
+        M = int(np.exp(rng.uniform(0, np.log(300))))
+        G = int(rng.choice([32, 64, 128, 0]))
+        if G:
+            K = G * int(rng.integers(1, 4096 // G + 1))
+        else:
+            K = 8 * int(rng.integers(1, 513)) + int(rng.choice([0, 0, 1]))
+            G = K
+        N = 8 * int(rng.integers(1, 1025))
+        dtype = "fp16" if rng.integers(2) else "bf16"
+        zp = bool(rng.integers(2))
+        p = random_problem(M, K, N, G, dtype, zp, seed=1000 + t)
+        cols = np.unique(np.r_[0:min(N, 16), max(0, N - 16):N, rng.integers(0, N, 64)])
+        got = dev_to_bits(p.gpu_gemm())[:, cols]
+        plan = W.plan(M, K, N, G, zp, TORCH_DT[dtype]).as_dict()
+        assert_within_tolerance(got, p.oracle_gemm(cols=cols), dtype, f"{(M, K, N, G, dtype, zp)} {plan}")
