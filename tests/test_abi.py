@@ -201,17 +201,18 @@ def test_python_wrapper_validates_shapes():
 def test_selector_routes_on_runtime_m():
     D, P = W.ROUTE_DECODE, W.ROUTE_PREFILL
     # K = N = 4096, fp16 groups of 32: decode up to 8 rows, one step per
-    # wavefront inside its group (mode 1, 32 splits); the prefill above
+    # wavefront inside its group (mode 1), 8 wavefronts per workgroup: 16
+    # splits over 256 workgroups (32 over 512 with 4); the prefill above
     for M in (1, 2, 4, 5, 6, 8):
         p = W.plan(M, 4096, 4096, 32, True, torch.float16)
-        assert (p.route, p.steps_per_wave, p.decode_mode, p.splits) == (D, 1, 1, 32), M
+        assert (p.route, p.steps_per_wave, p.decode_mode, p.splits, p.threads) == (D, 1, 1, 16, 512), M
     for M in (9, 16, 17, 64, 256, 2048, 4096):
         assert W.plan(M, 4096, 4096, 32, True, torch.float16).route == P
     assert W.plan(0, 4096, 4096, 32, True, torch.float16).route == W.ROUTE_NONE
     # K = N = 8192, fp16 groups of 32: mode 1 would take 64 splits, allowed at
     # one row only; from two rows the ring prefill's K split (N <= 8192)
     p = W.plan(1, 8192, 8192, 32, True, torch.float16)
-    assert (p.route, p.decode_mode, p.splits) == (D, 1, 64)
+    assert (p.route, p.decode_mode, p.splits * p.threads // 64) == (D, 1, 256)
     for M in (2, 4, 8):
         assert W.plan(M, 8192, 8192, 32, True, torch.float16).route == P
     # ... but wide N keeps the decode, with the rounded weights (mode 0)
@@ -332,7 +333,7 @@ def test_forced_routes_and_errors():
         W.plan(17, 4096, 4096, 32, True, torch.float16, route=W.ROUTE_DECODE)
     assert e.value.status == W.ERR_PLAN
     p = W.plan(4, 4096, 4096, 32, True, torch.float16, route=W.ROUTE_DECODE, steps_per_wave=1)
-    assert p.steps_per_wave == 1 and p.splits == 4096 // 32 // 4
+    assert p.steps_per_wave == 1 and p.splits == 4096 // 32 // (p.threads // 64)
     p = W.plan(4, 4096, 4096, 32, True, torch.float16, route=W.ROUTE_DECODE, decode_mode=2)
     assert p.decode_mode == 2
     for bad in (dict(steps_per_wave=3), dict(decode_mode=3),
@@ -478,9 +479,10 @@ def test_plan_invariants_over_random_shapes():
         assert d["lds_bytes"] <= 160 * 1024, what
         assert W.workspace_bytes(M, K, N, G, dt) >= d["workspace_bytes"], what
         if d["route"] == D:
-            KS, L, S = -(-K // 32), d["steps_per_wave"], d["splits"]
+            KS, L, S, Wv = -(-K // 32), d["steps_per_wave"], d["splits"], d["threads"] // 64
             assert M <= 16 and L in (1, 2, 4, 8), what
-            assert S == -(-KS // (4 * L)) and (S - 1) * 4 * L < KS, what       # K once, no empty split
+            assert Wv == 4 or (Wv == 8 and L <= 2 and M <= 8 and N % 16 == 0 and K % 8 == 0), what
+            assert S == -(-KS // (Wv * L)) and (S - 1) * Wv * L < KS, what     # K once, no empty split
             assert d["grid"] == -(-N // 256) * S, what
             assert d["decode_mode"] in (0, 1, 2), what
             if d["decode_mode"] == 0:

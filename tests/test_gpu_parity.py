@@ -515,6 +515,26 @@ def test_decode_counter_slots_reused_across_strides():
         assert_within_tolerance(got, want, p.dtype, f"N={p.N} splits={plan.splits}")
 
 
+# Eight wavefronts per workgroup (half the K splits at the same wavefront
+# count; the planner's choice for small shapes at one or two steps per
+# wavefront): every operand mode, M = 1..8 (row blocks of 4 and 8, one row per
+# wavefront in the hand-off), with the staged-scale modes 0 and 2 reading
+# their 256 columns' scales through the first 256 threads.
+@pytest.mark.parametrize("M,K,N,G,dtype,zp,L,mode", [
+    (1, 4096, 4096, 32, "fp16", True, 0, -1), (2, 4096, 4096, 32, "bf16", True, 0, -1),
+    (4, 4096, 4096, 32, "fp16", False, 0, -1), (5, 4096, 4096, 32, "fp16", True, 0, -1),
+    (8, 4096, 4096, 32, "bf16", False, 0, -1), (3, 8192, 4096, 32, "fp16", True, 2, 0),
+    (5, 8192, 4096, 32, "bf16", True, 2, 2), (8, 8192, 4096, 64, "fp16", True, 2, 1),
+    (7, 8192, 4096, 32, "fp16", True, 1, 1)])
+def test_decode_eight_wavefronts(M, K, N, G, dtype, zp, L, mode):
+    p = random_problem(M, K, N, G, dtype, zp, seed=970 + M + K // 1024 + L)
+    plan = W.plan(M, K, N, G, zp, TORCH_DT[dtype]) if L == 0 else _plan(p, W.ROUTE_DECODE, L=L, mode=mode)
+    assert plan.route == W.ROUTE_DECODE and plan.threads == 512, plan.as_dict()
+    cols = np.unique(np.r_[0:64, N - 64:N, np.random.default_rng(M).integers(0, N, 256)])
+    got = dev_to_bits(p.gpu_gemm(plan=None if L == 0 else plan))[:, cols]
+    assert_within_tolerance(got, p.oracle_gemm(cols=cols), dtype, f"M={M} L={L} mode={plan.decode_mode}")
+
+
 # From 9 to 16 rows the selector keeps the decode where each wavefront's 2 or
 # more steps lie inside one group with at most 16 splits: groups of 128 and
 # 64, through the selector's own plan (16-row MFMA blocks, 4 rows per

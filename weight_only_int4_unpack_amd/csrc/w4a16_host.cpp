@@ -93,11 +93,11 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // the scale into each weight (cheap packed fp16 ops); otherwise the scale is
 // applied per group to the fp32 partial, with one group per wavefront when
 // the wavefront's steps cannot straddle a group boundary.
-int decode_ng_max(int64_t K, int32_t G, int64_t L) {
+int decode_ng_max(int64_t K, int32_t G, int64_t L, int W = w4a16::kDecodeWaves) {
   using namespace w4a16;
   if ((int64_t)G == K) return 1;
   const int64_t SG = G / kStepRows;
-  return (int)std::max<int64_t>(1, (kDecodeWaves * L) / SG + 1);
+  return (int)std::max<int64_t>(1, (W * L) / SG + 1);
 }
 
 // Arrival counters of a split decode: one per (column block, wavefront),
@@ -107,12 +107,35 @@ int decode_ng_max(int64_t K, int32_t G, int64_t L) {
 // G = 32 at M = 5 (2048 arrivals on 64 counters) took 3-4 us to return and
 // the launch 14.0 us; spread, 9.6 us (M = 1, one step per wavefront: 8.7 ->
 // 7.4 us).
-int32_t decode_counter_stride(int64_t NB) {
+int32_t decode_counter_stride(int64_t NB, int W) {
   using namespace w4a16;
   const int64_t slots = kCounterBytes / (int64_t)sizeof(int32_t);
   int32_t cs = 1;
-  while (2 * cs <= kCounterStrideMax && 2 * cs * NB * kDecodeWaves <= slots) cs *= 2;
+  while (2 * cs <= kCounterStrideMax && 2 * cs * NB * W <= slots) cs *= 2;
   return cs;
+}
+
+// Wavefronts per workgroup of a decode launch: 8 instead of 4 halves the K
+// splits (and the partials the last arrival loads) at the same wavefront
+// count, where that helps: up to 8 rows, one or two steps per wavefront, at
+// least 16 splits with 4, and a grid that still covers every CU at least as
+// evenly (whole workgroups per CU) as the 4-wavefront one. Measured on
+// MI355X, K = N = 4096 fp16 G = 32, one step per wavefront: M = 1 7.3 ->
+// 6.7 us, M = 5 8.5 -> 7.6 us (256 workgroups of 8 instead of 512 of 4); at
+// the 5120 x 17408 shape 340 workgroups of 8 (two on some CUs, one on
+// others) took 16.6 us against 12.9 us, which the balance test keeps out.
+int decode_waves(int64_t M, int64_t K, int64_t N, int64_t L, int num_cus) {
+  using namespace w4a16;
+  const int64_t KS = ceil_div(K, kStepRows), NB = ceil_div(N, kDecodeCols);
+  const bool aligned = (N % 16 == 0) && (K % 8 == 0);
+  if (!aligned || M > kAutoDecodeMaxM || L > 2) return kDecodeWaves;
+  const int64_t S4 = ceil_div(KS, kDecodeWaves * L), S8 = ceil_div(KS, kDecodeWavesWide * L);
+  const int64_t g4 = S4 * NB, g8 = S8 * NB;
+  if (S4 < 16 || g8 < num_cus || NB * kDecodeWavesWide > kCounterBytes / (int64_t)sizeof(int32_t))
+    return kDecodeWaves;
+  // workgroups per CU, rounded up, against the even share: 1 is perfectly even
+  auto unevenness = [&](int64_t g) { return (double)ceil_div(g, num_cus) * num_cus / (double)g; };
+  return unevenness(g8) <= unevenness(g4) + 1e-9 ? kDecodeWavesWide : kDecodeWaves;
 }
 
 // Steps per wavefront (L) of a decode launch when the caller leaves them
@@ -247,7 +270,8 @@ w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dty
   // bf16 always takes the exact operand of modes 1 and 2.
   if (mode == 0 && dtype != W4A16_F16)
     return fail(W4A16_ERR_PLAN, "decode mode 0 (rounded weights) is fp16 only");
-  const int64_t S = ceil_div(KS, kDecodeWaves * L);
+  const int W = decode_waves(M, K, N, L, num_cus);
+  const int64_t S = ceil_div(KS, (int64_t)W * L);
   // the kernel addresses the split-K partials with 32-bit byte offsets
   if (S > 1 && S * M * N * 4 >= (int64_t(1) << 32))
     return fail(W4A16_ERR_PLAN, "decode split-K partials (%lld splits x %lld x %lld fp32) exceed 4 GiB",
@@ -263,8 +287,8 @@ w4a16_status plan_decode(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dty
   pl->splits = (int32_t)S;
   pl->steps_per_wave = (int32_t)L;
   pl->grid = (int32_t)(NB * S);
-  pl->threads = kDecodeThreads;
-  pl->lds_bytes = decode_lds_bytes((int)M, decode_ng_max(K, G, L));
+  pl->threads = 64 * W;
+  pl->lds_bytes = decode_lds_bytes((int)M, decode_ng_max(K, G, L, W), W);
   pl->workspace_bytes = S > 1 ? (int64_t)(kCounterBytes + S * M * N * 4) : 0;
   return W4A16_OK;
 }
@@ -529,14 +553,15 @@ w4a16_status run(const w4a16::GemmArgs& g, const w4a16_plan_t& pl, void* ws, hip
     p.KS = (int32_t)ceil_div(g.K, kStepRows);
     p.SG = ((int64_t)g.G == g.K) ? p.KS : g.G / kStepRows;
     p.sg_shift = ((int64_t)g.G == g.K) ? -1 : (g.G == 32 ? 0 : g.G == 64 ? 1 : 2);
-    p.ng_max = decode_ng_max(g.K, g.G, pl.steps_per_wave);
+    p.W = pl.threads / 64;
+    p.ng_max = decode_ng_max(g.K, g.G, pl.steps_per_wave, p.W);
     p.L = pl.steps_per_wave;
     p.S = pl.splits;
     p.NB = (int32_t)ceil_div(g.N, kDecodeCols);
     if (pl.splits > 1) {
       p.ws = partials;
       p.counters = counters;
-      p.cstride = decode_counter_stride(p.NB);
+      p.cstride = decode_counter_stride(p.NB, p.W);
     }
     e = launch_decode(p, g.dtype, g.qzeros != nullptr, pl.decode_mode, pl.grid, pl.lds_bytes,
                       stream);

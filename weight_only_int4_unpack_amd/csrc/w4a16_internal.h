@@ -15,6 +15,7 @@ namespace w4a16 {
 constexpr int kDecodeMaxM = 16;        // rows of one MFMA tile
 constexpr int kDecodeCols = 256;       // output columns per workgroup
 constexpr int kDecodeWaves = 4;        // wavefronts per workgroup
+constexpr int kDecodeWavesWide = 8;    // ... on small shapes at one or two steps per wavefront
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr int kStepRows = 32;          // K rows per MFMA step
 constexpr int kDecodeMaxSteps = 8;     // most 32-row steps one wavefront streams
@@ -47,10 +48,10 @@ constexpr int64_t kStaticPartialBytes = 32ll << 20;
 constexpr int64_t kStaticScratchBytes = kCounterBytes + kStaticPartialBytes;
 static_assert(kStaticScratchBytes == W4A16_NOALLOC_SCRATCH_BYTES, "header and library agree");
 
-// partial sums of the 4 wavefronts, then the staged scales (halves) and
+// partial sums of the W wavefronts, then the staged scales (halves) and
 // packed zero points (words) of at most ng_max groups
-inline int decode_lds_bytes(int M, int ng_max) {
-  return kDecodeWaves * M * kDecodeCols * (int)sizeof(float) + ng_max * kDecodeCols * 2 +
+inline int decode_lds_bytes(int M, int ng_max, int W = kDecodeWaves) {
+  return W * M * kDecodeCols * (int)sizeof(float) + ng_max * kDecodeCols * 2 +
          ng_max * (kDecodeCols / 8) * 4;
 }
 inline int prefill_lds_bytes(int bm) {
@@ -138,7 +139,7 @@ struct DecodeParams {
   const uint16_t* bias;  // nullable [N]
   uint16_t* out;
   float* ws;          // [S, M, N] fp32 partials (S > 1)
-  int32_t* counters;  // [NB][4] arrival counters per wavefront, zero between launches,
+  int32_t* counters;  // [NB][W] arrival counters per wavefront, zero between launches,
                       // cstride int32 apart
   int32_t M, K, N, G, zp_bias;
   int32_t KS;         // K steps of 32 rows
@@ -149,6 +150,7 @@ struct DecodeParams {
   int32_t S;          // splits across workgroups
   int32_t NB;         // column blocks
   int32_t cstride;    // int32 slots from one arrival counter to the next
+  int32_t W;          // wavefronts per workgroup (kDecodeWaves or kDecodeWavesWide)
 };
 
 struct PrefillParams {

@@ -265,7 +265,8 @@ __device__ __forceinline__ uint32_t join_rows(uint32_t w0, uint32_t w1, int h) {
 
 // ---------------------------------------------------------------------------
 // Decode: M <= 16. A workgroup owns 256 output columns and a contiguous range
-// of 4L steps of 32 K-rows; each of its 4 wavefronts streams L of them
+// of W L steps of 32 K-rows; each of its W wavefronts (4, or 8 where the
+// planner halves the K splits) streams L of them
 // through a ring of D = min(L, 2) register slots: the loads of D steps are in
 // flight from the start, and each slot is refilled with step j + D as soon as
 // step j has been consumed. Lane (g, c) loads, per step, rows 8g..8g+7 of
@@ -283,7 +284,7 @@ __device__ __forceinline__ uint32_t join_rows(uint32_t w0, uint32_t w1, int h) {
 //            with sum_k a from one extra MFMA against a ones operand.
 //   kMulti:  as kOneGrp, but a wavefront may span groups: each group's
 //            partial is folded into a second accumulator at its last step.
-// Partials of the 4 wavefronts meet in LDS; partials of the S workgroups of
+// Partials of the W wavefronts meet in LDS; partials of the S workgroups of
 // one column block meet in an fp32 scratch buffer through write-through
 // (agent-scope) stores, and the last workgroup to arrive (arrival counter)
 // adds them in split order and writes the output, so the result does not
@@ -359,9 +360,10 @@ struct DecodeSlot {
 
 // MT: M rounded up to 4, 8 or 16 (compile-time row count of the reductions).
 // SLIDE: the last arrival keeps a sliding window of partial loads in flight
-// (several rows, more splits than one window).
-template <typename T, bool HAS_ZP, int MODE, bool ALIGNED, int L, int MT, bool SLIDE>
-__global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams p) {
+// (several rows, more splits than one window). W: wavefronts per workgroup
+// (4, or 8 for half the K splits on small shapes).
+template <typename T, bool HAS_ZP, int MODE, bool ALIGNED, int L, int MT, bool SLIDE, int W>
+__global__ __launch_bounds__(64 * W, 2) void decode_kernel(DecodeParams p) {
   constexpr int D = L < kRing ? L : kRing;
   extern __shared__ __attribute__((aligned(16))) float red[];
 
@@ -384,16 +386,16 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
   const uint16_t* arow = p.a + (int64_t)mrow * p.K;
   const DqRegs mag = dq_regs(p.dq);
 
-  const int wg_beg = s * kDecodeWaves * L;
-  const int wg_last = min(wg_beg + kDecodeWaves * L, p.KS) - 1;
+  const int wg_beg = s * W * L;
+  const int wg_last = min(wg_beg + W * L, p.KS) - 1;
   const int step_beg = wg_beg + wave * L;
   const int nsteps = max(0, min(L, p.KS - step_beg));
   auto group_of = [&](int st) { return p.sg_shift < 0 ? 0 : (st >> p.sg_shift); };
   const int g_lo = group_of(wg_beg);
   const int ngroups = group_of(wg_last) - g_lo + 1;
 
-  // LDS: red[4][M][256] floats | scales[ng_max][256] halves | zeros[ng_max][32] words
-  uint16_t* lds_sc = (uint16_t*)(red + kDecodeWaves * M * kDecodeCols);
+  // LDS: red[W][M][256] floats | scales[ng_max][256] halves | zeros[ng_max][32] words
+  uint16_t* lds_sc = (uint16_t*)(red + W * M * kDecodeCols);
   uint32_t* lds_z = (uint32_t*)(lds_sc + p.ng_max * kDecodeCols);
 
   // ---- ring prologue: the first D steps' loads
@@ -461,10 +463,11 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
   // ---- the other modes stage this workgroup's scales and zero points in LDS
   if constexpr (MODE != kOneGrp) {
     const int colc = min(b * kDecodeCols + tid, p.N - 1);
-    for (int gi = 0; gi < ngroups; ++gi)
-      lds_sc[gi * kDecodeCols + tid] = p.sc[(int64_t)(g_lo + gi) * p.N + colc];
+    if (tid < kDecodeCols)
+      for (int gi = 0; gi < ngroups; ++gi)
+        lds_sc[gi * kDecodeCols + tid] = p.sc[(int64_t)(g_lo + gi) * p.N + colc];
     if constexpr (HAS_ZP) {
-      for (int i = tid; i < ngroups * 32; i += kDecodeThreads) {
+      for (int i = tid; i < ngroups * 32; i += 64 * W) {
         const int gi = i >> 5, wi = min(b * 32 + (i & 31), N8 - 1);
         lds_z[i] = p.qz[(int64_t)(g_lo + gi) * N8 + wi];
       }
@@ -587,7 +590,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
     if constexpr (MODE == kOneGrp) return &R; else return &acc;
   }();
 
-  // ---- the 4 wavefronts' partials meet in LDS: red[wave][m][256]
+  // ---- the W wavefronts' partials meet in LDS: red[wave][m][256]
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int m = 4 * g + v;
@@ -601,11 +604,11 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
   }
   __syncthreads();
 
-  // Wavefront w owns rows w, w + 4, ... (< M) and lane l columns b*256 + 4l
+  // Wavefront w owns rows w, w + W, ... (< M) and lane l columns b*256 + 4l
   // .. 4l + 3 of them: 16-byte LDS reads and 8-byte global accesses keep this
   // epilogue short, which matters because the last arrival of a column block
   // runs it once, from a cold instruction cache, on the kernel's critical path.
-  constexpr int RPT = MT / 4;  // rows per wavefront
+  constexpr int RPT = (MT + W - 1) / W;  // rows per wavefront
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int col4 = b * kDecodeCols + 4 * lane;
   const bool col_ok = col4 < p.N;  // N % 8 == 0: all four columns or none
@@ -616,11 +619,11 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
   f32x4 part[RPT];
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
-    const int m = wv + 4 * r;
+    const int m = wv + W * r;
     if (m < M) {
       f32x4 v = *(const f32x4*)(red + m * kDecodeCols + 4 * lane);
 #pragma unroll
-      for (int w = 1; w < kDecodeWaves; ++w)
+      for (int w = 1; w < W; ++w)
         v += *(const f32x4*)(red + (w * M + m) * kDecodeCols + 4 * lane);
       part[r] = v;
     }
@@ -630,8 +633,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
       const f32x4 bv = bias4(T{}, p.bias, col4);
 #pragma unroll
       for (int r = 0; r < RPT; ++r)
-        if (wv + 4 * r < M)
-          store_out4(T{}, p.out + (int64_t)(wv + 4 * r) * p.N + col4, part[r] + bv);
+        if (wv + W * r < M)
+          store_out4(T{}, p.out + (int64_t)(wv + W * r) * p.N + col4, part[r] + bv);
     }
     return;
   }
@@ -642,8 +645,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
   if (col_ok) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
-      if (wv + 4 * r < M)
-        store_wt4(wsr, (uint32_t)(s * M + wv + 4 * r) * row_bytes + lane_off, part[r]);
+      if (wv + W * r < M)
+        store_wt4(wsr, (uint32_t)(s * M + wv + W * r) * row_bytes + lane_off, part[r]);
   }
   // Ordering of the hand-off. The partials are stored, and later loaded,
   // with the device-scope cache policy (sc1): on gfx950 a store with that
@@ -661,7 +664,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
   // 15 -> 84 us at M = 5, for no change in what this code relies on.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  int32_t* counter = p.counters + (b * kDecodeWaves + wv) * p.cstride;
+  int32_t* counter = p.counters + (b * W + wv) * p.cstride;
   int prev = 0;
   if (lane == 0)
     prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -687,8 +690,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
         if (q0 + u < S) {
 #pragma unroll
           for (int r = 0; r < RPT; ++r)
-            if (wv + 4 * r < M)
-              tq[u][r] = load_wt4(wsr, (uint32_t)(wv + 4 * r) * row_bytes + lane_off,
+            if (wv + W * r < M)
+              tq[u][r] = load_wt4(wsr, (uint32_t)(wv + W * r) * row_bytes + lane_off,
                                   (uint32_t)(q0 + u) * split_bytes);
         }
 #pragma unroll
@@ -696,7 +699,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
         if (q0 + u < S) {
 #pragma unroll
           for (int r = 0; r < RPT; ++r)
-            if (wv + 4 * r < M) sum[r] += tq[u][r];
+            if (wv + W * r < M) sum[r] += tq[u][r];
         }
     }
   } else {
@@ -715,7 +718,7 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
     uint32_t row_off[RPT];
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
-      row_off[r] = wv + 4 * r < M ? (uint32_t)(wv + 4 * r) * row_bytes + lane_off
+      row_off[r] = wv + W * r < M ? (uint32_t)(wv + W * r) * row_bytes + lane_off
                                   : (uint32_t)S * split_bytes;
     auto split_off = [&](int q) { return (uint32_t)(q < S ? q : q - S) * split_bytes; };
     f32x4 tq[QB][RPT];
@@ -750,8 +753,8 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
     const f32x4 bv = bias4(T{}, p.bias, col4);
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
-      if (wv + 4 * r < M)
-        store_out4(T{}, p.out + (int64_t)(wv + 4 * r) * p.N + col4, sum[r] + bv);
+      if (wv + W * r < M)
+        store_out4(T{}, p.out + (int64_t)(wv + W * r) * p.N + col4, sum[r] + bv);
   }
 }
 
@@ -1819,16 +1822,16 @@ __global__ __launch_bounds__(kKpThreads) void kpacked_kernel(KPackedParams p) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <typename T, bool Z, int MODE, bool AL, int L, int MT, bool SLIDE>
+template <typename T, bool Z, int MODE, bool AL, int L, int MT, bool SLIDE, int W = kDecodeWaves>
 static hipError_t decode_go(const DecodeParams& p, int grid, int lds, hipStream_t st) {
   if (lds > 65536) {  // above the default dynamic LDS limit: raise it once
     static const hipError_t once = hipFuncSetAttribute(
-        (const void*)decode_kernel<T, Z, MODE, AL, L, MT, SLIDE>,
+        (const void*)decode_kernel<T, Z, MODE, AL, L, MT, SLIDE, W>,
         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 64);
     if (once != hipSuccess) return once;
   }
-  hipLaunchKernelGGL((decode_kernel<T, Z, MODE, AL, L, MT, SLIDE>), dim3(grid),
-                     dim3(kDecodeThreads), lds, st, p);
+  hipLaunchKernelGGL((decode_kernel<T, Z, MODE, AL, L, MT, SLIDE, W>), dim3(grid), dim3(64 * W),
+                     lds, st, p);
   return hipGetLastError();
 }
 // rows rounded up to MT, and the last arrival's partial loads: windows one
@@ -1843,6 +1846,16 @@ static hipError_t decode_slide(const DecodeParams& p, int grid, int lds, hipStre
 }
 template <typename T, bool Z, int MODE, bool AL, int L>
 static hipError_t decode_mt(const DecodeParams& p, int grid, int lds, hipStream_t st) {
+  if constexpr (AL && L <= 2) {
+    // eight wavefronts per workgroup (the planner's choice for up to 8 rows
+    // at one or two steps per wavefront): one row per wavefront
+    if (p.W == kDecodeWavesWide) {
+      if (p.M <= 4) return decode_go<T, Z, MODE, AL, L, 4, false, kDecodeWavesWide>(p, grid, lds, st);
+      if (p.M <= 8) return decode_go<T, Z, MODE, AL, L, 8, false, kDecodeWavesWide>(p, grid, lds, st);
+      return hipErrorInvalidValue;
+    }
+  }
+  if (p.W != kDecodeWaves) return hipErrorInvalidValue;
   if (p.M <= 4) return decode_go<T, Z, MODE, AL, L, 4, false>(p, grid, lds, st);
   if (p.M <= 8) return decode_slide<T, Z, MODE, AL, L, 8>(p, grid, lds, st);
   return decode_slide<T, Z, MODE, AL, L, 16>(p, grid, lds, st);
@@ -1851,7 +1864,7 @@ template <typename T, bool Z, int MODE, bool AL>
 static hipError_t decode_l(const DecodeParams& p, int grid, int lds, hipStream_t st) {
   if constexpr (!AL) {
     // shapes off the fast layout run one step per wavefront, 16-row reductions
-    if (p.L != 1) return hipErrorInvalidValue;
+    if (p.L != 1 || p.W != kDecodeWaves) return hipErrorInvalidValue;
     return decode_slide<T, Z, MODE, AL, 1, 16>(p, grid, lds, st);
   } else {
     switch (p.L) {
