@@ -209,11 +209,15 @@ def test_selector_routes_on_runtime_m():
     for M in (9, 16, 17, 64, 256, 2048, 4096):
         assert W.plan(M, 4096, 4096, 32, True, torch.float16).route == P
     assert W.plan(0, 4096, 4096, 32, True, torch.float16).route == W.ROUTE_NONE
-    # K = N = 8192, fp16 groups of 32: mode 1 would take 64 splits, allowed at
-    # one row only; from two rows the ring prefill's K split (N <= 8192)
+    # K = N = 8192, fp16 groups of 32: mode 1 takes 64 splits of 4 wavefronts
+    # or 32 of 8; up to 4 rows (M * S <= 128) the decode with 8, from 5 rows
+    # the ring prefill's K split (N <= 8192)
     p = W.plan(1, 8192, 8192, 32, True, torch.float16)
     assert (p.route, p.decode_mode, p.splits * p.threads // 64) == (D, 1, 256)
-    for M in (2, 4, 8):
+    for M in (2, 3, 4):
+        p = W.plan(M, 8192, 8192, 32, True, torch.float16)
+        assert (p.route, p.decode_mode, p.steps_per_wave, p.splits, p.threads) == (D, 1, 1, 32, 512), M
+    for M in (5, 8):
         assert W.plan(M, 8192, 8192, 32, True, torch.float16).route == P
     # ... but wide N keeps the decode, with the rounded weights (mode 0)
     p = W.plan(5, 5120, 17408, 32, True, torch.float16)

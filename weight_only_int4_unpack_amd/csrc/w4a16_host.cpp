@@ -118,12 +118,15 @@ int32_t decode_counter_stride(int64_t NB, int W) {
 // Wavefronts per workgroup of a decode launch: 8 instead of 4 halves the K
 // splits (and the partials the last arrival loads) at the same wavefront
 // count, where that helps: up to 8 rows, one or two steps per wavefront, at
-// least 16 splits with 4, and a grid that still covers every CU at least as
-// evenly (whole workgroups per CU) as the 4-wavefront one. Measured on
-// MI355X, K = N = 4096 fp16 G = 32, one step per wavefront: M = 1 7.3 ->
-// 6.7 us, M = 5 8.5 -> 7.6 us (256 workgroups of 8 instead of 512 of 4); at
-// the 5120 x 17408 shape 340 workgroups of 8 (two on some CUs, one on
-// others) took 16.6 us against 12.9 us, which the balance test keeps out.
+// least 16 splits with 4 (32 at one row), and a grid that still covers every
+// CU at least as evenly (whole workgroups per CU) as the 4-wavefront one.
+// Measured on MI355X, 4 -> 8 wavefronts: K = N = 4096 fp16 G = 32, one step
+// per wavefront, M = 1 7.3 -> 6.8 us, M = 5 8.6 -> 7.7 us; K = 5120,
+// N = 17408 bf16 G = 64, two steps, M = 5 17.6 -> 15.3 us; K = N = 8192
+// G = 32 M = 1 15.3 -> 14.9 us; at one row with 16-20 splits 8 lost (K =
+// 2048, N = 8192: 6.6 -> 6.9 us); at the 5120 x 17408 shape with four steps
+// 340 workgroups of 8 (two on some CUs, one on others) took 16.6 us against
+// 12.9 us, which the evenness test keeps out.
 int decode_waves(int64_t M, int64_t K, int64_t N, int64_t L, int num_cus) {
   using namespace w4a16;
   const int64_t KS = ceil_div(K, kStepRows), NB = ceil_div(N, kDecodeCols);
@@ -131,7 +134,8 @@ int decode_waves(int64_t M, int64_t K, int64_t N, int64_t L, int num_cus) {
   if (!aligned || M > kAutoDecodeMaxM || L > 2) return kDecodeWaves;
   const int64_t S4 = ceil_div(KS, kDecodeWaves * L), S8 = ceil_div(KS, kDecodeWavesWide * L);
   const int64_t g4 = S4 * NB, g8 = S8 * NB;
-  if (S4 < 16 || g8 < num_cus || NB * kDecodeWavesWide > kCounterBytes / (int64_t)sizeof(int32_t))
+  if (S4 < (M == 1 ? 32 : 16) || g8 < num_cus ||
+      NB * kDecodeWavesWide > kCounterBytes / (int64_t)sizeof(int32_t))
     return kDecodeWaves;
   // workgroups per CU, rounded up, against the even share: 1 is perfectly even
   auto unevenness = [&](int64_t g) { return (double)ceil_div(g, num_cus) * num_cus / (double)g; };
@@ -148,7 +152,10 @@ int decode_waves(int64_t M, int64_t K, int64_t N, int64_t L, int num_cus) {
 // barrier that waits for the stream's first loads. Its candidates are the L
 // whose steps fit in one group and whose K split count S stays at most 64
 // at one row, 32 up to 8 rows, 16 above (each split adds partials that the
-// last arrival loads). Among them: the L whose grid is resident at once (3
+// last arrival loads), counted at the plan's wavefronts per workgroup (where
+// only 8 bring S under that cap, also M * S <= 128: K = N = 8192 fp16 G = 32,
+// 32 splits of 8 wavefronts against the prefill route, M = 2 14.8 vs 16.2,
+// M = 4 15.8 vs 16.5 us, but M = 8 17.2 vs 16.6). Among them: the L whose grid is resident at once (3
 // wavefronts per SIMD, fewer if LDS says so) and whose workgroup count is
 // closest, by ratio, to max(column blocks, min(CUs, weight bytes / 32 KiB)),
 // halved above 8 rows but not below 64; with none
@@ -201,8 +208,14 @@ int64_t decode_auto_steps(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dt
   };
   if (mode_forced < 0 || mode_forced == 1) {
     const int64_t smax = M == 1 ? 64 : M <= w4a16::kAutoDecodeMaxM ? 32 : 16;
+    // splits at the plan's own wavefront count; a candidate that only 8
+    // wavefronts per workgroup bring under the cap also keeps M * S <= 128
     auto cand = [&](int64_t l) {
-      return fits_one_of(l) && (mode_forced == 1 || ceil_div(KS, kDecodeWaves * l) <= smax);
+      if (!fits_one_of(l)) return false;
+      if (mode_forced == 1 || ceil_div(KS, kDecodeWaves * l) <= smax) return true;
+      const int64_t w = decode_waves(M, K, N, l, num_cus);
+      const int64_t s = ceil_div(KS, w * l);
+      return w == kDecodeWavesWide && s <= smax && M * s <= 128;
     };
     int64_t L = 0;
     for (int64_t l = 1; l <= kDecodeMaxSteps; l *= 2)
