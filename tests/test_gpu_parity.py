@@ -525,7 +525,9 @@ def test_decode_counter_slots_reused_across_strides():
     (4, 4096, 4096, 32, "fp16", False, 0, -1), (5, 4096, 4096, 32, "fp16", True, 0, -1),
     (8, 4096, 4096, 32, "bf16", False, 0, -1), (3, 8192, 4096, 32, "fp16", True, 2, 0),
     (5, 8192, 4096, 32, "bf16", True, 2, 2), (8, 8192, 4096, 64, "fp16", True, 2, 1),
-    (7, 8192, 4096, 32, "fp16", True, 1, 1)])
+    (7, 8192, 4096, 32, "fp16", True, 1, 1),
+    # the selector's own plan at 32 splits of 8 wavefronts (64 with 4)
+    (3, 8192, 8192, 32, "fp16", True, 0, -1), (4, 8192, 8192, 32, "bf16", False, 0, -1)])
 def test_decode_eight_wavefronts(M, K, N, G, dtype, zp, L, mode):
     p = random_problem(M, K, N, G, dtype, zp, seed=970 + M + K // 1024 + L)
     plan = W.plan(M, K, N, G, zp, TORCH_DT[dtype]) if L == 0 else _plan(p, W.ROUTE_DECODE, L=L, mode=mode)
