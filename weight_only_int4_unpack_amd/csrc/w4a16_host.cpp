@@ -413,8 +413,9 @@ w4a16_status make_plan(int64_t M, int64_t K, int64_t N, int32_t G, int32_t dtype
   // 9.3 vs 9.6 us; K = 2112, N = 5120 fp16 G = 64 M = 8 7.6 vs 8.5; K = 8192,
   // N = 4096 bf16 G = 128 M = 4 8.8 vs 11.2; per-channel K = N = 4096 M = 16
   // 10.2 vs 10.7; K = N = 8192 bf16 G = 128 M = 8 14.6 vs 15.0; sent to the
-  // prefill: K = N = 8192 fp16 G = 32 M = 4 (64 splits for mode 1) 16.5
-  // against 17.1 (mode 1) and 18+ (mode 0, 4 steps). (N beyond what the
+  // prefill: K = N = 8192 fp16 G = 32 M = 8 (mode 1 would take 32 splits of
+  // 8 wavefronts, over the M * S cap above) 17.0 against 17.2 (mode 1) and
+  // 17.6 (mode 0, 2 steps). (N beyond what the
   // counter region serves, 2^20 columns, has column blocks enough to fill
   // the GPU on the prefill route's tiles.)
   if (route == 0) {
